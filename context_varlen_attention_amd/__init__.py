@@ -1,0 +1,349 @@
+"""Python binding of libcva: one context-parallel rank's share of packed
+variable-length attention on MI355X.
+
+This module only marshals arguments to the C ABI declared in ``include/cva.h``
+(ctypes); every step of the computation runs in libcva's C++ host code and HIP
+kernels.  PyTorch provides device memory and the current stream.  If the
+library has not been built the first call raises; there is no fallback path.
+
+Names follow the C ABI:
+
+* :class:`Plan`      -- ``cva_plan_create`` / ``cva_plan_get_metadata`` /
+                        ``cva_plan_upload`` / ``cva_plan_get_schedule``
+* :func:`fwd`        -- ``cva_fwd``
+* :func:`bwd`        -- ``cva_bwd``
+* :func:`local_token_ids`, :func:`rank_major_token_ids` -- the symmetric split
+  and the rank-major order, read from the library's metadata (what a data
+  loader and the K/V all-gather would produce).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+__all__ = ["Plan", "fwd", "bwd", "CvaError", "local_token_ids", "rank_major_token_ids",
+           "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libcva.so")
+_lib = None
+
+DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}
+MASKS = {"causal": 0, "lambda": 1, "shared_prefix": 2}
+STATUS = {
+    0: "CVA_OK", 1: "CVA_E_ARG", 2: "CVA_E_CU_SEQLENS", 3: "CVA_E_ALIGN", 4: "CVA_E_RANK",
+    5: "CVA_E_HEADS", 6: "CVA_E_HEADDIM", 7: "CVA_E_DTYPE", 8: "CVA_E_MASK",
+    9: "CVA_E_UNSUPPORTED", 10: "CVA_E_WORKLOAD", 11: "CVA_E_HIP", 12: "CVA_E_SCALE",
+    13: "CVA_E_WORKSPACE", 14: "CVA_E_NOT_UPLOADED",
+}
+
+
+class CvaError(AssertionError):
+    """A libcva call returned an error status (an AssertionError, as the RFC's
+    interfaces raise on invalid input)."""
+
+    def __init__(self, status, message):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+class _MaskDesc(ctypes.Structure):
+    _fields_ = [("type", ctypes.c_int32), ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("n_branches", ctypes.c_int32), ("branch_bounds", ctypes.POINTER(ctypes.c_int32))]
+
+
+_P32 = ctypes.POINTER(ctypes.c_int32)
+_P64 = ctypes.POINTER(ctypes.c_int64)
+
+
+class _Metadata(ctypes.Structure):
+    _fields_ = [("local_tokens", ctypes.c_int64), ("global_tokens", ctypes.c_int64),
+                ("n_seqs", ctypes.c_int32), ("n_segments", ctypes.c_int32),
+                ("cp_size", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("local_cu", _P32), ("actual_seq_qlen", _P32), ("actual_seq_kvlen", _P32),
+                ("kv_index", _P32), ("seg_q_pos0", _P32), ("kv_index_len", ctypes.c_int64),
+                ("workload_per_rank", _P64), ("visible_pairs", ctypes.c_int64),
+                ("fwd_tiles", ctypes.c_int64)]
+
+
+class _Schedule(ctypes.Structure):
+    _fields_ = [("tile_q", ctypes.c_int32), ("tile_kv", ctypes.c_int32),
+                ("n_tiles", ctypes.c_int32), ("n_spans", ctypes.c_int32),
+                ("tiles", _P32), ("spans", _P32)]
+
+
+EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_get_metadata",
+           "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_bwd_workspace_bytes",
+           "cva_bwd", "cva_plan_get_schedule"]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libcva.so (raises RuntimeError if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m context_varlen_attention_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, sz, i32, f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    L.cva_last_error.restype = ctypes.c_char_p
+    L.cva_last_error.argtypes = []
+    L.cva_plan_create.restype = i32
+    L.cva_plan_create.argtypes = [_P32, i32, i32, i32, ctypes.POINTER(_MaskDesc), i32, i32, i32,
+                                  i32, i32, ctypes.POINTER(vp)]
+    L.cva_plan_destroy.restype = None
+    L.cva_plan_destroy.argtypes = [vp]
+    L.cva_plan_get_metadata.restype = i32
+    L.cva_plan_get_metadata.argtypes = [vp, ctypes.POINTER(_Metadata)]
+    L.cva_plan_device_bytes.restype = sz
+    L.cva_plan_device_bytes.argtypes = [vp]
+    L.cva_plan_upload.restype = i32
+    L.cva_plan_upload.argtypes = [vp, vp, sz, vp]
+    L.cva_fwd.restype = i32
+    L.cva_fwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp]
+    L.cva_bwd_workspace_bytes.restype = sz
+    L.cva_bwd_workspace_bytes.argtypes = [vp]
+    L.cva_bwd.restype = i32
+    L.cva_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
+    L.cva_plan_get_schedule.restype = i32
+    L.cva_plan_get_schedule.argtypes = [vp, i32, ctypes.POINTER(_Schedule)]
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        msg = load_library().cva_last_error().decode(errors="replace")
+        raise CvaError(status, msg)
+
+
+def _arr(ptr, n, dtype):
+    if n == 0:
+        return np.zeros(0, dtype=dtype)
+    return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
+
+
+class Plan:
+    """Host plan of one rank: metadata + tile schedules (``cva_plan_create``).
+
+    ``branch_bounds``: shared-prefix layout, int [n_seqs][n_branches+1] of
+    in-sequence positions {prefix_end, answer ends...}.
+    """
+
+    def __init__(self, cu_seqlens, cp_size, rank, hq, hkv, d_qk, d_v=None, dtype="bf16",
+                 mask="causal", sink=0, window=0, branch_bounds=None):
+        L = load_library()
+        d_v = d_qk if d_v is None else d_v
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        if cu.ndim != 1:
+            raise CvaError(1, "cu_seqlens must be 1-D")
+        if cu.size and (cu.max() > np.iinfo(np.int32).max or cu.min() < np.iinfo(np.int32).min):
+            raise CvaError(1, "cu_seqlens out of int32 range")
+        self._cu = np.ascontiguousarray(cu.astype(np.int32))
+        if dtype not in DTYPES:
+            raise CvaError(7, f"unknown dtype {dtype!r}")
+        if mask not in MASKS:
+            raise CvaError(8, f"unknown mask {mask!r}")
+        self.cp_size, self.rank = int(cp_size), int(rank)
+        self.hq, self.hkv, self.d_qk, self.d_v = int(hq), int(hkv), int(d_qk), int(d_v)
+        self.dtype, self.mask = dtype, mask
+        md = _MaskDesc(MASKS[mask], int(sink), int(window), 0, None)
+        self._bounds = None
+        if branch_bounds is not None:
+            bb = np.ascontiguousarray(np.asarray(branch_bounds, dtype=np.int32))
+            if bb.ndim != 2:
+                raise CvaError(8, "branch_bounds must be 2-D [n_seqs][n_branches+1]")
+            self._bounds = bb
+            md.n_branches = bb.shape[1] - 1
+            md.branch_bounds = bb.ctypes.data_as(_P32)
+        handle = ctypes.c_void_p()
+        n_seqs = max(int(self._cu.size) - 1, 0)
+        cu_ptr = self._cu.ctypes.data_as(_P32) if self._cu.size else None
+        self._h = None
+        _check(L.cva_plan_create(cu_ptr, n_seqs, self.cp_size, self.rank, ctypes.byref(md),
+                                 self.hq, self.hkv, self.d_qk, self.d_v, DTYPES[dtype],
+                                 ctypes.byref(handle)))
+        self._h = handle
+        self._dev = None
+        m = _Metadata()
+        _check(L.cva_plan_get_metadata(self._h, ctypes.byref(m)))
+        nseg = m.n_segments
+        self.local_tokens = int(m.local_tokens)
+        self.global_tokens = int(m.global_tokens)
+        self.metadata = {
+            "local_tokens": int(m.local_tokens),
+            "global_tokens": int(m.global_tokens),
+            "local_cu": _arr(m.local_cu, m.n_seqs + 1, np.int64),
+            "actual_seq_qlen": _arr(m.actual_seq_qlen, nseg + 1, np.int64),
+            "actual_seq_kvlen": _arr(m.actual_seq_kvlen, nseg + 1, np.int64),
+            "kv_index": _arr(m.kv_index, m.kv_index_len, np.int64),
+            "seg_q_pos0": _arr(m.seg_q_pos0, nseg, np.int64),
+            "workload_per_rank": _arr(m.workload_per_rank, m.cp_size, np.int64),
+            "visible_pairs": int(m.visible_pairs),
+            "fwd_tiles": int(m.fwd_tiles),
+        }
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.cva_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def cu_seqlens(self):
+        return self._cu.astype(np.int64)
+
+    def schedule(self, which):
+        """(tile_q, tile_kv, tiles [n,5], spans [m,4]) of schedule 0 fwd, 1 dQ, 2 dK/dV."""
+        s = _Schedule()
+        _check(load_library().cva_plan_get_schedule(self._h, int(which), ctypes.byref(s)))
+        tiles = _arr(s.tiles, s.n_tiles * 5, np.int64).reshape(-1, 5)
+        spans = _arr(s.spans, s.n_spans * 4, np.int64).reshape(-1, 4)
+        return s.tile_q, s.tile_kv, tiles, spans
+
+    def device_bytes(self):
+        return int(load_library().cva_plan_device_bytes(self._h))
+
+    def upload(self, device=None, stream=None):
+        """Copy the plan tables into a torch uint8 buffer on ``device`` and bind them."""
+        import torch
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        nbytes = self.device_bytes()
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        off = (-buf.data_ptr()) % 256
+        view = buf[off: off + nbytes]
+        s = _stream_ptr(stream, dev)
+        _check(load_library().cva_plan_upload(self._h, ctypes.c_void_p(view.data_ptr()),
+                                              nbytes, s))
+        self._dev = buf  # keep alive while the plan is used
+        return self
+
+    @property
+    def uploaded(self):
+        return self._dev is not None
+
+    def visible_pairs(self):
+        return self.metadata["visible_pairs"]
+
+
+def _stream_ptr(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_TORCH_DT = {"bf16": "bfloat16", "fp16": "float16", "fp32": "float32"}
+
+
+def _expect(t, name, shape, dtype, device):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise CvaError(1, f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise CvaError(1, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != getattr(torch, dtype):
+        raise CvaError(7, f"{name} has dtype {t.dtype}, expected torch.{dtype}")
+    if not t.is_cuda or t.device != device:
+        raise CvaError(1, f"{name} must live on {device}")
+    if not t.is_contiguous():
+        raise CvaError(1, f"{name} must be contiguous")
+
+
+def _scale(plan, softmax_scale):
+    if softmax_scale is None:
+        return 1.0 / math.sqrt(plan.d_qk)
+    return float(softmax_scale)
+
+
+def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, stream=None):
+    """``cva_fwd``: returns (o [T_loc, Hq, Dv], lse [Hq, T_loc] float32)."""
+    import torch
+    if not plan.uploaded:
+        plan.upload(q.device)
+    dev = q.device
+    dt = _TORCH_DT[plan.dtype]
+    T, Tl = plan.global_tokens, plan.local_tokens
+    _expect(q, "q", (Tl, plan.hq, plan.d_qk), dt, dev)
+    _expect(k_rm, "k_rm", (T, plan.hkv, plan.d_qk), dt, dev)
+    _expect(v_rm, "v_rm", (T, plan.hkv, plan.d_v), dt, dev)
+    if out is None:
+        out = torch.empty((Tl, plan.hq, plan.d_v), dtype=q.dtype, device=dev)
+    _expect(out, "out", (Tl, plan.hq, plan.d_v), dt, dev)
+    if lse is None:
+        lse = torch.empty((plan.hq, Tl), dtype=torch.float32, device=dev)
+    _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
+    vp = ctypes.c_void_p
+    _check(load_library().cva_fwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()),
+                                  vp(v_rm.data_ptr()), vp(out.data_ptr()), vp(lse.data_ptr()),
+                                  _scale(plan, softmax_scale), _stream_ptr(stream, dev)))
+    return out, lse
+
+
+def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk_rm=None,
+        dv_rm=None, workspace=None, stream=None):
+    """``cva_bwd``: returns (dq [T_loc,Hq,Dqk], dk_rm [T,Hkv,Dqk], dv_rm [T,Hkv,Dv])."""
+    import torch
+    if not plan.uploaded:
+        plan.upload(q.device)
+    dev = q.device
+    dt = _TORCH_DT[plan.dtype]
+    T, Tl = plan.global_tokens, plan.local_tokens
+    _expect(q, "q", (Tl, plan.hq, plan.d_qk), dt, dev)
+    _expect(k_rm, "k_rm", (T, plan.hkv, plan.d_qk), dt, dev)
+    _expect(v_rm, "v_rm", (T, plan.hkv, plan.d_v), dt, dev)
+    _expect(o, "o", (Tl, plan.hq, plan.d_v), dt, dev)
+    _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
+    _expect(dout, "dout", (Tl, plan.hq, plan.d_v), dt, dev)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk_rm is None:
+        dk_rm = torch.empty_like(k_rm)
+    if dv_rm is None:
+        dv_rm = torch.empty_like(v_rm)
+    _expect(dq, "dq", (Tl, plan.hq, plan.d_qk), dt, dev)
+    _expect(dk_rm, "dk_rm", (T, plan.hkv, plan.d_qk), dt, dev)
+    _expect(dv_rm, "dv_rm", (T, plan.hkv, plan.d_v), dt, dev)
+    L = load_library()
+    ws_bytes = int(L.cva_bwd_workspace_bytes(plan.handle))
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=dev)
+    vp = ctypes.c_void_p
+    _check(L.cva_bwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
+                     vp(o.data_ptr()), vp(lse.data_ptr()), vp(dout.data_ptr()), vp(dq.data_ptr()),
+                     vp(dk_rm.data_ptr()), vp(dv_rm.data_ptr()), vp(workspace.data_ptr()),
+                     workspace.numel() * workspace.element_size(), _scale(plan, softmax_scale),
+                     _stream_ptr(stream, dev)))
+    return dq, dk_rm, dv_rm
+
+
+def local_token_ids(cu_seqlens, cp_size, rank):
+    """Packed token ids rank ``rank`` holds, in local order, from libcva's metadata."""
+    p = Plan(cu_seqlens, cp_size, rank, 1, 1, 64, 64, "bf16")
+    md = p.metadata
+    cu = p.cu_seqlens
+    aq, pos0 = md["actual_seq_qlen"], md["seg_q_pos0"]
+    out = np.empty(p.local_tokens, dtype=np.int64)
+    for s in range(len(pos0)):
+        i = s // 2
+        n = aq[s + 1] - aq[s]
+        out[aq[s]: aq[s + 1]] = cu[i] + pos0[s] + np.arange(n)
+    return out
+
+
+def rank_major_token_ids(cu_seqlens, cp_size):
+    """Packed token id at every row of the rank-major all-gathered K/V."""
+    return np.concatenate([local_token_ids(cu_seqlens, cp_size, s) for s in range(cp_size)])

@@ -1,0 +1,258 @@
+// C ABI of libcva (declared in include/cva.h).
+//
+// Plan creation is pure host work (validation, metadata, schedules).  Device
+// work is: one async copy of the plan tables (cva_plan_upload), one forward
+// kernel (cva_fwd) and the backward kernels (cva_bwd), all on the caller's
+// stream, all arguments checked on the host first so that a failing call
+// enqueues nothing (MindSpeed RFC section 3.4: validate before any operator
+// call).
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <sstream>
+
+#include <hip/hip_runtime_api.h>
+
+#include "../host/plan.hpp"
+#include "../kernels/launch.hpp"
+
+using cva::Plan;
+
+namespace {
+
+cva_status fail(cva_status s, const std::string& msg) {
+  cva::set_error(msg);
+  return s;
+}
+
+cva_status hip_fail(hipError_t e, const char* what) {
+  std::ostringstream os;
+  os << what << ": " << hipGetErrorString(e);
+  return fail(CVA_E_HIP, os.str());
+}
+
+cva::PlanTables tables(const Plan& p) {
+  const int32_t* b = (const int32_t*)p.dev;
+  const cva::BlobLayout& L = p.layout;
+  cva::PlanTables t;
+  t.segs = b + L.segs;
+  t.kv_index = b + L.kv_index;
+  t.row_iv = b + L.row_iv;
+  t.fwd_tiles = b + L.fwd_tiles;
+  t.fwd_spans = b + L.fwd_spans;
+  t.dq_tiles = b + L.dq_tiles;
+  t.dq_spans = b + L.dq_spans;
+  t.kv_tiles = b + L.kv_tiles;
+  t.kv_spans = b + L.kv_spans;
+  t.zero_rows = b + L.zero_rows;
+  return t;
+}
+
+cva_status check_scale(float s) {
+  if (!std::isfinite(s) || !(s > 0.f)) return fail(CVA_E_SCALE, "softmax_scale must be finite and > 0");
+  return CVA_OK;
+}
+
+cva_status check_ready(const Plan* p) {
+  if (p == nullptr) return fail(CVA_E_ARG, "plan is NULL");
+  if (p->dev == nullptr) return fail(CVA_E_NOT_UPLOADED, "plan has no device copy; call cva_plan_upload first");
+  return CVA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* cva_last_error(void) { return cva::last_error(); }
+
+cva_status cva_plan_create(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp_size,
+                           int32_t rank, const cva_mask_desc* mask, int32_t hq, int32_t hkv,
+                           int32_t d_qk, int32_t d_v, int32_t dtype, cva_plan** out) {
+  cva::set_error("");
+  if (out == nullptr) return fail(CVA_E_ARG, "out is NULL");
+  *out = nullptr;
+  cva_status st = cva::validate_request(cu_seqlens, n_seqs, cp_size, rank, mask, hq, hkv, d_qk,
+                                        d_v, dtype);
+  if (st != CVA_OK) return st;
+  Plan* p = new (std::nothrow) Plan();
+  if (p == nullptr) return fail(CVA_E_ARG, "out of host memory");
+  try {
+    p->n_seqs = n_seqs;
+    p->cp_size = cp_size;
+    p->rank = rank;
+    p->hq = hq;
+    p->hkv = hkv;
+    p->d_qk = d_qk;
+    p->d_v = d_v;
+    p->dtype = dtype;
+    p->cu.assign(cu_seqlens, cu_seqlens + n_seqs + 1);
+    if (mask != nullptr) {
+      p->mask_type = mask->type;
+      p->sink = mask->sink;
+      p->window = mask->window;
+      if (mask->type == CVA_MASK_SHARED_PREFIX) {
+        p->n_branches = mask->n_branches;
+        const size_t nb = (size_t)n_seqs * (mask->n_branches + 1);
+        p->branch_bounds.assign(mask->branch_bounds, mask->branch_bounds + nb);
+      }
+    }
+    st = cva::build_metadata(*p);
+    if (st == CVA_OK) st = cva::build_schedules(*p);
+    if (st == CVA_OK) cva::build_blob(*p);
+  } catch (const std::bad_alloc&) {
+    st = fail(CVA_E_ARG, "out of host memory while building the plan");
+  }
+  if (st != CVA_OK) {
+    delete p;
+    return st;
+  }
+  *out = reinterpret_cast<cva_plan*>(p);
+  return CVA_OK;
+}
+
+void cva_plan_destroy(cva_plan* plan) { delete reinterpret_cast<Plan*>(plan); }
+
+cva_status cva_plan_get_metadata(const cva_plan* plan, cva_metadata* out) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p == nullptr || out == nullptr) return fail(CVA_E_ARG, "plan or out is NULL");
+  out->local_tokens = p->T_loc;
+  out->global_tokens = p->T;
+  out->n_seqs = p->n_seqs;
+  out->n_segments = 2 * p->n_seqs;
+  out->cp_size = p->cp_size;
+  out->rank = p->rank;
+  out->local_cu = p->local_cu.data();
+  out->actual_seq_qlen = p->aq.data();
+  out->actual_seq_kvlen = p->akv.data();
+  out->kv_index = p->kv_index.data();
+  out->seg_q_pos0 = p->seg_q_pos0.data();
+  out->kv_index_len = (int64_t)p->kv_index.size();
+  out->workload_per_rank = p->workload.data();
+  out->visible_pairs = p->visible_pairs;
+  out->fwd_tiles = p->fwd.tile_pairs;
+  return CVA_OK;
+}
+
+size_t cva_plan_device_bytes(const cva_plan* plan) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  return p == nullptr ? 0 : (size_t)p->layout.total * sizeof(int32_t);
+}
+
+cva_status cva_plan_upload(cva_plan* plan, void* dev_buf, size_t bytes, void* stream) {
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (p == nullptr || dev_buf == nullptr) return fail(CVA_E_ARG, "plan or dev_buf is NULL");
+  const size_t need = (size_t)p->layout.total * sizeof(int32_t);
+  if (bytes < need) {
+    std::ostringstream os;
+    os << "device buffer too small: " << bytes << " < " << need;
+    return fail(CVA_E_ARG, os.str());
+  }
+  if (((uintptr_t)dev_buf) % 256 != 0) return fail(CVA_E_ARG, "device buffer must be 256-byte aligned");
+  hipError_t e = hipMemcpyAsync(dev_buf, p->blob.data(), need, hipMemcpyHostToDevice,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
+  // the copy reads the host blob, which the plan keeps alive; make it complete
+  // before returning so the caller may reuse pageable memory freely
+  e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan upload)");
+  p->dev = dev_buf;
+  p->dev_bytes = bytes;
+  return CVA_OK;
+}
+
+cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                   void* o, float* lse, float softmax_scale, void* stream) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  cva_status st = check_ready(p);
+  if (st != CVA_OK) return st;
+  if (q == nullptr || k_rm == nullptr || v_rm == nullptr || o == nullptr || lse == nullptr)
+    return fail(CVA_E_ARG, "a tensor pointer is NULL");
+  if ((st = check_scale(softmax_scale)) != CVA_OK) return st;
+  cva::FwdParams fp;
+  fp.q = q;
+  fp.k = k_rm;
+  fp.v = v_rm;
+  fp.o = o;
+  fp.lse = lse;
+  fp.t = tables(*p);
+  fp.n_tiles = p->fwd.n_tiles();
+  fp.heads_per_tile = p->fwd_heads_per_tile;
+  fp.n_head_groups = p->hq / p->fwd_heads_per_tile;
+  fp.hq = p->hq;
+  fp.hkv = p->hkv;
+  fp.group = p->hq / p->hkv;
+  fp.t_loc = (int32_t)p->T_loc;
+  fp.tile_q = p->fwd.tile_q;
+  fp.tile_kv = p->fwd.tile_kv;
+  fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = cva::launch_fwd(p->dtype, p->d_qk, p->d_v, fp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
+  return CVA_OK;
+}
+
+size_t cva_bwd_workspace_bytes(const cva_plan* plan) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p == nullptr) return 0;
+  return (size_t)p->T_loc * p->hq * sizeof(float);
+}
+
+cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                   const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
+                   void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
+                   void* stream) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  cva_status st = check_ready(p);
+  if (st != CVA_OK) return st;
+  if (q == nullptr || k_rm == nullptr || v_rm == nullptr || o == nullptr || lse == nullptr ||
+      dout == nullptr || dq == nullptr || dk_rm == nullptr || dv_rm == nullptr)
+    return fail(CVA_E_ARG, "a tensor pointer is NULL");
+  if ((st = check_scale(softmax_scale)) != CVA_OK) return st;
+  if (p->dtype == CVA_FP32) return fail(CVA_E_UNSUPPORTED, "backward is implemented for bf16 and fp16");
+  const size_t need = cva_bwd_workspace_bytes(plan);
+  if (workspace == nullptr || ws_bytes < need) {
+    std::ostringstream os;
+    os << "workspace needs " << need << " bytes";
+    return fail(CVA_E_WORKSPACE, os.str());
+  }
+  cva::BwdParams bp;
+  bp.q = q;
+  bp.k = k_rm;
+  bp.v = v_rm;
+  bp.o = o;
+  bp.lse = lse;
+  bp.dout = dout;
+  bp.dq = dq;
+  bp.dk = dk_rm;
+  bp.dv = dv_rm;
+  bp.delta = (float*)workspace;
+  bp.t = tables(*p);
+  bp.n_dq_tiles = p->dq.n_tiles();
+  bp.n_kv_tiles = p->dkdv.n_tiles();
+  bp.n_zero_ranges = (int32_t)(p->zero_rows.size() / 2);
+  bp.hq = p->hq;
+  bp.hkv = p->hkv;
+  bp.group = p->hq / p->hkv;
+  bp.t_loc = (int32_t)p->T_loc;
+  bp.t_total = p->T;
+  bp.scale = softmax_scale;
+  bp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = cva::launch_bwd(p->dtype, p->d_qk, p->d_v, bp, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "backward launch");
+  return CVA_OK;
+}
+
+cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p == nullptr || out == nullptr) return fail(CVA_E_ARG, "plan or out is NULL");
+  const cva::Schedule* s = which == 0 ? &p->fwd : which == 1 ? &p->dq : which == 2 ? &p->dkdv : nullptr;
+  if (s == nullptr) return fail(CVA_E_ARG, "which must be 0, 1 or 2");
+  out->tile_q = s->tile_q;
+  out->tile_kv = s->tile_kv;
+  out->n_tiles = s->n_tiles();
+  out->n_spans = s->n_spans();
+  out->tiles = s->tiles.data();
+  out->spans = s->spans.data();
+  return CVA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Host-side plan: validation, metadata and tile schedules for one CP rank.
+// Pure C++17; no HIP calls, so it builds and runs on a machine without a GPU.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "cva.h"
+
+namespace cva {
+
+// Per-segment record as laid out in the device blob (8 int32 each).
+// A segment is one (sub-sequence, chunk) pair of this rank, in local order.
+enum SegField {
+  SEG_SEQ = 0,     // sub-sequence index
+  SEG_CHUNK = 1,   // chunk id j (r or 2R-1-r)
+  SEG_QLEN = 2,    // queries in the segment (= chunk length c)
+  SEG_KVLEN = 3,   // causal K/V prefix length (j+1)*c
+  SEG_QROW0 = 4,   // local row of the first query
+  SEG_KVOFF = 5,   // offset of the segment's prefix in kv_index
+  SEG_QPOS0 = 6,   // in-sequence position of the first query (j*c)
+  SEG_SEQLEN = 7,  // length of the sub-sequence
+  SEG_INTS = 8
+};
+
+// Q-stationary tile record (forward and backward dQ), 5 int32.
+enum QTileField { QT_SEG = 0, QT_Q0 = 1, QT_ROWS = 2, QT_SPAN0 = 3, QT_NSPAN = 4, QT_INTS = 5 };
+// K/V-stationary tile record (backward dK/dV), 5 int32.
+enum KvTileField { KT_SEQ = 0, KT_K0 = 1, KT_KEYS = 2, KT_SPAN0 = 3, KT_NSPAN = 4, KT_INTS = 5 };
+// Span record, 4 int32.  Q-stationary: {kv tile begin, kv tile end, partial, 0}.
+// K/V-stationary: {segment, q tile begin, q tile end, partial}.
+enum { SPAN_INTS = 4 };
+
+struct Schedule {
+  int32_t tile_q = 0;   // query positions per Q tile
+  int32_t tile_kv = 0;  // keys per K/V tile
+  std::vector<int32_t> tiles;  // [n][5], launch order (most work first)
+  std::vector<int32_t> spans;  // [m][4]
+  int64_t tile_pairs = 0;      // non-empty (Q tile, K/V tile) pairs
+  int32_t n_tiles() const { return (int32_t)(tiles.size() / 5); }
+  int32_t n_spans() const { return (int32_t)(spans.size() / SPAN_INTS); }
+};
+
+// Offsets (in int32 elements) of the tables inside the device blob.
+struct BlobLayout {
+  int64_t segs = 0, kv_index = 0, row_iv = 0;
+  int64_t fwd_tiles = 0, fwd_spans = 0;
+  int64_t dq_tiles = 0, dq_spans = 0;
+  int64_t kv_tiles = 0, kv_spans = 0;
+  int64_t zero_rows = 0;
+  int64_t total = 0;
+};
+
+struct Plan {
+  // request
+  int32_t n_seqs = 0, cp_size = 1, rank = 0;
+  int32_t hq = 0, hkv = 0, d_qk = 0, d_v = 0, dtype = 0;
+  int32_t mask_type = CVA_MASK_CAUSAL, sink = 0, window = 0, n_branches = 0;
+  std::vector<int32_t> cu;             // [n+1]
+  std::vector<int32_t> branch_bounds;  // [n][n_branches+1] (shared prefix)
+
+  // metadata
+  int64_t T = 0, T_loc = 0;
+  std::vector<int32_t> local_cu, aq, akv, kv_index, seg_q_pos0;
+  std::vector<int64_t> workload;
+  int64_t visible_pairs = 0;
+  std::vector<int32_t> segs;    // [2n][8]
+  std::vector<int32_t> row_iv;  // [T_loc][4]: visible keys = [a0,a1) u [b0,b1)
+
+  // kernel configuration + schedules
+  int32_t fwd_heads_per_tile = 1;  // query heads of one K/V group sharing a forward work-group
+  Schedule fwd, dq, dkdv;
+  std::vector<int32_t> zero_rows;  // [m][2] rank-major row ranges no local query sees
+
+  // device copy
+  std::vector<int32_t> blob;
+  BlobLayout layout;
+  void* dev = nullptr;
+  size_t dev_bytes = 0;
+};
+
+// Thread-local error message used by the C ABI.
+void set_error(const std::string& msg);
+const char* last_error();
+
+// validate.cpp
+cva_status validate_request(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp_size,
+                            int32_t rank, const cva_mask_desc* mask, int32_t hq, int32_t hkv,
+                            int32_t d_qk, int32_t d_v, int32_t dtype);
+
+// metadata.cpp
+cva_status build_metadata(Plan& p);
+
+// schedule.cpp
+void row_intervals(const Plan& p, int seg, int32_t a, int32_t iv[4]);
+cva_status build_schedules(Plan& p);
+void build_blob(Plan& p);
+
+// Tile shape of the forward kernel for a plan's head shape.
+struct FwdShape {
+  int32_t heads_per_tile;  // query heads per work-group (share one K/V head)
+  int32_t tile_q;          // query positions per work-group
+  int32_t tile_kv;
+};
+FwdShape forward_shape(const Plan& p);
+
+constexpr int32_t kWavesPerFwdTile = 4;
+constexpr int32_t kRowsPerWave = 32;
+constexpr int32_t kFwdTileKv = 64;
+constexpr int32_t kBwdTileQ = 64;
+constexpr int32_t kBwdTileKv = 64;
+
+}  // namespace cva

@@ -1,0 +1,71 @@
+// Device helpers for the gfx950 attention kernels: MFMA wrappers, 16-bit
+// element types, LDS fragments, cross-half-wave exchange.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace cva {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// 16-bit element type tag: bf16 or fp16.  Values travel as raw bits (uint16 /
+// packed uint32) and are reinterpreted only at the MFMA and at conversions.
+struct Bf16 {
+  using vec8 = bf16x8_t;
+  __device__ static inline f32x16_t mfma32(vec8 a, vec8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline uint16_t from_float(float x) {
+    __bf16 h = (__bf16)x;
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static inline float to_float(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+  }
+};
+
+struct Fp16 {
+  using vec8 = f16x8_t;
+  __device__ static inline f32x16_t mfma32(vec8 a, vec8 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline uint16_t from_float(float x) {
+    _Float16 h = (_Float16)x;
+    return __builtin_bit_cast(uint16_t, h);
+  }
+  __device__ static inline float to_float(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+};
+
+template <typename E>
+__device__ inline typename E::vec8 as_vec8(u32x4_t x) {
+  return __builtin_bit_cast(typename E::vec8, x);
+}
+
+template <typename E>
+__device__ inline uint32_t pack2(float lo, float hi) {
+  return (uint32_t)E::from_float(lo) | ((uint32_t)E::from_float(hi) << 16);
+}
+
+// Value held by lane (l ^ 32): the two half-waves of a 32x32 MFMA output hold
+// different rows of the same column.
+__device__ inline float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ inline f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+}  // namespace cva

@@ -1,0 +1,65 @@
+// Kernel parameter blocks and launchers shared by the C ABI and the HIP kernels.
+#pragma once
+
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+namespace cva {
+
+// Device tables of a plan (int32, see plan.hpp for the record layouts).
+struct PlanTables {
+  const int32_t* segs;
+  const int32_t* kv_index;
+  const int32_t* row_iv;
+  const int32_t* fwd_tiles;
+  const int32_t* fwd_spans;
+  const int32_t* dq_tiles;
+  const int32_t* dq_spans;
+  const int32_t* kv_tiles;
+  const int32_t* kv_spans;
+  const int32_t* zero_rows;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  PlanTables t;
+  int32_t n_tiles;         // forward Q tiles
+  int32_t n_head_groups;   // hq / heads_per_tile
+  int32_t heads_per_tile;
+  int32_t hq, hkv, group;  // group = hq / hkv
+  int32_t t_loc;
+  int32_t tile_q;
+  int32_t tile_kv;
+  float scale_log2;        // softmax_scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;            // [hq, t_loc] workspace
+  PlanTables t;
+  int32_t n_dq_tiles, n_kv_tiles, n_zero_ranges;
+  int32_t hq, hkv, group;
+  int32_t t_loc;
+  int64_t t_total;
+  float scale;             // softmax_scale
+  float scale_log2;        // softmax_scale * log2(e)
+};
+
+// dtype: 0 bf16, 1 fp16, 2 fp32.  Return hipSuccess or the launch error.
+hipError_t launch_fwd(int dtype, int d_qk, int d_v, const FwdParams& p, hipStream_t stream);
+hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t stream);
+
+}  // namespace cva

@@ -1,0 +1,198 @@
+/*
+ * cva.h -- C ABI of libcva: one context-parallel rank's share of packed
+ * variable-length (THD) attention with online softmax, for AMD MI355X (gfx950).
+ *
+ * The operation (MindSpeed RFC "EOD-aware load balancing for KVAllGather CP
+ * with THD", gitcode Ascend/MindSpeed issue 232):
+ *   - every EOD sub-sequence of a packed batch is cut into 2*cp_size equal
+ *     chunks and rank r holds chunks r and 2*cp_size-r-1 (section 2);
+ *   - K/V of all ranks are all-gathered in rank order ("rank-major"), and each
+ *     local Q chunk attends to its causal K/V prefix, selected from the
+ *     rank-major K/V by a direct index; both local chunks of every
+ *     sub-sequence run in one fused attention call (section 3.1, 3.3);
+ *   - the backward adds dK/dV into a rank-major gradient buffer through the
+ *     same index (section 3.1).
+ * The attention itself is masked softmax attention evaluated block-wise with
+ * the online-softmax trick (DCP paper, background section and its block-wise
+ * listing); besides causal/EOD-reset it supports the DCP paper's lambda mask
+ * (attention sink + sliding window) and shared-question mask (sparse-mask
+ * section, Fig. 6(b) and 6(d)).
+ *
+ * Conventions shared by every call:
+ *   - Every call returns a cva_status.  On any error nothing has been
+ *     enqueued on the GPU, and cva_last_error() returns a message for the
+ *     calling thread.
+ *   - Tensors are caller-owned, contiguous, row-major, in device memory:
+ *       q     [T_loc, Hq,  Dqk]   local queries (this rank's two chunks of
+ *                                 every sub-sequence, local order)
+ *       k_rm  [T,     Hkv, Dqk]   rank-major gathered keys
+ *       v_rm  [T,     Hkv, Dv ]   rank-major gathered values
+ *       o     [T_loc, Hq,  Dv ]   output, same dtype as q
+ *       lse   [Hq, T_loc] float   natural-log sum-exp of the scaled logits
+ *     with T = cu_seqlens[n], T_loc = T / cp_size.  Query head h uses K/V head
+ *     h / (Hq/Hkv) (grouped-query attention, contiguous groups).
+ *   - A stream argument is a hipStream_t passed as void* (NULL: the null
+ *     stream).  Kernel calls are asynchronous on it.
+ *   - Plans are built on the host from (cu_seqlens, cp_size, rank, mask,
+ *     head shape, dtype), are immutable afterwards except for binding their
+ *     device copy with cva_plan_upload, and can be reused for every layer that
+ *     sees the same batch (the RFC caches the same metadata, section 3.3).
+ */
+#ifndef CVA_H
+#define CVA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CVA_OK = 0,
+  CVA_E_ARG = 1,          /* null pointer, negative count, bad size argument    */
+  CVA_E_CU_SEQLENS = 2,   /* empty, not starting at 0, or not strictly increasing */
+  CVA_E_ALIGN = 3,        /* a sub-sequence length not divisible by 2*cp_size    */
+  CVA_E_RANK = 4,         /* cp_size < 1 or rank outside [0, cp_size)            */
+  CVA_E_HEADS = 5,        /* Hq or Hkv < 1, or Hq not a multiple of Hkv          */
+  CVA_E_HEADDIM = 6,      /* head dims not supported (Dqk < Dv, or no kernel)    */
+  CVA_E_DTYPE = 7,        /* unknown dtype                                        */
+  CVA_E_MASK = 8,         /* bad mask descriptor                                  */
+  CVA_E_UNSUPPORTED = 9,  /* valid request that this build does not implement     */
+  CVA_E_WORKLOAD = 10,    /* per-rank sum(q_len*kv_len) not equal (never for valid input) */
+  CVA_E_HIP = 11,         /* a HIP runtime call failed                            */
+  CVA_E_SCALE = 12,       /* softmax_scale not finite or not > 0                  */
+  CVA_E_WORKSPACE = 13,   /* workspace missing or too small                       */
+  CVA_E_NOT_UPLOADED = 14 /* the plan has no device copy yet (cva_plan_upload)    */
+} cva_status;
+
+typedef enum { CVA_BF16 = 0, CVA_FP16 = 1, CVA_FP32 = 2 } cva_dtype;
+
+typedef enum {
+  CVA_MASK_CAUSAL = 0,        /* key k visible to query q iff k <= q (positions within the sub-sequence) */
+  CVA_MASK_LAMBDA = 1,        /* causal and (k < sink or q - k < window)                                 */
+  CVA_MASK_SHARED_PREFIX = 2  /* prefix rows causal; an answer row sees the prefix and itself causally   */
+} cva_mask_type;
+
+/* Mask descriptor, copied into the plan by cva_plan_create.
+ *   type          cva_mask_type
+ *   sink, window  lambda mask only: sink >= 0, window >= 1
+ *   n_branches    shared-prefix only: answers per sequence, >= 1
+ *   branch_bounds shared-prefix only: int32 [n_seqs][n_branches + 1], per sequence
+ *                 {prefix_end, end_of_answer_0, ..., end_of_answer_{n_branches-1}}
+ *                 as in-sequence positions, non-decreasing, last == sequence length.
+ *                 Caller-owned, read only during cva_plan_create.
+ * A NULL descriptor means causal. */
+typedef struct {
+  int32_t type;
+  int32_t sink;
+  int32_t window;
+  int32_t n_branches;
+  const int32_t* branch_bounds;
+} cva_mask_desc;
+
+typedef struct cva_plan cva_plan;
+
+/* Metadata of one rank (RFC interface get_thd_load_balanced_cp_metadata,
+ * section 3.5.2.1).  All arrays are owned by the plan and live as long as it.
+ *   local_cu          [n_seqs+1]      cu_seqlens / cp_size: local offsets of the sub-sequences
+ *   actual_seq_qlen   [n_segments+1]  cumulative query lengths, leading 0; segment 2i is
+ *                                     chunk r of sub-sequence i, segment 2i+1 chunk 2R-1-r
+ *   actual_seq_kvlen  [n_segments+1]  cumulative K/V prefix lengths, leading 0
+ *   kv_index          [kv_index_len]  rank-major row of every prefix position, segment by
+ *                                     segment, positions 0..kv_len-1 in order
+ *   seg_q_pos0        [n_segments]    in-sequence position of each segment's first query
+ *   workload_per_rank [cp_size]       sum(q_len * kv_len) of every rank (all equal)
+ *   visible_pairs     unmasked (query, key) pairs of this rank, per query head
+ *   fwd_tiles         non-empty (Q tile, K/V tile) pairs the forward schedule visits, per item head group */
+typedef struct {
+  int64_t local_tokens;
+  int64_t global_tokens;
+  int32_t n_seqs;
+  int32_t n_segments;
+  int32_t cp_size;
+  int32_t rank;
+  const int32_t* local_cu;
+  const int32_t* actual_seq_qlen;
+  const int32_t* actual_seq_kvlen;
+  const int32_t* kv_index;
+  const int32_t* seg_q_pos0;
+  int64_t kv_index_len;
+  const int64_t* workload_per_rank;
+  int64_t visible_pairs;
+  int64_t fwd_tiles;
+} cva_metadata;
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* cva_last_error(void);
+
+/* Build a plan on the host: validate (RFC section 2 usage limits and section
+ * 3.4 reliability: sequence, rank, head and head-dim checks before any device
+ * work), build the metadata and the tile schedules.  dtype is a cva_dtype.
+ * Supported head dims: (Dqk, Dv) in {(64,64), (128,128), (192,128)} for bf16/fp16
+ * and any Dqk >= Dv with Dqk, Dv <= 256 for fp32 (forward only).
+ * On success *out owns a new plan (release with cva_plan_destroy). */
+cva_status cva_plan_create(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp_size,
+                           int32_t rank, const cva_mask_desc* mask, int32_t hq, int32_t hkv,
+                           int32_t d_qk, int32_t d_v, int32_t dtype, cva_plan** out);
+
+void cva_plan_destroy(cva_plan* plan);
+
+/* Fill *out with views of the plan's host metadata. */
+cva_status cva_plan_get_metadata(const cva_plan* plan, cva_metadata* out);
+
+/* Bytes of device memory the plan's tables need (4-byte aligned blob). */
+size_t cva_plan_device_bytes(const cva_plan* plan);
+
+/* Copy the plan's tables to caller-owned device memory dev_buf (at least
+ * cva_plan_device_bytes bytes, 256-byte aligned) on `stream`, and bind the plan
+ * to that buffer for later cva_fwd / cva_bwd calls.  The buffer must stay
+ * alive and untouched while those calls may run. */
+cva_status cva_plan_upload(cva_plan* plan, void* dev_buf, size_t bytes, void* stream);
+
+/* Forward (RFC interface AttnFuncWithCPAndKVAllGatherForTHDLoadBalanced,
+ * section 3.5.2.2, forward half; k/v arrive already gathered rank-major):
+ * o = softmax(scale * q k^T masked) v for this rank's rows, plus lse.
+ * softmax_scale must be finite and > 0 (the binding maps None to 1/sqrt(Dqk)). */
+cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                   void* o, float* lse, float softmax_scale, void* stream);
+
+/* Workspace bytes cva_bwd needs (fp32 row statistics). */
+size_t cva_bwd_workspace_bytes(const cva_plan* plan);
+
+/* Backward (same interface, backward half): given dout [T_loc, Hq, Dv] and the
+ * forward's o and lse, write dq [T_loc, Hq, Dqk] and the rank-major
+ * dk_rm [T, Hkv, Dqk], dv_rm [T, Hkv, Dv].  dk_rm/dv_rm are fully written:
+ * rows no local query attends to are zero, so the result equals index_add_ of
+ * the per-segment gradients into a zeroed buffer (RFC section 3.1).
+ * Deterministic: no atomics, fixed summation order.  bf16/fp16 only. */
+cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                    const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
+                    void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
+                    void* stream);
+
+/* Schedule introspection for tests and tools.  which: 0 forward, 1 backward dQ,
+ * 2 backward dK/dV.  Returns the tile sizes and a host view of the schedule:
+ *   forward / dQ:  q tiles {segment, first local query of the tile (segment-relative),
+ *                  rows in tile, span_begin, span_count}; spans {first K/V tile,
+ *                  end K/V tile, partial flag} in units of tile_kv keys.
+ *   dK/dV:         kv tiles {sequence, first key position, keys in tile, span_begin,
+ *                  span_count}; spans {segment, first q tile, end q tile, partial flag}
+ *                  with q tiles of tile_q rows counted from the segment start.
+ * Arrays are owned by the plan. */
+typedef struct {
+  int32_t tile_q;
+  int32_t tile_kv;
+  int32_t n_tiles;
+  int32_t n_spans;
+  const int32_t* tiles; /* [n_tiles][5] */
+  const int32_t* spans; /* [n_spans][4] */
+} cva_schedule;
+
+cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CVA_H */

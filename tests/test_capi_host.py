@@ -1,0 +1,255 @@
+"""libcva host side on the CPU: exports, metadata, schedules, validation.
+
+No GPU is touched: plan creation is host-only C++.  Metadata must equal the
+oracle's enumeration bit for bit; the tile schedules must visit exactly the
+(Q tile, K/V tile) pairs where the oracle's materialised mask is not all
+zero, and call a tile full exactly when every element is visible.
+"""
+import ctypes
+import random
+import re
+import os
+
+import numpy as np
+import pytest
+
+import context_varlen_attention_amd as cva
+import oracle
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "cva.h")
+
+
+def test_library_exports_every_declared_symbol():
+    names = set(re.findall(r"\b(cva_[a-z_]+)\s*\(", open(HEADER).read()))
+    assert names, "no declarations parsed"
+    lib = ctypes.CDLL(cva.library_path())
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} declared in cva.h but not exported"
+    assert names == set(cva.EXPORTS)
+
+
+def _random_cu(rng, R, n_max=6, c_max=40):
+    n = rng.randint(1, n_max)
+    return [0] + list(np.cumsum([2 * R * rng.randint(1, c_max) for _ in range(n)]))
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4, 8])
+def test_metadata_bit_exact(R):
+    rng = random.Random(1234 + R)
+    for _ in range(8):
+        cu = _random_cu(rng, R)
+        for r in range(R):
+            md = cva.Plan(cu, R, r, 4, 2, 128, 128, "bf16").metadata
+            ref = oracle.metadata_ref(cu, R, r)
+            for key in ("local_cu", "actual_seq_qlen", "actual_seq_kvlen", "kv_index",
+                        "seg_q_pos0", "workload_per_rank"):
+                assert np.array_equal(md[key], ref[key]), (cu, R, r, key)
+            assert md["local_tokens"] == ref["local_tokens"]
+            assert md["global_tokens"] == ref["global_tokens"]
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa16k", "long128k", "mla32k"])
+def test_metadata_bit_exact_workloads(name):
+    w = synth.make_workload(name)
+    md = cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, "bf16").metadata
+    ref = oracle.metadata_ref(w.cu_seqlens, w.cp_size, w.rank)
+    for key in ("local_cu", "actual_seq_qlen", "actual_seq_kvlen", "kv_index", "seg_q_pos0",
+                "workload_per_rank"):
+        assert np.array_equal(md[key], ref[key]), key
+
+
+def test_split_helpers_match_oracle():
+    rng = random.Random(9)
+    for R in (1, 2, 4):
+        cu = _random_cu(rng, R)
+        for r in range(R):
+            assert cva.local_token_ids(cu, R, r).tolist() == oracle.rank_local_positions(cu, R, r)
+        assert cva.rank_major_token_ids(cu, R).tolist() == oracle.split.rank_major_order(cu, R)
+
+
+def _wl(lens, R, r, mask, hq=4, hkv=4, **kw):
+    return synth.custom_workload(lens, R, r, hq, hkv, 128, 128, "bf16", mask=mask, **kw)
+
+
+def _plan(w):
+    return cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype,
+                    mask=w.mask, sink=w.sink, window=w.window,
+                    branch_bounds=None if w.branch_bounds is None else w.branch_bounds)
+
+
+MASK_CASES = [
+    ([64, 128, 64], 2, 0, "causal", {}),
+    ([8, 24, 200, 16, 1000], 4, 3, "causal", {}),
+    ([1024, 640], 1, 0, "lambda", dict(sink=64, window=256)),
+    ([1200, 400], 2, 1, "lambda", dict(sink=5, window=77)),
+    ([640, 832], 2, 0, "lambda", dict(sink=0, window=100)),
+    ([1280, 768], 1, 0, "shared_prefix",
+     dict(branch_bounds=[[256, 512, 768, 1024, 1280], [128, 288, 448, 608, 768]])),
+    ([1280, 768], 2, 1, "shared_prefix",
+     dict(branch_bounds=[[200, 300, 300, 900, 1280], [0, 100, 400, 500, 768]])),
+]
+
+
+def _oracle_segments(w):
+    """(sub-sequence, in-sequence q positions, kv_len) per segment, from the oracle's split."""
+    md = oracle.metadata_ref(w.cu_seqlens, w.cp_size, w.rank)
+    aq, akv, pos0 = md["actual_seq_qlen"], md["actual_seq_kvlen"], md["seg_q_pos0"]
+    out = []
+    for s in range(len(pos0)):
+        n = aq[s + 1] - aq[s]
+        out.append((s // 2, pos0[s] + np.arange(n), akv[s + 1] - akv[s]))
+    return out
+
+
+def _mask_rows(w, i, pos):
+    L = int(w.cu_seqlens[i + 1] - w.cu_seqlens[i])
+    b = None if w.branch_bounds is None else w.branch_bounds[i]
+    return oracle.masks.mask_rows_ref(w.mask, L, pos, w.sink, w.window, b)
+
+
+@pytest.mark.parametrize("ci", range(len(MASK_CASES)))
+@pytest.mark.parametrize("which", [0, 1])
+def test_q_schedule_covers_exactly_nonempty_tiles(ci, which):
+    lens, R, r, mask, ex = MASK_CASES[ci]
+    w = _wl(lens, R, r, mask, **ex)
+    plan = _plan(w)
+    tq, tk, tiles, spans = plan.schedule(which)
+    segs = _oracle_segments(w)
+    got = {}
+    for seg, q0, rows, s0, ns in tiles:
+        assert rows == min(tq, len(segs[seg][1]) - q0)
+        for a, b, partial, _ in spans[s0: s0 + ns]:
+            for t in range(a, b):
+                assert (seg, q0, t) not in got
+                got[(seg, q0, t)] = bool(partial)
+    exp = {}
+    for seg, (i, pos, kv_len) in enumerate(segs):
+        M = _mask_rows(w, i, pos)
+        for q0 in range(0, len(pos), tq):
+            blk = M[q0: q0 + tq, :kv_len]
+            for t in range((kv_len + tk - 1) // tk):
+                sub = blk[:, t * tk: (t + 1) * tk]
+                if sub.any():
+                    exp[(seg, q0, t)] = not (sub.all() and sub.shape[1] == tk)
+    assert got == exp
+
+
+@pytest.mark.parametrize("ci", range(len(MASK_CASES)))
+def test_kv_schedule_covers_exactly_nonempty_tiles(ci):
+    lens, R, r, mask, ex = MASK_CASES[ci]
+    w = _wl(lens, R, r, mask, **ex)
+    plan = _plan(w)
+    tq, tk, tiles, spans = plan.schedule(2)
+    segs = _oracle_segments(w)
+    got = {}
+    seen_tiles = set()
+    for seq, k0, keys, s0, ns in tiles:
+        assert k0 % tk == 0
+        seen_tiles.add((seq, k0 // tk))
+        for seg, qa, qb, partial in spans[s0: s0 + ns]:
+            assert segs[seg][0] == seq
+            for qt in range(qa, qb):
+                got[(seg, qt, k0 // tk)] = bool(partial)
+    exp = {}
+    for seg, (i, pos, kv_len) in enumerate(segs):
+        M = _mask_rows(w, i, pos)
+        for qt in range((len(pos) + tq - 1) // tq):
+            blk = M[qt * tq: (qt + 1) * tq, :kv_len]
+            for t in range((kv_len + tk - 1) // tk):
+                sub = blk[:, t * tk: (t + 1) * tk]
+                if sub.any():
+                    exp[(seg, qt, t)] = not (sub.all() and sub.shape[1] == tk)
+    assert got == exp
+    # every K/V tile of every sub-sequence's longest prefix has a record
+    for seg in range(1, len(segs), 2):
+        i, _, kv_len = segs[seg]
+        for t in range((kv_len + tk - 1) // tk):
+            assert (i, t) in seen_tiles
+
+
+@pytest.mark.parametrize("ci", range(len(MASK_CASES)))
+def test_visible_pairs_match_oracle(ci):
+    lens, R, r, mask, ex = MASK_CASES[ci]
+    w = _wl(lens, R, r, mask, **ex)
+    assert _plan(w).visible_pairs() == oracle.visible_pairs_ref(w)
+
+
+def test_causal_visible_pairs_closed_form():
+    for name in ("gqa16k", "long128k", "mla32k"):
+        w = synth.make_workload(name)
+        L = w.lengths.astype(np.int64)
+        p = cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, "bf16")
+        assert p.visible_pairs() == int((L * (L + 1)).sum() // (2 * w.cp_size))
+
+
+def test_sparse_visible_pairs_closed_form():
+    w = synth.make_workload("sparse8", mask="lambda")
+    p = _plan(w)
+    exp = 0
+    for L in w.lengths:
+        q = np.arange(L)
+        exp += int(np.where(q < 4096, q + 1, 4096 + np.minimum(64, q - 4095)).sum())
+    assert p.visible_pairs() == exp
+    w = synth.make_workload("sparse8", mask="shared_prefix")
+    exp = 0
+    for b in w.branch_bounds:
+        P = int(b[0])
+        exp += P * (P + 1) // 2
+        for s, e in zip(b[:-1], b[1:]):
+            n = int(e - s)
+            exp += n * P + n * (n + 1) // 2
+    assert _plan(w).visible_pairs() == exp
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(cu=[0]), "CVA_E_CU_SEQLENS"),
+    (dict(cu=[4, 12]), "CVA_E_CU_SEQLENS"),
+    (dict(cu=[0, 8, 8]), "CVA_E_CU_SEQLENS"),
+    (dict(cu=[0, 8, 4]), "CVA_E_CU_SEQLENS"),
+    (dict(cu=[0, 6], R=2), "CVA_E_ALIGN"),
+    (dict(R=0), "CVA_E_RANK"),
+    (dict(R=2, r=2), "CVA_E_RANK"),
+    (dict(r=-1), "CVA_E_RANK"),
+    (dict(hq=6, hkv=4), "CVA_E_HEADS"),
+    (dict(hq=0), "CVA_E_HEADS"),
+    (dict(d_qk=64, d_v=128), "CVA_E_HEADDIM"),
+    (dict(d_qk=96, d_v=96), "CVA_E_HEADDIM"),
+    (dict(mask="lambda", window=0), "CVA_E_MASK"),
+    (dict(mask="lambda", sink=-1, window=4), "CVA_E_MASK"),
+    (dict(mask="shared_prefix", bounds=[[4, 2, 16]]), "CVA_E_MASK"),
+    (dict(mask="shared_prefix", bounds=[[4, 8, 15]]), "CVA_E_MASK"),
+])
+def test_invalid_requests_rejected(kw, status):
+    args = dict(cu=[0, 16], R=1, r=0, hq=4, hkv=2, d_qk=128, d_v=128, mask="causal", sink=0,
+                window=0, bounds=None)
+    args.update(kw)
+    with pytest.raises(cva.CvaError) as ei:
+        cva.Plan(args["cu"], args["R"], args["r"], args["hq"], args["hkv"], args["d_qk"],
+                 args["d_v"], "bf16", mask=args["mask"], sink=args["sink"],
+                 window=args["window"], branch_bounds=args["bounds"])
+    assert ei.value.status_name == status, str(ei.value)
+
+
+def test_errors_before_device_work():
+    """Calls that need a device copy refuse a plan that has none, without touching HIP."""
+    lib = cva.load_library()
+    p = cva.Plan([0, 64], 1, 0, 2, 2, 64, 64, "bf16")
+    vp = ctypes.c_void_p
+    st = lib.cva_fwd(p.handle, vp(16), vp(16), vp(16), vp(16), vp(16), 0.125, None)
+    assert cva.STATUS[st] == "CVA_E_NOT_UPLOADED"
+    st = lib.cva_bwd(p.handle, *([vp(16)] * 9), vp(16), 1 << 20, 0.125, None)
+    assert cva.STATUS[st] == "CVA_E_NOT_UPLOADED"
+    assert "cva_plan_upload" in lib.cva_last_error().decode()
+    assert lib.cva_plan_upload(p.handle, None, 0, None) == 1
+
+
+def test_zero_rows_complement_prefixes():
+    """Rank-major rows that dK/dV zero-fills are exactly those outside every prefix."""
+    for R, r in ((2, 0), (2, 1), (4, 2), (1, 0)):
+        cu = [0, 8 * R, 24 * R, 32 * R]
+        md = oracle.metadata_ref(cu, R, r)
+        covered = np.zeros(cu[-1], bool)
+        covered[md["kv_index"]] = True
+        # chunks of positions >= (2R - r) c belong to ranks < r (their second chunk)
+        assert covered.sum() == sum((2 * R - r) * (cu[i + 1] - cu[i]) // (2 * R) for i in range(3))
