@@ -229,6 +229,8 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   bp.n_dq_tiles = p->dq.n_tiles();
   bp.n_kv_tiles = p->dkdv.n_tiles();
   bp.n_zero_ranges = (int32_t)(p->zero_rows.size() / 2);
+  bp.dq_heads_per_tile = p->fwd_heads_per_tile;
+  bp.dq_head_groups = p->hq / p->fwd_heads_per_tile;
   bp.hq = p->hq;
   bp.hkv = p->hkv;
   bp.group = p->hq / p->hkv;

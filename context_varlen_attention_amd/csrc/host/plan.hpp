@@ -108,7 +108,8 @@ FwdShape forward_shape(const Plan& p);
 constexpr int32_t kWavesPerFwdTile = 4;
 constexpr int32_t kRowsPerWave = 32;
 constexpr int32_t kFwdTileKv = 64;
-constexpr int32_t kBwdTileQ = 64;
-constexpr int32_t kBwdTileKv = 64;
+constexpr int32_t kDqTileKv = 64;     // dQ kernel: keys per K/V tile (query tile as forward)
+constexpr int32_t kDkvTileQ = 64;     // dK/dV kernel: queries per Q tile
+constexpr int32_t kDkvTileKv = 128;   // dK/dV kernel: keys per work-group (4 waves x 32)
 
 }  // namespace cva

@@ -243,8 +243,8 @@ cva_status build_schedules(Plan& p) {
   FwdShape fs = forward_shape(p);
   p.fwd_heads_per_tile = fs.heads_per_tile;
   build_q_schedule(p, p.fwd, fs.tile_q, fs.tile_kv);
-  build_q_schedule(p, p.dq, kBwdTileQ, kBwdTileKv);
-  build_kv_schedule(p, p.dkdv, kBwdTileQ, kBwdTileKv);
+  build_q_schedule(p, p.dq, fs.tile_q, kDqTileKv);
+  build_kv_schedule(p, p.dkdv, kDkvTileQ, kDkvTileKv);
 
   // rank-major rows outside every prefix are zero in dK/dV
   std::vector<char> covered((size_t)p.T, 0);

@@ -61,6 +61,26 @@ __device__ inline float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within every group of 16 lanes,
+// output lane i receives element (i % 4) of the 8-byte words addressed by
+// source lanes i/4, i/4+4, i/4+8, i/4+12.  tr_operand() below turns that into
+// "4 consecutive rows of one column" for an MFMA operand.
+__device__ inline u32x2_t lds_read_tr16(const uint16_t* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// For a row-major LDS tile X (row stride ld elements, ld % 4 == 0), return
+// to lane l the values X[row0 + k][col0 + (l % 32)] for k = 0..3, packed as
+// four 16-bit elements.  row0 may differ between the two half-waves.
+__device__ inline u32x2_t tr_operand(const uint16_t* X, int ld, int row0, int col0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  return lds_read_tr16(X + (row0 + (s >> 2)) * ld + col0 + 16 * (g & 1) + 4 * (s & 3));
+}
+
 __device__ inline f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll

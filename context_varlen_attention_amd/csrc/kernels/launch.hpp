@@ -51,6 +51,7 @@ struct BwdParams {
   float* delta;            // [hq, t_loc] workspace
   PlanTables t;
   int32_t n_dq_tiles, n_kv_tiles, n_zero_ranges;
+  int32_t dq_heads_per_tile, dq_head_groups;
   int32_t hq, hkv, group;
   int32_t t_loc;
   int64_t t_total;

@@ -145,12 +145,14 @@ def fwd_full_ref(w, q, k, v, scale=None):
     return o, lse
 
 
-def bwd_ref(w, q, k, v, do_local, scale=None):
+def bwd_ref(w, q, k, v, do_local, scale=None, heads=None):
     """Backward on rank (w.cp_size, w.rank)'s share.
 
     q, k, v: full unsplit tensors.  do_local: [T_loc, Hq, Dv] gradient of the
     local output rows.  Returns dq_local [T_loc, Hq, Dqk] and rank-major
-    dk [T, Hkv, Dqk], dv [T, Hkv, Dv], all float64.
+    dk [T, Hkv, Dqk], dv [T, Hkv, Dv], all float64.  ``heads`` restricts the
+    work to those query heads (their dQ, and their K/V groups' dK/dV -- complete
+    only for groups whose every head is listed); other entries stay zero.
     """
     scale = default_scale(w.d_qk) if scale is None else float(scale)
     G = w.hq // w.hkv
@@ -168,7 +170,7 @@ def bwd_ref(w, q, k, v, do_local, scale=None):
         Ki = np.asarray(k[s0: s0 + L], dtype=np.float64)
         Vi = np.asarray(v[s0: s0 + L], dtype=np.float64)
         M = _mask_for(w, i, L, pos)
-        for h in range(w.hq):
+        for h in (range(w.hq) if heads is None else heads):
             g = h // G
             P, _ = softmax_rows_ref(scale * (Qi[:, h] @ Ki[:, g].T), M)
             dOh = dO[lrows, h, :]
