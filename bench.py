@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Benchmark of one context-parallel rank's share of packed varlen attention
+on one MI355X, through libcva's C ABI.
+
+A step is one batch through the whole hot path: the host plan (rank metadata
+and block-mask tile schedules), its upload, the forward and the backward.
+Plans are built by a look-ahead host thread and uploaded on a side stream, so
+host planning overlaps the GPU work of the previous step (the look-ahead
+planning of the DCP paper's data loader); when planning is slower than the
+GPU the step waits for it and the measured time includes that wait.
+
+Prints ONE JSON line.  ``value`` is useful attention TFLOP/s over the step:
+only unmasked (query, key) pairs count, forward 2*N*Hq*(Dqk+Dv), backward
+2*N*Hq*(3*Dqk+2*Dv) (scores and dP counted once).  ``roofline`` is the
+dominant kernel's algorithmic rate against the MI355X dense MFMA peak, from
+hipEvents recorded around its launches on its own stream during the timed
+steps.  ``cpu_baseline`` times the fp64 oracle on a bounded sample of the
+same workload on this host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa16k]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import queue
+import sys
+import threading
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "fp32": 157.3}  # dense; 256 CU x 2.4 GHz x 4096 (16-bit)
+PEAK_HBM_GBS = 8000.0
+METRIC = "useful attention TFLOP/s (bf16 fwd/bwd) and % of MI355X MFMA peak"
+
+DESCRIPTIONS = {
+    "gqa16k": "packed varlen GQA, 16384 tokens (log-uniform lengths 128..8192), CP rank 1 of 4, "
+              "32/8 heads, D=128, causal + EOD reset",
+    "long128k": "single 131072-token sequence, CP rank 3 of 8, 32/8 heads, D=128, causal",
+    "sparse8": "8 sequences (log-normal lengths, median 8192), no CP split, 16/16 heads, D=128",
+    "mla32k": "32768 packed tokens (uniform lengths 512..16384), CP rank 2 of 4, 16/16 heads, "
+              "Dqk=192, Dv=128, causal",
+    "tiny": "cu_seqlens [0,64,192,256], CP rank 0 of 2, 4/4 heads, D=64",
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def make_plan(cva, w):
+    return cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype,
+                    mask=w.mask, sink=w.sink, window=w.window, branch_bounds=w.branch_bounds)
+
+
+class LookAheadPlanner:
+    """Builds and uploads plans on a host thread, `depth` batches ahead."""
+
+    def __init__(self, cva, w, n, depth=2):
+        import torch
+        self.cva, self.w, self.n = cva, w, n
+        self.q = queue.Queue(maxsize=depth)
+        self.stream = torch.cuda.Stream()
+        self.build_s = []
+        self.err = None
+        self.t = threading.Thread(target=self._run, daemon=True)
+        self.t.start()
+
+    def _run(self):
+        import torch
+        try:
+            with torch.cuda.stream(self.stream):
+                for _ in range(self.n):
+                    t0 = time.perf_counter()
+                    p = make_plan(self.cva, self.w)
+                    self.build_s.append(time.perf_counter() - t0)
+                    p.upload(stream=self.stream)  # returns after the copy has landed
+                    self.q.put(p)
+        except BaseException as e:  # surfaced to the consumer
+            self.err = e
+            self.q.put(None)
+
+    def get(self):
+        p = self.q.get()
+        if p is None:
+            raise RuntimeError(f"planner thread failed: {self.err!r}")
+        return p
+
+
+def kernel_flops(w, pairs):
+    hq, dqk, dv = w.hq, w.d_qk, w.d_v
+    return {
+        "fwd": 2 * pairs * hq * (dqk + dv),
+        "bwd_dkdv": 2 * pairs * hq * (2 * dqk + 2 * dv),
+        "bwd_dq": 2 * pairs * hq * (2 * dqk + dv),
+    }
+
+
+def kernel_bytes(w):
+    t_loc = w.total_tokens // w.cp_size
+    esz = 4 if w.dtype == "fp32" else 2
+    return {"bwd_pre": 2 * t_loc * w.hq * w.d_v * esz + t_loc * w.hq * 4}
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """fp64 oracle forward+backward on a bounded sample: whole K/V head groups."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the visible core count
+        threads = os.cpu_count()
+    q, k, v, do = synth.make_tensors(w)
+    loc = oracle.rank_local_positions(w.cu_seqlens, w.cp_size, w.rank)
+    do_loc = do[loc]
+    G = w.hq // w.hkv
+    pairs = oracle.visible_pairs_ref(w)
+    done_heads, elapsed = 0, 0.0
+    for g in range(w.hkv):
+        heads = list(range(g * G, (g + 1) * G))
+        t0 = time.perf_counter()
+        oracle.fwd_ref(w, q, k, v, heads=heads)
+        oracle.bwd_ref(w, q, k, v, do_loc, heads=heads)
+        elapsed += time.perf_counter() - t0
+        done_heads += G
+        if elapsed >= budget_s:
+            break
+    flops = 2 * pairs * done_heads * ((w.d_qk + w.d_v) + (3 * w.d_qk + 2 * w.d_v))
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"fp64 numpy oracle fwd+bwd on {done_heads} of {w.hq} query heads "
+                  f"({done_heads // G} K/V groups), all local rows of the same batch; "
+                  f"{elapsed:.1f} s; useful flops counted as on the GPU",
+        "seconds": elapsed,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gqa16k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix"])
+    ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
+    ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU's share on a single MI355X; --gpus {args.gpus} "
+              f"(WORLD_SIZE={world}) is not supported: this build has no multi-GPU path",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import context_varlen_attention_amd as cva
+    cva.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    w = synth.make_workload(args.workload, mask=args.mask, dtype=args.dtype)
+    dev = torch.device("cuda", 0)
+    tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
+    T, T_loc = w.total_tokens, w.total_tokens // w.cp_size
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 * synth.CONFIG_IDS[w.name] + args.seed)
+    q = torch.randn((T_loc, w.hq, w.d_qk), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    k = torch.randn((T, w.hkv, w.d_qk), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    v = torch.randn((T, w.hkv, w.d_v), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    do = torch.randn((T_loc, w.hq, w.d_v), generator=gen, device=dev, dtype=torch.float32).to(tdt)
+    o = torch.empty((T_loc, w.hq, w.d_v), device=dev, dtype=tdt)
+    lse = torch.empty((w.hq, T_loc), device=dev, dtype=torch.float32)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+
+    ref_plan = make_plan(cva, w)
+    pairs = ref_plan.visible_pairs()
+    ws = torch.empty(max(int(cva.load_library().cva_bwd_workspace_bytes(ref_plan.handle)), 4),
+                     dtype=torch.uint8, device=dev)
+    fwd_only = args.fwd_only or w.dtype == "fp32"
+    log(f"workload {w.name}: T={T} T_loc={T_loc} seqs={len(w.lengths)} pairs/head={pairs} "
+        f"fwd_only={fwd_only}")
+
+    def step(plan):
+        cva.fwd(plan, q, k, v, out=o, lse=lse)
+        if not fwd_only:
+            cva.bwd(plan, q, k, v, o, lse, do, dq=dq, dk_rm=dk, dv_rm=dv, workspace=ws)
+
+    planner = LookAheadPlanner(cva, w, args.warmup + args.steps)
+    keep = []  # plans stay alive until the final synchronize (their device tables are in use)
+    for _ in range(args.warmup):
+        p = planner.get()
+        keep.append(p)
+        step(p)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+
+    cva.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        p = planner.get()
+        keep.append(p)
+        step(p)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    times = cva.timing_read()
+    cva.timing_enable(False)
+    log(f"timed {args.steps} steps in {t1 - t0:.3f} s")
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    fl_fwd = 2 * pairs * w.hq * (w.d_qk + w.d_v)
+    fl_bwd = 0 if fwd_only else 2 * pairs * w.hq * (3 * w.d_qk + 2 * w.d_v)
+    value = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    kfl = kernel_flops(w, pairs)
+    kby = kernel_bytes(w)
+    kernels = {}
+    for name, (n, tot) in times.items():
+        if n == 0:
+            continue
+        avg = tot / n
+        rec = {"launches_per_step": n / args.steps, "avg_ms": avg, "ms_per_step": tot / args.steps}
+        if name in kfl:
+            rec.update(bound="mfma", achieved=kfl[name] / (avg * 1e-3) / 1e12, unit="TFLOP/s",
+                       peak=peak)
+        elif name in kby:
+            rec.update(bound="hbm", achieved=kby[name] / (avg * 1e-3) / 1e9, unit="GB/s",
+                       peak=PEAK_HBM_GBS)
+        if "achieved" in rec:
+            rec["frac"] = rec["achieved"] / rec["peak"]
+        kernels[name] = rec
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
+    d = kernels[dom]
+    roofline = {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"),
+                "peak": d.get("peak"), "unit": d.get("unit"), "frac": d.get("frac"),
+                "traffic": None,
+                "per_launch": (f"{kfl[dom]:.4e} flop" if dom in kfl else f"{kby.get(dom, 0)} B")}
+    fwd_ms = kernels.get("fwd", {}).get("ms_per_step")
+    bwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("bwd"))
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "description": DESCRIPTIONS[w.name], "tokens": T,
+                   "sub_sequences": int(len(w.lengths)), "cp_size": w.cp_size, "rank": w.rank,
+                   "hq": w.hq, "hkv": w.hkv, "d_qk": w.d_qk, "d_v": w.d_v, "mask": w.mask,
+                   "step": "plan (look-ahead) + upload + fwd" + ("" if fwd_only else " + bwd")},
+        "pct_of_peak": 100.0 * value / peak,
+        "useful_tflop_per_step": (fl_fwd + fl_bwd) / 1e12,
+        "fwd_tflops": fl_fwd / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,
+        "bwd_tflops": fl_bwd / (bwd_ms * 1e-3) / 1e12 if bwd_ms and fl_bwd else None,
+        "plan_ms_host": 1e3 * float(np.mean(planner.build_s)) if planner.build_s else None,
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    del keep
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a bounded sample (cpu_baseline)")
+        cb = cpu_baseline(w)
+        out["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -25,7 +25,7 @@ import os
 import numpy as np
 
 __all__ = ["Plan", "fwd", "bwd", "CvaError", "local_token_ids", "rank_major_token_ids",
-           "library_path", "load_library"]
+           "library_path", "load_library", "timing_enable", "timing_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcva.so")
@@ -78,7 +78,13 @@ class _Schedule(ctypes.Structure):
 
 EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_get_metadata",
            "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_bwd_workspace_bytes",
-           "cva_bwd", "cva_plan_get_schedule"]
+           "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read"]
+
+KERNEL_NAMES = ["fwd", "bwd_pre", "bwd_zero", "bwd_dkdv", "bwd_dq"]
+
+
+class _KernelTimes(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int64 * 5), ("total_ms", ctypes.c_double * 5)]
 
 
 def library_path() -> str:
@@ -116,6 +122,10 @@ def load_library():
     L.cva_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
     L.cva_plan_get_schedule.restype = i32
     L.cva_plan_get_schedule.argtypes = [vp, i32, ctypes.POINTER(_Schedule)]
+    L.cva_timing_enable.restype = i32
+    L.cva_timing_enable.argtypes = [i32]
+    L.cva_timing_read.restype = i32
+    L.cva_timing_read.argtypes = [ctypes.POINTER(_KernelTimes)]
     _lib = L
     return L
 
@@ -328,6 +338,18 @@ def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk
                      workspace.numel() * workspace.element_size(), _scale(plan, softmax_scale),
                      _stream_ptr(stream, dev)))
     return dq, dk_rm, dv_rm
+
+
+def timing_enable(on=True):
+    """``cva_timing_enable``: start (and reset) or stop per-kernel event timing."""
+    _check(load_library().cva_timing_enable(1 if on else 0))
+
+
+def timing_read():
+    """``cva_timing_read``: {kernel name: (launches, total ms)} since timing_enable(True)."""
+    t = _KernelTimes()
+    _check(load_library().cva_timing_read(ctypes.byref(t)))
+    return {n: (int(t.launches[i]), float(t.total_ms[i])) for i, n in enumerate(KERNEL_NAMES)}
 
 
 def local_token_ids(cu_seqlens, cp_size, rank):

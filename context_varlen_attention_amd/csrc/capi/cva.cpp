@@ -10,6 +10,7 @@
 #include <cstring>
 #include <new>
 #include <sstream>
+#include <vector>
 
 #include <hip/hip_runtime_api.h>
 
@@ -52,6 +53,54 @@ cva_status check_scale(float s) {
   if (!std::isfinite(s) || !(s > 0.f)) return fail(CVA_E_SCALE, "softmax_scale must be finite and > 0");
   return CVA_OK;
 }
+
+// Event-pair timing around kernel launches (cva_timing_enable / cva_timing_read).
+struct Timer final : cva::LaunchHook {
+  struct Rec { int kernel; hipEvent_t a, b; };
+  bool on = false;
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[CVA_N_KERNELS] = {};
+  double total_ms[CVA_N_KERNELS] = {};
+  hipEvent_t get() {
+    if (!pool.empty()) { hipEvent_t e = pool.back(); pool.pop_back(); return e; }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  void before(int kernel, hipStream_t s) override {
+    Rec r{kernel, get(), get()};
+    if (r.a) (void)hipEventRecord(r.a, s);
+    pending.push_back(r);
+  }
+  void after(int, hipStream_t s) override {
+    if (!pending.empty() && pending.back().b) (void)hipEventRecord(pending.back().b, s);
+  }
+  hipError_t drain() {
+    hipError_t err = hipSuccess;
+    for (Rec& r : pending) {
+      float ms = 0.f;
+      if (r.a && r.b) {
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess && err == hipSuccess) err = e;
+      }
+      launches[r.kernel] += 1;
+      total_ms[r.kernel] += ms;
+      if (r.a) pool.push_back(r.a);
+      if (r.b) pool.push_back(r.b);
+    }
+    pending.clear();
+    return err;
+  }
+  void reset() {
+    for (int k = 0; k < CVA_N_KERNELS; ++k) { launches[k] = 0; total_ms[k] = 0.0; }
+  }
+};
+
+Timer g_timer;
+
+cva::LaunchHook* hook() { return g_timer.on ? &g_timer : nullptr; }
 
 cva_status check_ready(const Plan* p) {
   if (p == nullptr) return fail(CVA_E_ARG, "plan is NULL");
@@ -185,7 +234,7 @@ cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   fp.tile_q = p->fwd.tile_q;
   fp.tile_kv = p->fwd.tile_kv;
   fp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipError_t e = cva::launch_fwd(p->dtype, p->d_qk, p->d_v, fp, (hipStream_t)stream);
+  hipError_t e = cva::launch_fwd(p->dtype, p->d_qk, p->d_v, fp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return CVA_OK;
 }
@@ -238,7 +287,7 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   bp.t_total = p->T;
   bp.scale = softmax_scale;
   bp.scale_log2 = softmax_scale * 1.4426950408889634f;
-  hipError_t e = cva::launch_bwd(p->dtype, p->d_qk, p->d_v, bp, (hipStream_t)stream);
+  hipError_t e = cva::launch_bwd(p->dtype, p->d_qk, p->d_v, bp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return CVA_OK;
 }
@@ -254,6 +303,29 @@ cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedu
   out->n_spans = s->n_spans();
   out->tiles = s->tiles.data();
   out->spans = s->spans.data();
+  return CVA_OK;
+}
+
+cva_status cva_timing_enable(int32_t on) {
+  if (on) {
+    hipError_t e = g_timer.drain();
+    g_timer.reset();
+    g_timer.on = true;
+    if (e != hipSuccess) return hip_fail(e, "timing drain");
+  } else {
+    g_timer.on = false;
+  }
+  return CVA_OK;
+}
+
+cva_status cva_timing_read(cva_kernel_times* out) {
+  if (out == nullptr) return fail(CVA_E_ARG, "out is NULL");
+  hipError_t e = g_timer.drain();
+  for (int k = 0; k < CVA_N_KERNELS; ++k) {
+    out->launches[k] = g_timer.launches[k];
+    out->total_ms[k] = g_timer.total_ms[k];
+  }
+  if (e != hipSuccess) return hip_fail(e, "timing events");
   return CVA_OK;
 }
 

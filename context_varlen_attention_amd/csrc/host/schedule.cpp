@@ -18,6 +18,7 @@
 // time order) so that long causal rows do not trail at the end of a launch.
 #include <algorithm>
 #include <array>
+#include <cstring>
 #include <numeric>
 
 #include "plan.hpp"
@@ -29,84 +30,111 @@ namespace {
 using Iv = std::pair<int32_t, int32_t>;  // [first, end)
 using IvList = std::vector<Iv>;
 
-IvList normalize(IvList v) {
-  v.erase(std::remove_if(v.begin(), v.end(), [](const Iv& x) { return x.second <= x.first; }),
-          v.end());
-  std::sort(v.begin(), v.end());
-  IvList out;
-  for (const Iv& x : v) {
-    if (!out.empty() && x.first <= out.back().second)
-      out.back().second = std::max(out.back().second, x.second);
-    else
-      out.push_back(x);
+// A row's visible set: at most two disjoint, sorted intervals.
+struct RowSet {
+  int n = 0;
+  Iv v[2];
+};
+
+RowSet row_set(const int32_t* iv) {
+  RowSet r;
+  Iv a{iv[0], iv[1]}, b{iv[2], iv[3]};
+  if (a.second <= a.first) std::swap(a, b);
+  if (a.second <= a.first) return r;                 // both empty
+  if (b.second <= b.first) { r.n = 1; r.v[0] = a; return r; }
+  if (b.first < a.first) std::swap(a, b);
+  if (b.first <= a.second) {                          // overlap or touch: merge
+    r.n = 1;
+    r.v[0] = {a.first, std::max(a.second, b.second)};
+  } else {
+    r.n = 2;
+    r.v[0] = a;
+    r.v[1] = b;
   }
-  return out;
+  return r;
 }
 
-IvList intersect(const IvList& a, const IvList& b) {
-  IvList out;
-  size_t i = 0, j = 0;
-  while (i < a.size() && j < b.size()) {
-    int32_t lo = std::max(a[i].first, b[j].first);
-    int32_t hi = std::min(a[i].second, b[j].second);
-    if (hi > lo) out.push_back({lo, hi});
-    if (a[i].second < b[j].second) ++i; else ++j;
+// Intersection of a sorted disjoint list with a row set, in place.
+void intersect_into(IvList& F, const RowSet& s, IvList& tmp) {
+  tmp.clear();
+  size_t i = 0;
+  int j = 0;
+  while (i < F.size() && j < s.n) {
+    const int32_t lo = std::max(F[i].first, s.v[j].first);
+    const int32_t hi = std::min(F[i].second, s.v[j].second);
+    if (hi > lo) tmp.push_back({lo, hi});
+    if (F[i].second < s.v[j].second) ++i; else ++j;
   }
-  return out;
-}
-
-IvList row_set(const Plan& p, int seg, int32_t a) {
-  int32_t iv[4];
-  row_intervals(p, seg, a, iv);
-  return normalize({{iv[0], iv[1]}, {iv[2], iv[3]}});
+  F.swap(tmp);
 }
 
 struct SpanOut {
   int32_t t0, t1, partial;
 };
 
+// Scratch buffers reused across tiles so the hot loop does not allocate.
+struct Scratch {
+  IvList all, U, F, tmp, ne, full;
+  std::vector<SpanOut> spans;
+};
+
 // Spans of tiles of width `bn` given the union U and intersection F of the rows' visible sets.
-std::vector<SpanOut> tile_spans(const IvList& U, const IvList& F, int32_t bn) {
-  std::vector<Iv> ne;  // non-empty tile ranges
-  for (const Iv& u : U) {
-    int32_t t0 = u.first / bn, t1 = (u.second + bn - 1) / bn;
-    if (!ne.empty() && t0 <= ne.back().second)
-      ne.back().second = std::max(ne.back().second, t1);
+void tile_spans(Scratch& w, int32_t bn) {
+  w.ne.clear();
+  for (const Iv& u : w.U) {
+    const int32_t t0 = u.first / bn, t1 = (u.second + bn - 1) / bn;
+    if (!w.ne.empty() && t0 <= w.ne.back().second)
+      w.ne.back().second = std::max(w.ne.back().second, t1);
     else
-      ne.push_back({t0, t1});
+      w.ne.push_back({t0, t1});
   }
-  std::vector<Iv> full;
-  for (const Iv& f : F) {
-    int32_t t0 = (f.first + bn - 1) / bn, t1 = f.second / bn;
-    if (t1 > t0) full.push_back({t0, t1});
+  w.full.clear();
+  for (const Iv& f : w.F) {
+    const int32_t t0 = (f.first + bn - 1) / bn, t1 = f.second / bn;
+    if (t1 > t0) w.full.push_back({t0, t1});
   }
-  std::vector<SpanOut> out;
+  w.spans.clear();
   size_t k = 0;
-  for (const Iv& r : ne) {
+  for (const Iv& r : w.ne) {
     int32_t cur = r.first;
-    while (k < full.size() && full[k].second <= cur) ++k;
-    while (k < full.size() && full[k].first < r.second) {
-      int32_t f0 = std::max(full[k].first, cur), f1 = std::min(full[k].second, r.second);
-      if (f0 > cur) out.push_back({cur, f0, 1});
-      if (f1 > f0) out.push_back({f0, f1, 0});
+    while (k < w.full.size() && w.full[k].second <= cur) ++k;
+    while (k < w.full.size() && w.full[k].first < r.second) {
+      const int32_t f0 = std::max(w.full[k].first, cur), f1 = std::min(w.full[k].second, r.second);
+      if (f0 > cur) w.spans.push_back({cur, f0, 1});
+      if (f1 > f0) w.spans.push_back({f0, f1, 0});
       cur = std::max(cur, f1);
-      if (full[k].second <= r.second) ++k; else break;
+      if (w.full[k].second <= r.second) ++k; else break;
     }
-    if (cur < r.second) out.push_back({cur, r.second, 1});
+    if (cur < r.second) w.spans.push_back({cur, r.second, 1});
   }
-  return out;
 }
 
-// Union and intersection of the visible sets of rows [a0, a1) of a segment.
-void tile_sets(const Plan& p, int seg, int32_t a0, int32_t a1, IvList& U, IvList& F) {
-  IvList all;
-  F.clear();
+// Union U and intersection F of the visible sets of rows [a0, a1) of a segment.
+void tile_sets(const Plan& p, int seg, int32_t a0, int32_t a1, Scratch& w) {
+  const int32_t row0 = p.segs[(size_t)seg * SEG_INTS + SEG_QROW0];
+  w.all.clear();
+  w.F.clear();
+  bool monotone = true;  // row starts/ends non-decreasing: union is a sweep, no sort
   for (int32_t a = a0; a < a1; ++a) {
-    IvList s = row_set(p, seg, a);
-    all.insert(all.end(), s.begin(), s.end());
-    F = (a == a0) ? s : intersect(F, s);
+    const RowSet s = row_set(&p.row_iv[(size_t)(row0 + a) * 4]);
+    for (int k = 0; k < s.n; ++k) {
+      if (!w.all.empty() && s.v[k].first < w.all.back().first) monotone = false;
+      w.all.push_back(s.v[k]);
+    }
+    if (a == a0) {
+      for (int k = 0; k < s.n; ++k) w.F.push_back(s.v[k]);
+    } else if (!w.F.empty()) {
+      intersect_into(w.F, s, w.tmp);
+    }
   }
-  U = normalize(all);
+  if (!monotone) std::sort(w.all.begin(), w.all.end());
+  w.U.clear();
+  for (const Iv& x : w.all) {
+    if (!w.U.empty() && x.first <= w.U.back().second)
+      w.U.back().second = std::max(w.U.back().second, x.second);
+    else
+      w.U.push_back(x);
+  }
 }
 
 void build_q_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_kv) {
@@ -115,29 +143,36 @@ void build_q_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_k
   s.tiles.clear();
   s.spans.clear();
   s.tile_pairs = 0;
-  struct Rec { int32_t seg, q0, rows; std::vector<SpanOut> sp; int64_t cost; };
+  struct Rec { int32_t seg, q0, rows, span0, nspan; int64_t cost; };
   std::vector<Rec> recs;
+  std::vector<SpanOut> all_spans;
+  Scratch w;
   const int32_t nseg = (int32_t)(p.segs.size() / SEG_INTS);
   for (int32_t sg = 0; sg < nseg; ++sg) {
     const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
     for (int32_t a0 = 0; a0 < q_len; a0 += tile_q) {
       const int32_t a1 = std::min(q_len, a0 + tile_q);
-      IvList U, F;
-      tile_sets(p, sg, a0, a1, U, F);
-      Rec r{sg, a0, a1 - a0, tile_spans(U, F, tile_kv), 0};
-      for (const SpanOut& x : r.sp) r.cost += x.t1 - x.t0;
-      recs.push_back(std::move(r));
+      tile_sets(p, sg, a0, a1, w);
+      tile_spans(w, tile_kv);
+      Rec r{sg, a0, a1 - a0, (int32_t)all_spans.size(), (int32_t)w.spans.size(), 0};
+      for (const SpanOut& x : w.spans) r.cost += x.t1 - x.t0;
+      all_spans.insert(all_spans.end(), w.spans.begin(), w.spans.end());
+      recs.push_back(r);
     }
   }
   std::vector<size_t> order(recs.size());
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [&](size_t x, size_t y) { return recs[x].cost > recs[y].cost; });
+  s.tiles.reserve(recs.size() * QT_INTS);
+  s.spans.reserve(all_spans.size() * SPAN_INTS);
   for (size_t oi : order) {
     const Rec& r = recs[oi];
-    s.tiles.insert(s.tiles.end(),
-                   {r.seg, r.q0, r.rows, s.n_spans(), (int32_t)r.sp.size()});
-    for (const SpanOut& x : r.sp) s.spans.insert(s.spans.end(), {x.t0, x.t1, x.partial, 0});
+    s.tiles.insert(s.tiles.end(), {r.seg, r.q0, r.rows, s.n_spans(), r.nspan});
+    for (int32_t k = 0; k < r.nspan; ++k) {
+      const SpanOut& x = all_spans[r.span0 + k];
+      s.spans.insert(s.spans.end(), {x.t0, x.t1, x.partial, 0});
+    }
     s.tile_pairs += r.cost;
   }
 }
@@ -150,42 +185,69 @@ void build_kv_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_
   s.tiles.clear();
   s.spans.clear();
   s.tile_pairs = 0;
-  struct Rec { int32_t seq, k0, keys; std::vector<std::array<int32_t, 4>> sp; int64_t cost; };
+  struct Rec { int32_t seq, k0, keys, span0, nspan; int64_t cost; };
+  struct Hit { int32_t seg, qt, partial; };
   std::vector<Rec> recs;
+  std::vector<std::array<int32_t, 4>> all_spans;
+  std::vector<int32_t> count, start;
+  std::vector<Hit> hits;
+  struct QSpan { int32_t seg, qt; SpanOut sp; };
+  std::vector<QSpan> qspans;
+  Scratch w;
   for (int32_t i = 0; i < p.n_seqs; ++i) {
     const int32_t segA = 2 * i, segB = 2 * i + 1;
     const int32_t kvmax = std::max(p.segs[segA * SEG_INTS + SEG_KVLEN], p.segs[segB * SEG_INTS + SEG_KVLEN]);
     const int32_t nkt = (kvmax + tile_kv - 1) / tile_kv;
-    // per K/V tile: list of (segment, q tile, partial)
-    std::vector<std::vector<std::array<int32_t, 3>>> hits(nkt);
+    // pass 1: K/V spans of every Q tile of both segments (in segment, q tile order)
+    qspans.clear();
+    count.assign(nkt, 0);
     for (int32_t sg : {segA, segB}) {
       const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
       for (int32_t a0 = 0, qt = 0; a0 < q_len; a0 += tile_q, ++qt) {
-        IvList U, F;
-        tile_sets(p, sg, a0, std::min(q_len, a0 + tile_q), U, F);
-        for (const SpanOut& x : tile_spans(U, F, tile_kv))
-          for (int32_t t = x.t0; t < x.t1 && t < nkt; ++t) hits[t].push_back({sg, qt, x.partial});
+        tile_sets(p, sg, a0, std::min(q_len, a0 + tile_q), w);
+        tile_spans(w, tile_kv);
+        for (const SpanOut& x : w.spans) {
+          qspans.push_back({sg, qt, x});
+          for (int32_t t = x.t0; t < std::min(x.t1, nkt); ++t) ++count[t];
+        }
       }
     }
+    // pass 2: bucket the hits by K/V tile (CSR), keeping (segment, q tile) order
+    start.assign(nkt + 1, 0);
+    for (int32_t t = 0; t < nkt; ++t) start[t + 1] = start[t] + count[t];
+    hits.resize(start[nkt]);
+    std::fill(count.begin(), count.end(), 0);
+    for (const QSpan& qs : qspans)
+      for (int32_t t = qs.sp.t0; t < std::min(qs.sp.t1, nkt); ++t)
+        hits[start[t] + count[t]++] = {qs.seg, qs.qt, qs.sp.partial};
     for (int32_t t = 0; t < nkt; ++t) {
-      Rec r{i, t * tile_kv, std::min(tile_kv, kvmax - t * tile_kv), {}, (int64_t)hits[t].size()};
-      for (const auto& h : hits[t]) {
-        if (!r.sp.empty() && r.sp.back()[0] == h[0] && r.sp.back()[2] == h[1] && r.sp.back()[3] == h[2])
-          r.sp.back()[2] = h[1] + 1;
-        else
-          r.sp.push_back({h[0], h[1], h[1] + 1, h[2]});
+      Rec r{i, t * tile_kv, std::min(tile_kv, kvmax - t * tile_kv), (int32_t)all_spans.size(), 0,
+            (int64_t)(start[t + 1] - start[t])};
+      for (int32_t h = start[t]; h < start[t + 1]; ++h) {
+        const Hit& x = hits[h];
+        if (r.nspan > 0) {
+          auto& b = all_spans.back();
+          if (b[0] == x.seg && b[2] == x.qt && b[3] == x.partial) { b[2] = x.qt + 1; continue; }
+        }
+        all_spans.push_back({x.seg, x.qt, x.qt + 1, x.partial});
+        ++r.nspan;
       }
-      recs.push_back(std::move(r));
+      recs.push_back(r);
     }
   }
   std::vector<size_t> order(recs.size());
   std::iota(order.begin(), order.end(), 0);
   std::stable_sort(order.begin(), order.end(),
                    [&](size_t x, size_t y) { return recs[x].cost > recs[y].cost; });
+  s.tiles.reserve(recs.size() * KT_INTS);
+  s.spans.reserve(all_spans.size() * SPAN_INTS);
   for (size_t oi : order) {
     const Rec& r = recs[oi];
-    s.tiles.insert(s.tiles.end(), {r.seq, r.k0, r.keys, s.n_spans(), (int32_t)r.sp.size()});
-    for (const auto& x : r.sp) s.spans.insert(s.spans.end(), x.begin(), x.end());
+    s.tiles.insert(s.tiles.end(), {r.seq, r.k0, r.keys, s.n_spans(), r.nspan});
+    for (int32_t k = 0; k < r.nspan; ++k) {
+      const auto& x = all_spans[r.span0 + k];
+      s.spans.insert(s.spans.end(), x.begin(), x.end());
+    }
     s.tile_pairs += r.cost;
   }
 }
@@ -237,13 +299,17 @@ cva_status build_schedules(Plan& p) {
     for (int32_t a = 0; a < q_len; ++a) {
       int32_t* iv = &p.row_iv[(size_t)(row0 + a) * 4];
       row_intervals(p, sg, a, iv);
-      for (const Iv& x : normalize({{iv[0], iv[1]}, {iv[2], iv[3]}})) p.visible_pairs += x.second - x.first;
+      const RowSet rs = row_set(iv);
+      for (int k = 0; k < rs.n; ++k) p.visible_pairs += rs.v[k].second - rs.v[k].first;
     }
   }
   FwdShape fs = forward_shape(p);
   p.fwd_heads_per_tile = fs.heads_per_tile;
   build_q_schedule(p, p.fwd, fs.tile_q, fs.tile_kv);
-  build_q_schedule(p, p.dq, fs.tile_q, kDqTileKv);
+  if (kDqTileKv == fs.tile_kv)
+    p.dq = p.fwd;  // same tile shape: the dQ kernel walks the forward schedule
+  else
+    build_q_schedule(p, p.dq, fs.tile_q, kDqTileKv);
   build_kv_schedule(p, p.dkdv, kDkvTileQ, kDkvTileKv);
 
   // rank-major rows outside every prefix are zero in dK/dV
@@ -263,25 +329,21 @@ cva_status build_schedules(Plan& p) {
 
 void build_blob(Plan& p) {
   BlobLayout& L = p.layout;
-  std::vector<int32_t>& b = p.blob;
-  b.clear();
-  auto put = [&](const std::vector<int32_t>& v) {
-    int64_t off = (int64_t)b.size();
-    b.insert(b.end(), v.begin(), v.end());
-    while (b.size() % 64) b.push_back(0);  // keep every table 256-byte aligned
-    return off;
-  };
-  L.segs = put(p.segs);
-  L.kv_index = put(p.kv_index);
-  L.row_iv = put(p.row_iv);
-  L.fwd_tiles = put(p.fwd.tiles);
-  L.fwd_spans = put(p.fwd.spans);
-  L.dq_tiles = put(p.dq.tiles);
-  L.dq_spans = put(p.dq.spans);
-  L.kv_tiles = put(p.dkdv.tiles);
-  L.kv_spans = put(p.dkdv.spans);
-  L.zero_rows = put(p.zero_rows);
-  L.total = (int64_t)b.size();
+  const std::vector<int32_t>* parts[] = {&p.segs, &p.kv_index, &p.row_iv, &p.fwd.tiles, &p.fwd.spans,
+                                         &p.dq.tiles, &p.dq.spans, &p.dkdv.tiles, &p.dkdv.spans,
+                                         &p.zero_rows};
+  int64_t* offs[] = {&L.segs, &L.kv_index, &L.row_iv, &L.fwd_tiles, &L.fwd_spans,
+                     &L.dq_tiles, &L.dq_spans, &L.kv_tiles, &L.kv_spans, &L.zero_rows};
+  int64_t total = 0;
+  for (int k = 0; k < 10; ++k) {
+    *offs[k] = total;
+    total += ((int64_t)parts[k]->size() + 63) / 64 * 64;  // every table 256-byte aligned
+  }
+  L.total = total;
+  p.blob.assign((size_t)total, 0);
+  for (int k = 0; k < 10; ++k)
+    if (!parts[k]->empty())
+      std::memcpy(p.blob.data() + *offs[k], parts[k]->data(), parts[k]->size() * sizeof(int32_t));
 }
 
 }  // namespace cva

@@ -25,8 +25,7 @@ static cva_status fail(cva_status s, const std::string& msg) {
   return s;
 }
 
-static bool head_dims_supported(int32_t dtype, int32_t d_qk, int32_t d_v) {
-  if (dtype == CVA_FP32) return d_qk >= 1 && d_v >= 1 && d_qk <= 256 && d_v <= 256;
+static bool head_dims_supported(int32_t /*dtype*/, int32_t d_qk, int32_t d_v) {
   return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
 }
 
@@ -64,7 +63,7 @@ cva_status validate_request(const int32_t* cu, int32_t n_seqs, int32_t cp_size, 
   if (!head_dims_supported(dtype, d_qk, d_v)) {
     std::ostringstream os;
     os << "no kernel for (Dqk, Dv) = (" << d_qk << ", " << d_v
-       << "); bf16/fp16 support (64,64), (128,128), (192,128)";
+       << "); supported: (64,64), (128,128), (192,128)";
     return fail(CVA_E_HEADDIM, os.str());
   }
   if (mask != nullptr) {

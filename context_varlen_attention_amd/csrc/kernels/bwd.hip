@@ -418,47 +418,35 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams P) {
 }
 
 template <typename E, int DQK, int DV>
-hipError_t launch_all(const BwdParams& p, hipStream_t s) {
+hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
+  hipError_t e = hipSuccess;
+  auto launch = [&](int id, auto kernel, unsigned grid) {
+    if (e != hipSuccess || grid == 0) return;
+    if (hook) hook->before(id, s);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    if (hook) hook->after(id, s);
+    e = hipGetLastError();
+  };
   const int64_t n_pre = (int64_t)p.t_loc * p.hq;
-  if (n_pre > 0) {
-    hipLaunchKernelGGL((bwd_pre_kernel<E, DV>), dim3((unsigned)((n_pre + kThreads - 1) / kThreads)),
-                       dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.n_zero_ranges > 0) {
-    hipLaunchKernelGGL((zero_rows_kernel<DQK, DV>), dim3((unsigned)p.n_zero_ranges), dim3(kThreads),
-                       0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.n_kv_tiles > 0) {
-    hipLaunchKernelGGL((dkdv_kernel<E, DQK, DV>), dim3((unsigned)p.n_kv_tiles * (unsigned)p.hkv),
-                       dim3(kThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (p.n_dq_tiles > 0) {
-    hipLaunchKernelGGL((dq_kernel<E, DQK, DV>),
-                       dim3((unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups), dim3(kThreads),
-                       0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  launch(K_BWD_PRE, bwd_pre_kernel<E, DV>, (unsigned)((n_pre + kThreads - 1) / kThreads));
+  launch(K_BWD_ZERO, zero_rows_kernel<DQK, DV>, (unsigned)p.n_zero_ranges);
+  launch(K_BWD_DKDV, dkdv_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv);
+  launch(K_BWD_DQ, dq_kernel<E, DQK, DV>, (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups);
+  return e;
 }
 
 }  // namespace
 
-hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t s) {
+hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t s,
+                      LaunchHook* h) {
   if (dtype == 0) {
-    if (d_qk == 64 && d_v == 64) return launch_all<Bf16, 64, 64>(p, s);
-    if (d_qk == 128 && d_v == 128) return launch_all<Bf16, 128, 128>(p, s);
-    if (d_qk == 192 && d_v == 128) return launch_all<Bf16, 192, 128>(p, s);
+    if (d_qk == 64 && d_v == 64) return launch_all<Bf16, 64, 64>(p, s, h);
+    if (d_qk == 128 && d_v == 128) return launch_all<Bf16, 128, 128>(p, s, h);
+    if (d_qk == 192 && d_v == 128) return launch_all<Bf16, 192, 128>(p, s, h);
   } else if (dtype == 1) {
-    if (d_qk == 64 && d_v == 64) return launch_all<Fp16, 64, 64>(p, s);
-    if (d_qk == 128 && d_v == 128) return launch_all<Fp16, 128, 128>(p, s);
-    if (d_qk == 192 && d_v == 128) return launch_all<Fp16, 192, 128>(p, s);
+    if (d_qk == 64 && d_v == 64) return launch_all<Fp16, 64, 64>(p, s, h);
+    if (d_qk == 128 && d_v == 128) return launch_all<Fp16, 128, 128>(p, s, h);
+    if (d_qk == 192 && d_v == 128) return launch_all<Fp16, 192, 128>(p, s, h);
   }
   return hipErrorInvalidValue;
 }

@@ -283,36 +283,41 @@ __global__ __launch_bounds__(128) void fwd_fp32_kernel(FwdParams P) {
 }
 
 template <typename E, int DQK, int DV>
-hipError_t launch_mfma(const FwdParams& p, hipStream_t s) {
+hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.n_head_groups;
   if (grid == 0) return hipSuccess;
+  if (hook) hook->before(K_FWD, s);
   hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (hook) hook->after(K_FWD, s);
   return hipGetLastError();
 }
 
 template <int DQK, int DV>
-hipError_t launch_fp32(const FwdParams& p, hipStream_t s) {
+hipError_t launch_fp32(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.n_head_groups;
   if (grid == 0) return hipSuccess;
+  if (hook) hook->before(K_FWD, s);
   hipLaunchKernelGGL((fwd_fp32_kernel<DQK, DV>), dim3(grid), dim3(128), 0, s, p);
+  if (hook) hook->after(K_FWD, s);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_fwd(int dtype, int d_qk, int d_v, const FwdParams& p, hipStream_t s) {
+hipError_t launch_fwd(int dtype, int d_qk, int d_v, const FwdParams& p, hipStream_t s,
+                      LaunchHook* h) {
   if (dtype == 0) {
-    if (d_qk == 64 && d_v == 64) return launch_mfma<Bf16, 64, 64>(p, s);
-    if (d_qk == 128 && d_v == 128) return launch_mfma<Bf16, 128, 128>(p, s);
-    if (d_qk == 192 && d_v == 128) return launch_mfma<Bf16, 192, 128>(p, s);
+    if (d_qk == 64 && d_v == 64) return launch_mfma<Bf16, 64, 64>(p, s, h);
+    if (d_qk == 128 && d_v == 128) return launch_mfma<Bf16, 128, 128>(p, s, h);
+    if (d_qk == 192 && d_v == 128) return launch_mfma<Bf16, 192, 128>(p, s, h);
   } else if (dtype == 1) {
-    if (d_qk == 64 && d_v == 64) return launch_mfma<Fp16, 64, 64>(p, s);
-    if (d_qk == 128 && d_v == 128) return launch_mfma<Fp16, 128, 128>(p, s);
-    if (d_qk == 192 && d_v == 128) return launch_mfma<Fp16, 192, 128>(p, s);
+    if (d_qk == 64 && d_v == 64) return launch_mfma<Fp16, 64, 64>(p, s, h);
+    if (d_qk == 128 && d_v == 128) return launch_mfma<Fp16, 128, 128>(p, s, h);
+    if (d_qk == 192 && d_v == 128) return launch_mfma<Fp16, 192, 128>(p, s, h);
   } else if (dtype == 2) {
-    if (d_qk == 64 && d_v == 64) return launch_fp32<64, 64>(p, s);
-    if (d_qk == 128 && d_v == 128) return launch_fp32<128, 128>(p, s);
-    if (d_qk == 192 && d_v == 128) return launch_fp32<192, 128>(p, s);
+    if (d_qk == 64 && d_v == 64) return launch_fp32<64, 64>(p, s, h);
+    if (d_qk == 128 && d_v == 128) return launch_fp32<128, 128>(p, s, h);
+    if (d_qk == 192 && d_v == 128) return launch_fp32<192, 128>(p, s, h);
   }
   return hipErrorInvalidValue;
 }

@@ -59,8 +59,18 @@ struct BwdParams {
   float scale_log2;        // softmax_scale * log2(e)
 };
 
+// Optional hook around every kernel launch (timing); ids as in cva.h.
+enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_ZERO = 2, K_BWD_DKDV = 3, K_BWD_DQ = 4 };
+struct LaunchHook {
+  virtual void before(int kernel, hipStream_t s) = 0;
+  virtual void after(int kernel, hipStream_t s) = 0;
+  virtual ~LaunchHook() = default;
+};
+
 // dtype: 0 bf16, 1 fp16, 2 fp32.  Return hipSuccess or the launch error.
-hipError_t launch_fwd(int dtype, int d_qk, int d_v, const FwdParams& p, hipStream_t stream);
-hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t stream);
+hipError_t launch_fwd(int dtype, int d_qk, int d_v, const FwdParams& p, hipStream_t stream,
+                      LaunchHook* hook);
+hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t stream,
+                      LaunchHook* hook);
 
 }  // namespace cva

@@ -129,8 +129,8 @@ const char* cva_last_error(void);
 /* Build a plan on the host: validate (RFC section 2 usage limits and section
  * 3.4 reliability: sequence, rank, head and head-dim checks before any device
  * work), build the metadata and the tile schedules.  dtype is a cva_dtype.
- * Supported head dims: (Dqk, Dv) in {(64,64), (128,128), (192,128)} for bf16/fp16
- * and any Dqk >= Dv with Dqk, Dv <= 256 for fp32 (forward only).
+ * Supported head dims: (Dqk, Dv) in {(64,64), (128,128), (192,128)}; fp32 is a
+ * forward-only correctness path (VALU kernel), bf16/fp16 run on MFMA.
  * On success *out owns a new plan (release with cva_plan_destroy). */
 cva_status cva_plan_create(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp_size,
                            int32_t rank, const cva_mask_desc* mask, int32_t hq, int32_t hkv,
@@ -190,6 +190,23 @@ typedef struct {
 } cva_schedule;
 
 cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out);
+
+/* Per-kernel timing, for benchmarks.  While enabled, cva_fwd and cva_bwd
+ * record a hipEvent before and after every kernel they launch, on the stream
+ * the kernel is launched on.  cva_timing_read waits for the recorded events,
+ * folds their elapsed times into per-kernel totals and returns the totals
+ * since the last cva_timing_enable(1) (which resets them).  Kernel ids:
+ *   0 forward, 1 backward Delta, 2 backward zero fill, 3 backward dK/dV,
+ *   4 backward dQ.
+ * Process-wide state; use from one thread at a time. */
+#define CVA_N_KERNELS 5
+typedef struct {
+  int64_t launches[CVA_N_KERNELS];
+  double total_ms[CVA_N_KERNELS];
+} cva_kernel_times;
+
+cva_status cva_timing_enable(int32_t on);
+cva_status cva_timing_read(cva_kernel_times* out);
 
 #ifdef __cplusplus
 }

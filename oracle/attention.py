@@ -90,13 +90,13 @@ def _mask_for(w, i, L, positions):
     return mask_rows_ref(w.mask, L, positions, w.sink, w.window, bounds)
 
 
-def fwd_ref(w, q, k, v, scale=None, rows=None, block=512):
+def fwd_ref(w, q, k, v, scale=None, rows=None, block=512, heads=None):
     """Forward on rank (w.cp_size, w.rank)'s local rows.
 
     q, k, v are the *full unsplit* tensors [T, H, D] (any float dtype; upcast
     to float64).  Returns o [T_loc, Hq, Dv] and lse [Hq, T_loc] as float64;
-    when ``rows`` is given only those local rows are computed and the rest are
-    NaN.
+    when ``rows`` (local row ids) or ``heads`` (query heads) are given only
+    those are computed and the rest are NaN.
     """
     scale = default_scale(w.d_qk) if scale is None else float(scale)
     G = w.hq // w.hkv
@@ -116,7 +116,7 @@ def fwd_ref(w, q, k, v, scale=None, rows=None, block=512):
             toks = s0 + ps
             Qb = np.asarray(q[toks], dtype=np.float64)
             M = _mask_for(w, i, L, ps)
-            for h in range(w.hq):
+            for h in (range(w.hq) if heads is None else heads):
                 S = scale * (Qb[:, h, :] @ Ki[:, h // G, :].T)
                 P, l = softmax_rows_ref(S, M)
                 o[lr, h, :] = P @ Vi[:, h // G, :]
