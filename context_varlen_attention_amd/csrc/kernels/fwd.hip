@@ -28,16 +28,77 @@ namespace cva {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 64;
+constexpr int kBN = 64;  // keys per K/V tile
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: stale row max may lag by up to 2^8
+
+// Issue the direct-to-LDS loads of K tile rows kb0..kb0+63 (rows past the
+// prefix re-read its last row; those keys are masked).  Slot s of the tile holds
+// row s / CH, logical 16-byte chunk (s % CH) ^ (row & 7): the XOR swizzle keeps the
+// MFMA operand reads conflict-free without padding.
+template <int DQK>
+__device__ inline void load_k_tile(uint16_t* sk, const uint16_t* __restrict__ kg, const int32_t* kvi,
+                                   int kb0, int kv_len, int hkv, int kvh, int tid) {
+  constexpr int CH = DQK / 8;
+  constexpr int SLOTS = kBN * CH;
+  const int wave_base = tid & ~63;
+#pragma unroll
+  for (int i = 0; i < SLOTS / kThreads; ++i) {
+    const int s = i * kThreads + tid;
+    const int r = s / CH;
+    const int c = (s % CH) ^ (r & 7);
+    const int b = min(kb0 + r, kv_len - 1);
+    const int64_t g = kvi[b];
+    const uint16_t* src = kg + (g * hkv + kvh) * DQK + c * 8;
+    __builtin_amdgcn_global_load_lds(
+        (const void*)src,
+        (__attribute__((address_space(3))) void*)(sk + (size_t)(i * kThreads + wave_base) * 8), 16, 0, 0);
+  }
+}
+
+// V tile: thread (group g of 16 keys, half h, 8-dim chunk c) loads the 8 key
+// rows of its reduction slots; they are transposed in registers later.
+template <int DV>
+__device__ inline void load_v_regs(u32x4_t (&vr)[8], const uint16_t* __restrict__ vg, const int32_t* kvi,
+                                   int kb0, int kv_len, int hkv, int kvh, int tid) {
+  constexpr int CH = DV / 8;
+  if (tid >= (kBN / 8) * CH) return;
+  const int c = tid % CH, gh = tid / CH;  // gh = 2 * group + half
+  const int g = gh >> 1, h = gh & 1;
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    const int key = 16 * g + (m < 4 ? 4 * h + m : 8 + 4 * h + (m - 4));
+    const int b = min(kb0 + key, kv_len - 1);
+    const int64_t row = kvi[b];
+    vr[m] = *(const u32x4_t*)(vg + (row * hkv + kvh) * DV + c * 8);
+  }
+}
+
+template <int DV>
+__device__ inline void store_vt(uint16_t* svt, const u32x4_t (&vr)[8], int tid) {
+  constexpr int CH = DV / 8;
+  constexpr int VT_LD = kBN + 8;
+  if (tid >= (kBN / 8) * CH) return;
+  const int c = tid % CH, gh = tid / CH;
+  const int g = gh >> 1, h = gh & 1;
+#pragma unroll
+  for (int dd = 0; dd < 8; ++dd) {
+    const int w = dd >> 1;
+    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+    u32x4_t out;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[j] = __builtin_amdgcn_perm(vr[2 * j + 1][w], vr[2 * j][w], sel);
+    *(u32x4_t*)(svt + (8 * c + dd) * VT_LD + 16 * g + 8 * h) = out;
+  }
+}
 
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
   constexpr int KSTEPS = DQK / 16;  // 16-wide reduction steps of S^T
   constexpr int DB = DV / 32;       // 32-row blocks of O^T
-  constexpr int K_LD = DQK + 8;     // LDS row stride of K (elements), 16-byte aligned rows
-  constexpr int VT_LD = kBN + 8;    // LDS row stride of V^T (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBN * K_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[DV * VT_LD];
+  constexpr int KCH = DQK / 8;
+  constexpr int VT_LD = kBN + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][DV * VT_LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -56,15 +117,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
   const bool valid = a < q_len;
   const int row = q_row0 + a;                   // local row
 
-  const uint16_t* __restrict__ qg = (const uint16_t*)P.q;
   const uint16_t* __restrict__ kg = (const uint16_t*)P.k;
   const uint16_t* __restrict__ vg = (const uint16_t*)P.v;
   const int32_t* __restrict__ kvi = P.t.kv_index + kv_off;
+  const int32_t* __restrict__ spans = P.t.fwd_spans + span0 * 4;
 
   // Q fragments: lane holds Q[row][16t + 8*half .. +7] for every step t.
   typename E::vec8 qf[KSTEPS];
   {
-    const uint16_t* qrow = qg + ((int64_t)row * P.hq + head) * DQK + 8 * half;
+    const uint16_t* qrow = (const uint16_t*)P.q + ((int64_t)row * P.hq + head) * DQK + 8 * half;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
       u32x4_t x = {0u, 0u, 0u, 0u};
@@ -78,134 +139,130 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
     lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
   }
 
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run = -INFINITY, m_base = 0.f, l_run = 0.f;
   f32x16_t acc[DB];
 #pragma unroll
   for (int d = 0; d < DB; ++d) acc[d] = zero16();
-
   const float sl2 = P.scale_log2;
 
-  for (int sp = 0; sp < nspan; ++sp) {
-    const int32_t* spr = P.t.fwd_spans + (span0 + sp) * 4;
-    const int t_begin = spr[0], t_end = spr[1];
-    const bool partial = spr[2] != 0;
-    for (int t = t_begin; t < t_end; ++t) {
-      const int kb0 = t * kBN;
-      __syncthreads();
-      // ---- K tile: rows kb0..kb0+63 gathered through the prefix index ----
-      {
-        constexpr int CH = DQK / 8;  // 16-byte chunks per row
-        for (int idx = tid; idx < kBN * CH; idx += kThreads) {
-          const int r = idx / CH, c = idx % CH;
-          const int b = kb0 + r;
-          u32x4_t x = {0u, 0u, 0u, 0u};
-          if (b < kv_len) {
-            const int64_t g = kvi[b];
-            x = *(const u32x4_t*)(kg + (g * P.hkv + kvh) * DQK + c * 8);
-          }
-          *(u32x4_t*)(sK + r * K_LD + c * 8) = x;
-        }
-      }
-      // ---- V^T tile: 4 keys x 8 dims per thread, transposed in registers ----
-      {
-        constexpr int CH = DV / 8;
-        for (int idx = tid; idx < (kBN / 4) * CH; idx += kThreads) {
-          const int g4 = idx / CH, c = idx % CH;
-          u32x4_t rows[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int b = kb0 + 4 * g4 + j;
-            rows[j] = u32x4_t{0u, 0u, 0u, 0u};
-            if (b < kv_len) {
-              const int64_t g = kvi[b];
-              rows[j] = *(const u32x4_t*)(vg + (g * P.hkv + kvh) * DV + c * 8);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            const bool hi = e & 1;
-            uint32_t x0 = hi ? (rows[0][w] >> 16) : (rows[0][w] & 0xFFFFu);
-            uint32_t x1 = hi ? (rows[1][w] >> 16) : (rows[1][w] & 0xFFFFu);
-            uint32_t x2 = hi ? (rows[2][w] >> 16) : (rows[2][w] & 0xFFFFu);
-            uint32_t x3 = hi ? (rows[3][w] >> 16) : (rows[3][w] & 0xFFFFu);
-            u32x2_t out = {x0 | (x1 << 16), x2 | (x3 << 16)};
-            *(u32x2_t*)(sVt + (8 * c + e) * VT_LD + 4 * g4) = out;
-          }
-        }
-      }
-      __syncthreads();
+  if (nspan == 0) {  // no visible key for any row of the tile (unreachable for the supported masks)
+    if (valid) {
+      uint16_t* orow = (uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV;
+      for (int d = half; d < DV; d += 2) orow[d] = 0;
+      if (half == 0) P.lse[(int64_t)head * P.t_loc + row] = -INFINITY;
+    }
+    return;
+  }
+  // V^T tile layout: in every 16-key group, the two half-waves' reduction slots
+  // {4h..4h+3, 8+4h..8+4h+3} are stored as one contiguous 8-element run, so each
+  // PV operand is a single 16-byte read.
+  // walk the spans' tiles as one sequence, double-buffered
+  int sp = 0, t = spans[0], t_end = spans[1];
+  bool partial = spans[2] != 0;
+  u32x4_t vr[8];
+  load_k_tile<DQK>(sK[0], kg, kvi, t * kBN, kv_len, P.hkv, kvh, tid);
+  load_v_regs<DV>(vr, vg, kvi, t * kBN, kv_len, P.hkv, kvh, tid);
+  store_vt<DV>(sVt[0], vr, tid);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
 
-      // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks) ----
-      f32x16_t s[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        s[nb] = zero16();
-        const uint16_t* krow = sK + (nb * 32 + col) * K_LD + 8 * half;
-#pragma unroll
-        for (int kt = 0; kt < KSTEPS; ++kt) {
-          u32x4_t x = *(const u32x4_t*)(krow + 16 * kt);
-          s[nb] = E::mfma32(as_vec8<E>(x), qf[kt], s[nb]);
-        }
+  for (int buf = 0;; buf ^= 1) {
+    // next tile of the sequence
+    int nsp = sp, nt = t + 1, nt_end = t_end;
+    bool npartial = partial;
+    if (nt >= nt_end) {
+      ++nsp;
+      if (nsp < nspan) {
+        nt = spans[nsp * 4];
+        nt_end = spans[nsp * 4 + 1];
+        npartial = spans[nsp * 4 + 2] != 0;
       }
-      // ---- scale, mask, running max ----
-      float mx = -INFINITY;
+    }
+    const bool has_next = nsp < nspan;
+    if (has_next) {
+      load_k_tile<DQK>(sK[buf ^ 1], kg, kvi, nt * kBN, kv_len, P.hkv, kvh, tid);
+      load_v_regs<DV>(vr, vg, kvi, nt * kBN, kv_len, P.hkv, kvh, tid);
+    }
+    const int kb0 = t * kBN;
+    const uint16_t* sk = sK[buf];
+    const uint16_t* svt = sVt[buf];
+
+    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks) ----
+    f32x16_t s[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < 2; ++nb) {
+      s[nb] = zero16();
+      const int r = nb * 32 + col;
+      const uint16_t* krow = sk + r * DQK;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[nb][r] * sl2;
-          if (partial) {
-            const int b = kb0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool vis = (b >= lo1 && b < hi1) || (b >= lo2 && b < hi2);
-            x = vis ? x : -INFINITY;
-          }
+      for (int kt = 0; kt < KSTEPS; ++kt) {
+        const int c = (2 * kt + half) ^ (r & 7);
+        const u32x4_t x = *(const u32x4_t*)(krow + c * 8);
+        s[nb] = E::mfma32(as_vec8<E>(x), qf[kt], s[nb]);
+      }
+    }
+    // ---- mask (partial tiles only) and running max of the raw scores ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[nb][r];
+        if (partial) {
+          const int b = kb0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool vis = (b >= lo1 && b < hi1) || (b >= lo2 && b < hi2);
+          x = vis ? x : -INFINITY;
           s[nb][r] = x;
-          mx = fmaxf(mx, x);
         }
+        mx = fmaxf(mx, x);
       }
-      mx = fmaxf(mx, swap_halves(mx));
+    }
+    mx = fmaxf(mx, swap_halves(mx)) * sl2;
+    // lazy rescale: move the exponent base only when the max grew by more than 2^8
+    if (__ballot(mx > m_run + kRescaleThreshold) != 0) {
       const float m_new = fmaxf(m_run, mx);
-      const float base = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - base);
-      m_run = m_new;
-      float rs = 0.f;
-      uint32_t pk[2][2][4];  // [nb][16-key step][packed pairs]
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(s[nb][r] - base);
-          const float p1 = __builtin_amdgcn_exp2f(s[nb][r + 1] - base);
-          rs += p0 + p1;
-          pk[nb][r >> 3][(r & 7) >> 1] = pack2<E>(p0, p1);
-        }
-      }
-      l_run = l_run * alpha + rs;
+      const float nb_ = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_base - nb_);
+      l_run *= alpha;
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-
-      // ---- O^T += V^T P^T: 4 reduction steps of 16 keys ----
+      m_run = m_new;
+      m_base = nb_;
+    }
+    const float nbase = -m_base;
+    uint32_t pk[2][2][4];  // [nb][16-key step][packed pairs]
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const u32x4_t pv = {pk[nb][st][0], pk[nb][st][1], pk[nb][st][2], pk[nb][st][3]};
-          const typename E::vec8 bfrag = as_vec8<E>(pv);
-          const int kbase = nb * 32 + st * 16 + 4 * half;
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, nbase));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, nbase));
+        l_run += p0 + p1;
+        pk[nb][r >> 3][(r & 7) >> 1] = pack2<E>(p0, p1);
+      }
+    }
+    // ---- O^T += V^T P^T: 4 reduction steps of 16 keys, one 16-byte V^T read each ----
 #pragma unroll
-          for (int d = 0; d < DB; ++d) {
-            const uint16_t* vrow = sVt + (d * 32 + col) * VT_LD + kbase;
-            const u32x2_t lo = *(const u32x2_t*)(vrow);
-            const u32x2_t hi = *(const u32x2_t*)(vrow + 8);
-            const u32x4_t af = {lo[0], lo[1], hi[0], hi[1]};
-            acc[d] = E::mfma32(as_vec8<E>(af), bfrag, acc[d]);
-          }
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const u32x4_t pv = {pk[nb][st][0], pk[nb][st][1], pk[nb][st][2], pk[nb][st][3]};
+        const typename E::vec8 bfrag = as_vec8<E>(pv);
+        const int kofs = nb * 32 + st * 16 + 8 * half;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const u32x4_t af = *(const u32x4_t*)(svt + (d * 32 + col) * VT_LD + kofs);
+          acc[d] = E::mfma32(as_vec8<E>(af), bfrag, acc[d]);
         }
       }
     }
+    if (!has_next) break;
+    store_vt<DV>(sVt[buf ^ 1], vr, tid);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    sp = nsp; t = nt; t_end = nt_end; partial = npartial;
   }
 
   // ---- epilogue: normalise, write O and LSE ----
@@ -224,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
       }
     }
     if (half == 0) {
-      const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+      const float lse = l_tot > 0.f ? (m_base + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
       P.lse[(int64_t)head * P.t_loc + row] = lse;
     }
   }
