@@ -14,7 +14,7 @@ Source: MindSpeed RFC "KVAllGather CP: EOD-aware load balancing for THD"
   actual_seq_kvlen, and that index.
 * glossary: rank-major means the all-gather result concatenated in rank order.
 
-Readings taken where the page is silent (each also listed in the design doc):
+Readings taken where the page is silent:
 
 * a rank's local layout is sub-sequence by sub-sequence, and inside each the
   earlier chunk (r) comes first, then chunk 2R-1-r;
