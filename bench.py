@@ -146,6 +146,26 @@ def cpu_baseline(w, budget_s=12.0):
     }
 
 
+COPY_BYTES = 1 << 30
+
+
+def calibrate_copy(torch, dev, reps=3):
+    """A plain element-wise copy of COPY_BYTES bytes (fp32 x * 1 -> y), `reps` times.
+
+    Profiled with the same HBM byte counters as the attention kernels, it gives
+    the factor that turns those counters into bytes.
+    """
+    n = COPY_BYTES // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(reps):
+        torch.mul(x, 1.0, out=y)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy": {"bytes_read": COPY_BYTES, "bytes_written": COPY_BYTES,
+                                         "launches": reps}}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -157,6 +177,8 @@ def main():
     ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,8 +195,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
 
-    w = synth.make_workload(args.workload, mask=args.mask, dtype=args.dtype)
     dev = torch.device("cuda", 0)
+    if args.calibrate_copy:
+        return calibrate_copy(torch, dev)
+    w = synth.make_workload(args.workload, mask=args.mask, dtype=args.dtype)
     tdt = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[w.dtype]
     T, T_loc = w.total_tokens, w.total_tokens // w.cp_size
     gen = torch.Generator(device=dev)

@@ -106,6 +106,7 @@ struct FwdShape {
 FwdShape forward_shape(const Plan& p);
 
 constexpr int32_t kWavesPerFwdTile = 4;
+constexpr int32_t kFwdMaxSpans = 8;   // forward kernel keeps a work item's spans in LDS
 constexpr int32_t kRowsPerWave = 32;
 constexpr int32_t kFwdTileKv = 64;
 constexpr int32_t kDqTileKv = 64;     // dQ kernel: keys per K/V tile (query tile as forward)

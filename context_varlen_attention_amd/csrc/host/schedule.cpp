@@ -306,6 +306,12 @@ cva_status build_schedules(Plan& p) {
   FwdShape fs = forward_shape(p);
   p.fwd_heads_per_tile = fs.heads_per_tile;
   build_q_schedule(p, p.fwd, fs.tile_q, fs.tile_kv);
+  for (int32_t t = 0; t < p.fwd.n_tiles(); ++t) {
+    if (p.fwd.tiles[(size_t)t * QT_INTS + QT_NSPAN] > kFwdMaxSpans) {
+      set_error("mask gives a query tile more K/V spans than the forward kernel supports");
+      return CVA_E_UNSUPPORTED;
+    }
+  }
   if (kDqTileKv == fs.tile_kv)
     p.dq = p.fwd;  // same tile shape: the dQ kernel walks the forward schedule
   else

@@ -50,9 +50,22 @@ __device__ inline typename E::vec8 as_vec8(u32x4_t x) {
   return __builtin_bit_cast(typename E::vec8, x);
 }
 
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats to one packed 16-bit pair (round to nearest even; one v_cvt_pk).
 template <typename E>
-__device__ inline uint32_t pack2(float lo, float hi) {
-  return (uint32_t)E::from_float(lo) | ((uint32_t)E::from_float(hi) << 16);
+__device__ inline uint32_t pack2(float lo, float hi);
+
+template <>
+__device__ inline uint32_t pack2<Bf16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
+
+template <>
+__device__ inline uint32_t pack2<Fp16>(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 
 // Value held by lane (l ^ 32): the two half-waves of a 32x32 MFMA output hold

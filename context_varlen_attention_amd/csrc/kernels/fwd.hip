@@ -14,12 +14,28 @@
 // one head.  The kernel computes the transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q from registers), so every lane
 // ends up holding 16 keys of ONE query column: the softmax statistics are
-// lane-local, plus one exchange with the lane 32 apart.  The output is kept
-// transposed too, O^T = V^T P^T, with P^T taken straight from the S^T
+// lane-local, plus one v_permlane32_swap with the other half-wave.  The output
+// is kept transposed too, O^T = V^T P^T, with P^T taken straight from the S^T
 // accumulators (the MFMA's reduction slots are permuted to match the layout the
-// accumulators already have) and V^T staged in LDS by a register transpose
-// during the tile load.  K/V rows are gathered through the prefix index while
-// they are loaded (the index_select of the RFC, never materialised).
+// accumulators already have) and the V^T operand read from row-major V tiles
+// with the transposing LDS read ds_read_b64_tr_b16.
+//
+// Per K/V tile the vector ALU does only what the softmax needs:
+//   * Q is pre-multiplied by scale*log2(e) when it is loaded, and the S^T
+//     accumulators start at -base (the row's exponent base), so P = exp2(acc)
+//     with no extra arithmetic;
+//   * the row maximum uses v_max3, the base moves only when the maximum grows
+//     by more than 2^8 (lazy rescaling), so the O rescale is rare;
+//   * P is packed to 16 bits with v_cvt_pk and the row sum is accumulated from
+//     the packed values with v_dot2 (the sum of exactly the values the PV MFMA
+//     consumes);
+//   * masking is a separate code path taken only on partial tiles.
+// K/V rows are gathered through the prefix index straight into LDS with
+// global_load_lds_dwordx4 (the index_select of the RFC, never materialised),
+// one tile ahead, with the tile's indices fetched two tiles ahead.
+#include <type_traits>
+
+#include "../host/plan.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,80 +44,290 @@ namespace cva {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 64;  // keys per K/V tile
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: stale row max may lag by up to 2^8
+constexpr int kBN = 64;                    // keys per K/V tile
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: the base may lag the row max by 2^8
 
-// Issue the direct-to-LDS loads of K tile rows kb0..kb0+63 (rows past the
-// prefix re-read its last row; those keys are masked).  Slot s of the tile holds
-// row s / CH, logical 16-byte chunk (s % CH) ^ (row & 7): the XOR swizzle keeps the
-// MFMA operand reads conflict-free without padding.
-template <int DQK>
-__device__ inline void load_k_tile(uint16_t* sk, const uint16_t* __restrict__ kg, const int32_t* kvi,
-                                   int kb0, int kv_len, int hkv, int kvh, int tid) {
-  constexpr int CH = DQK / 8;
-  constexpr int SLOTS = kBN * CH;
-  const int wave_base = tid & ~63;
-#pragma unroll
-  for (int i = 0; i < SLOTS / kThreads; ++i) {
+// LDS layouts (16-byte chunks, XOR-swizzled so the MFMA operand reads hit
+// distinct banks):
+//   K: row r, logical chunk c at physical chunk c ^ (r & 7); read with
+//      ds_read_b128, 32 consecutive rows per instruction.
+//   V: row r, logical 32-byte group G at physical group G ^ f(r) with
+//      f(r) = (r & 3) ^ ((r & 1) << 2) for rows of 8+ groups (else r & 3); read
+//      with ds_read_b64_tr_b16, which takes 4 consecutive rows x 32 bytes per
+//      16 lanes.
+__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+
+template <int VCH>
+__device__ __forceinline__ int v_swz(int r) {  // XOR applied to the 16-byte chunk index
+  if constexpr (VCH >= 16)
+    return 2 * ((r & 3) ^ ((r & 1) << 2));
+  else
+    return 2 * (r & 3);
+}
+
+constexpr int kMaxSpans = kFwdMaxSpans;  // spans per forward work item (checked by the plan builder)
+
+// Cursor over the tiles of a work item: the spans' [t0, t1) ranges, in order.
+// The span table sits in LDS (sp) so that advancing is a short, uniform read.
+struct TileCursor {
+  int sp, t, t_end, partial;
+};
+
+__device__ __forceinline__ TileCursor span_start(const int32_t* sp_tab, int sp) {
+  const int4 r = *(const int4*)(sp_tab + 4 * sp);
+  return TileCursor{sp, __builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                    __builtin_amdgcn_readfirstlane(r.z)};
+}
+
+__device__ __forceinline__ TileCursor next_tile(TileCursor c, const int32_t* sp_tab, int nspan) {
+  ++c.t;
+  if (c.t >= c.t_end) {
+    ++c.sp;
+    if (c.sp < nspan) c = span_start(sp_tab, c.sp);
+  }
+  return c;
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at LDS byte address lds + 16*l (lds is wave-uniform).
+// Issued through inline assembly so that the compiler does not make LDS reads
+// of the other buffer wait for this load; completion is awaited explicitly
+// (s_waitcnt vmcnt(0) + barrier) before the destination buffer is read.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait
+// bookkeeping knows every vector memory load has completed here (encoding:
+// vmcnt 0, expcnt 7, lgkmcnt 15).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+template <int DQK, int DV>
+struct TileLoader {
+  static constexpr int KCH = DQK / 8, VCH = DV / 8;
+  static constexpr int KN = kBN * KCH / kThreads;  // K slots per thread
+  static constexpr int VN = kBN * VCH / kThreads;  // V slots per thread
+  static constexpr bool kShared = (KCH == VCH);    // K and V slots cover the same rows
+  static constexpr int NIDX = kShared ? KN : KN + VN;
+  static_assert(kBN * KCH % kThreads == 0 && kBN * VCH % kThreads == 0, "tile / thread mismatch");
+
+  __device__ static int krow(int i, int tid) { return (i * kThreads + tid) / KCH; }
+  __device__ static int vrow(int i, int tid) { return (i * kThreads + tid) / VCH; }
+  // byte offset of this thread's 16-byte chunk inside its row (swizzled position)
+  __device__ static uint32_t kchunk(int i, int tid) {
     const int s = i * kThreads + tid;
-    const int r = s / CH;
-    const int c = (s % CH) ^ (r & 7);
-    const int b = min(kb0 + r, kv_len - 1);
-    const int64_t g = kvi[b];
-    const uint16_t* src = kg + (g * hkv + kvh) * DQK + c * 8;
-    __builtin_amdgcn_global_load_lds(
-        (const void*)src,
-        (__attribute__((address_space(3))) void*)(sk + (size_t)(i * kThreads + wave_base) * 8), 16, 0, 0);
+    return (uint32_t)(((s % KCH) ^ k_swz(s / KCH)) * 16);
+  }
+  __device__ static uint32_t vchunk(int i, int tid) {
+    const int s = i * kThreads + tid;
+    return (uint32_t)(((s % VCH) ^ v_swz<VCH>(s / VCH)) * 16);
+  }
+
+  // Prefix-index entries of the rows this thread loads (clamped into the prefix:
+  // rows past it re-read the last key, which is masked).
+  __device__ static void fetch_index(int (&idx)[NIDX], const int32_t* __restrict__ kvi, int kb0,
+                                     int kv_len, int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) idx[i] = kvi[min(kb0 + krow(i, tid), kv_len - 1)];
+    if constexpr (!kShared) {
+#pragma unroll
+      for (int i = 0; i < VN; ++i) idx[KN + i] = kvi[min(kb0 + vrow(i, tid), kv_len - 1)];
+    }
+  }
+
+  // Issue the direct-to-LDS loads of one K tile and one V tile.  kg / vg point at
+  // the K/V head's first element; strides are bytes between gathered rows.
+  // wave_off is the wave's first slot (uniform), so the LDS base is scalar.
+  __device__ static void issue(uint16_t* sk, uint16_t* sv, const char* kg, const char* vg,
+                               const int (&idx)[NIDX], uint32_t kstride, uint32_t vstride, int tid,
+                               int wave_off) {
+    const uint32_t kl = lds_addr(sk) + (uint32_t)wave_off * 16;
+    const uint32_t vl = lds_addr(sv) + (uint32_t)wave_off * 16;
+#pragma unroll
+    for (int i = 0; i < KN; ++i)
+      dma16(kg + ((uint64_t)(uint32_t)idx[i] * kstride + kchunk(i, tid)), kl + i * kThreads * 16);
+#pragma unroll
+    for (int i = 0; i < VN; ++i) {
+      const int id = kShared ? idx[i] : idx[KN + i];
+      dma16(vg + ((uint64_t)(uint32_t)id * vstride + vchunk(i, tid)), vl + i * kThreads * 16);
+    }
+  }
+};
+
+// Per-lane LDS byte offsets of the MFMA operand reads, relative to a tile buffer.
+// The swizzles only permute 16-byte chunks inside aligned groups, so every read
+// of a tile is one of a few per-lane offsets plus a compile-time constant.
+//
+// K (S^T A operand): step kt of 32-key block nb reads logical chunk 2kt + half of
+// row nb*32 + col, i.e. byte  koff[kt & 3] + 128*(kt >> 2) + nb*32*rowbytes.
+template <int DQK>
+__device__ __forceinline__ void k_offsets(uint32_t (&koff)[4], int col, int half) {
+  const int sw = k_swz(col);  // rows nb*32 + col share (row & 7) = col & 7
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+    koff[u] = (uint32_t)(col * DQK * 2 + 32 * (u ^ (sw >> 1)) + 16 * (half ^ (sw & 1)));
+}
+
+// V (PV A operand, transposing read): lane (s = lane & 15, g = lane >> 4) reads
+// 8 bytes of row key0 + 4*half + (s >> 2) at logical column 32*blk + 16*(g&1) +
+// 4*(s&3); for key0 a multiple of 8 the row's swizzle depends on the lane only,
+// so the read is at  voff[blk] + key0*rowbytes.
+template <int DV>
+__device__ __forceinline__ void v_offsets(uint32_t (&voff)[DV / 32], int lane) {
+  constexpr int VCH = DV / 8;
+  const int s = lane & 15, g = lane >> 4;
+  const int r = 4 * (g >> 1) + (s >> 2);  // row relative to key0 (half = g >> 1)
+  const int sw = v_swz<VCH>(r);
+#pragma unroll
+  for (int blk = 0; blk < DV / 32; ++blk) {
+    const int col = blk * 32 + 16 * (g & 1) + 4 * (s & 3);
+    const int c = (col >> 3) ^ sw;
+    voff[blk] = (uint32_t)(r * DV * 2 + c * 16 + (col & 7) * 2);
   }
 }
 
-// V tile: thread (group g of 16 keys, half h, 8-dim chunk c) loads the 8 key
-// rows of its reduction slots; they are transposed in registers later.
-template <int DV>
-__device__ inline void load_v_regs(u32x4_t (&vr)[8], const uint16_t* __restrict__ vg, const int32_t* kvi,
-                                   int kb0, int kv_len, int hkv, int kvh, int tid) {
-  constexpr int CH = DV / 8;
-  if (tid >= (kBN / 8) * CH) return;
-  const int c = tid % CH, gh = tid / CH;  // gh = 2 * group + half
-  const int g = gh >> 1, h = gh & 1;
-#pragma unroll
-  for (int m = 0; m < 8; ++m) {
-    const int key = 16 * g + (m < 4 ? 4 * h + m : 8 + 4 * h + (m - 4));
-    const int b = min(kb0 + key, kv_len - 1);
-    const int64_t row = kvi[b];
-    vr[m] = *(const u32x4_t*)(vg + (row * hkv + kvh) * DV + c * 8);
-  }
+__device__ __forceinline__ u32x4_t lds_read128(const uint16_t* base, uint32_t off) {
+  return *(const u32x4_t*)((const char*)base + off);
 }
 
-template <int DV>
-__device__ inline void store_vt(uint16_t* svt, const u32x4_t (&vr)[8], int tid) {
-  constexpr int CH = DV / 8;
-  constexpr int VT_LD = kBN + 8;
-  if (tid >= (kBN / 8) * CH) return;
-  const int c = tid % CH, gh = tid / CH;
-  const int g = gh >> 1, h = gh & 1;
+__device__ __forceinline__ u32x2_t lds_read_tr(const uint16_t* base, uint32_t off) {
+  return lds_read_tr16((const uint16_t*)((const char*)base + off));
+}
+
+__device__ __forceinline__ float wave_half_max(float x) {
+  // max with the value the lane 32 apart holds
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
+__device__ __forceinline__ float wave_half_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+template <typename E>
+__device__ __forceinline__ float dot2_acc(uint32_t packed, float acc);
+
+template <>
+__device__ __forceinline__ float dot2_acc<Bf16>(uint32_t packed, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
+}
+
+template <>
+__device__ __forceinline__ float dot2_acc<Fp16>(uint32_t packed, float acc) {
+  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+  const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), one, acc, false);
+}
+
+// Per-lane state of the online softmax: exponent base (log2 units, shared by the
+// two half-waves holding the same query), running sum and the O^T accumulators.
+template <int DB>
+struct SoftmaxState {
+  float base, l;
+  f32x16_t acc[DB];
+};
+
+// One K/V tile, as two blocks of 32 keys, each: S^T, (mask), max / lazy rescale,
+// P, row sum, O^T += V^T P^T.  Working on 32 keys at a time keeps the score and
+// probability registers small enough for two waves per SIMD.
+template <typename E, int DQK, int DV, bool kPartial>
+__device__ __forceinline__ void tile_step(SoftmaxState<DV / 32>& st, const typename E::vec8 (&qf)[DQK / 16],
+                                          const uint16_t* sk, const uint16_t* sv,
+                                          const uint32_t (&koff)[4], const uint32_t (&voff)[DV / 32],
+                                          int kb0, int half, int lo1, int hi1, int lo2, int hi2) {
+  constexpr int KSTEPS = DQK / 16;
+  constexpr int DB = DV / 32;
 #pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int w = dd >> 1;
-    const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-    u32x4_t out;
+  for (int nb = 0; nb < 2; ++nb) {
+    // ---- S^T = K (scaled Q)^T - base for keys nb*32 .. nb*32+31 ----
+    f32x16_t s;
+    const float init = -st.base;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) out[j] = __builtin_amdgcn_perm(vr[2 * j + 1][w], vr[2 * j][w], sel);
-    *(u32x4_t*)(svt + (8 * c + dd) * VT_LD + 16 * g + 8 * h) = out;
+    for (int r = 0; r < 16; ++r) s[r] = init;
+#pragma unroll
+    for (int kt = 0; kt < KSTEPS; ++kt) {
+      const u32x4_t x = lds_read128(sk + nb * 32 * DQK + (kt >> 2) * 64, koff[kt & 3]);
+      s = E::mfma32(as_vec8<E>(x), qf[kt], s);
+    }
+    if constexpr (kPartial) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int b = kb0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool vis = ((b >= lo1) & (b < hi1)) | ((b >= lo2) & (b < hi2));
+        s[r] = vis ? s[r] : -INFINITY;
+      }
+    }
+    // ---- row max relative to the base; move the base when it grew by > 2^8 ----
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[r], s[r + 1]));
+    mx = wave_half_max(mx);
+    // a row with nothing accumulated yet (l == 0) takes its first finite max as base
+    const bool grow = (mx > kRescaleThreshold) | ((st.l == 0.f) & (mx > -INFINITY));
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float shift = grow ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      st.base += shift;
+      st.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[d][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] -= shift;
+    }
+    // ---- P = exp2(S^T), packed to 16 bits; row sum from the packed values ----
+    uint32_t pk[2][4];  // [16-key step][packed pairs]
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const uint32_t w = pack2<E>(__builtin_amdgcn_exp2f(s[r]), __builtin_amdgcn_exp2f(s[r + 1]));
+      pk[r >> 3][(r & 7) >> 1] = w;
+      st.l = dot2_acc<E>(w, st.l);
+    }
+    // ---- O^T += V^T P^T: 2 reduction steps of 16 keys ----
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t pv = {pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]};
+      const typename E::vec8 bfrag = as_vec8<E>(pv);
+      const int key0 = nb * 32 + ks * 16;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+        const u32x2_t lo = lds_read_tr(sv + key0 * DV, voff[d]);
+        const u32x2_t hi = lds_read_tr(sv + (key0 + 8) * DV, voff[d]);
+        st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bfrag, st.acc[d]);
+      }
+    }
   }
 }
 
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
+  using TL = TileLoader<DQK, DV>;
   constexpr int KSTEPS = DQK / 16;  // 16-wide reduction steps of S^T
   constexpr int DB = DV / 32;       // 32-row blocks of O^T
-  constexpr int KCH = DQK / 8;
-  constexpr int VT_LD = kBN + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * DQK];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[2][DV * VT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * DV];
+  __shared__ __attribute__((aligned(16))) int32_t sSpan[kMaxSpans * 4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   const int tile = blockIdx.x / P.n_head_groups;
@@ -117,33 +343,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
   const bool valid = a < q_len;
   const int row = q_row0 + a;                   // local row
 
-  const uint16_t* __restrict__ kg = (const uint16_t*)P.k;
-  const uint16_t* __restrict__ vg = (const uint16_t*)P.v;
+  const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
+  const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
+  const uint32_t kstride = (uint32_t)P.hkv * DQK * 2, vstride = (uint32_t)P.hkv * DV * 2;
   const int32_t* __restrict__ kvi = P.t.kv_index + kv_off;
-  const int32_t* __restrict__ spans = P.t.fwd_spans + span0 * 4;
-
-  // Q fragments: lane holds Q[row][16t + 8*half .. +7] for every step t.
-  typename E::vec8 qf[KSTEPS];
-  {
-    const uint16_t* qrow = (const uint16_t*)P.q + ((int64_t)row * P.hq + head) * DQK + 8 * half;
-#pragma unroll
-    for (int t = 0; t < KSTEPS; ++t) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (valid) x = *(const u32x4_t*)(qrow + 16 * t);
-      qf[t] = as_vec8<E>(x);
-    }
-  }
-  int lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
-  if (valid) {
-    const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
-    lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
-  }
-
-  float m_run = -INFINITY, m_base = 0.f, l_run = 0.f;
-  f32x16_t acc[DB];
-#pragma unroll
-  for (int d = 0; d < DB; ++d) acc[d] = zero16();
-  const float sl2 = P.scale_log2;
 
   if (nspan == 0) {  // no visible key for any row of the tile (unreachable for the supported masks)
     if (valid) {
@@ -153,120 +356,84 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
     }
     return;
   }
-  // V^T tile layout: in every 16-key group, the two half-waves' reduction slots
-  // {4h..4h+3, 8+4h..8+4h+3} are stored as one contiguous 8-element run, so each
-  // PV operand is a single 16-byte read.
-  // walk the spans' tiles as one sequence, double-buffered
-  int sp = 0, t = spans[0], t_end = spans[1];
-  bool partial = spans[2] != 0;
-  u32x4_t vr[8];
-  load_k_tile<DQK>(sK[0], kg, kvi, t * kBN, kv_len, P.hkv, kvh, tid);
-  load_v_regs<DV>(vr, vg, kvi, t * kBN, kv_len, P.hkv, kvh, tid);
-  store_vt<DV>(sVt[0], vr, tid);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (tid < 4 * nspan) sSpan[tid] = P.t.fwd_spans[span0 * 4 + tid];
   __syncthreads();
 
-  for (int buf = 0;; buf ^= 1) {
-    // next tile of the sequence
-    int nsp = sp, nt = t + 1, nt_end = t_end;
-    bool npartial = partial;
-    if (nt >= nt_end) {
-      ++nsp;
-      if (nsp < nspan) {
-        nt = spans[nsp * 4];
-        nt_end = spans[nsp * 4 + 1];
-        npartial = spans[nsp * 4 + 2] != 0;
-      }
-    }
-    const bool has_next = nsp < nspan;
-    if (has_next) {
-      load_k_tile<DQK>(sK[buf ^ 1], kg, kvi, nt * kBN, kv_len, P.hkv, kvh, tid);
-      load_v_regs<DV>(vr, vg, kvi, nt * kBN, kv_len, P.hkv, kvh, tid);
-    }
-    const int kb0 = t * kBN;
-    const uint16_t* sk = sK[buf];
-    const uint16_t* svt = sVt[buf];
+  // first tile's indices and loads, second tile's indices
+  const int wave_off = wave * 64;
+  TileCursor cur = span_start(sSpan, 0);
+  int idx[TL::NIDX];
+  TL::fetch_index(idx, kvi, cur.t * kBN, kv_len, tid);
+  TL::issue(sK[0], sV[0], kg, vg, idx, kstride, vstride, tid, wave_off);
+  TileCursor nxt = next_tile(cur, sSpan, nspan);
+  if (nxt.sp < nspan) TL::fetch_index(idx, kvi, nxt.t * kBN, kv_len, tid);
 
-    // ---- S^T = K Q^T for the 64 keys of the tile (two 32-key blocks) ----
-    f32x16_t s[2];
+  // Q fragments, pre-scaled by scale*log2(e): lane holds Q[row][16t + 8*half .. +7].
+  typename E::vec8 qf[KSTEPS];
+  {
+    const uint16_t* qrow = (const uint16_t*)P.q + ((int64_t)row * P.hq + head) * DQK + 8 * half;
+    const float c = P.scale_log2;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      s[nb] = zero16();
-      const int r = nb * 32 + col;
-      const uint16_t* krow = sk + r * DQK;
+    for (int t = 0; t < KSTEPS; ++t) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (valid) x = *(const u32x4_t*)(qrow + 16 * t);
+      u32x4_t y;
 #pragma unroll
-      for (int kt = 0; kt < KSTEPS; ++kt) {
-        const int c = (2 * kt + half) ^ (r & 7);
-        const u32x4_t x = *(const u32x4_t*)(krow + c * 8);
-        s[nb] = E::mfma32(as_vec8<E>(x), qf[kt], s[nb]);
-      }
+      for (int w = 0; w < 4; ++w)
+        y[w] = pack2<E>(E::to_float((uint16_t)(x[w] & 0xFFFFu)) * c, E::to_float((uint16_t)(x[w] >> 16)) * c);
+      qf[t] = as_vec8<E>(y);
     }
-    // ---- mask (partial tiles only) and running max of the raw scores ----
-    float mx = -INFINITY;
+  }
+  int lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
+  if (valid) {
+    const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
+    lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
+  }
+
+  uint32_t koff[4], voff[DB];
+  k_offsets<DQK>(koff, col, half);
+  v_offsets<DV>(voff, lane);
+
+  SoftmaxState<DB> st;
+  st.base = 0.f;
+  st.l = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[nb][r];
-        if (partial) {
-          const int b = kb0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool vis = (b >= lo1 && b < hi1) || (b >= lo2 && b < hi2);
-          x = vis ? x : -INFINITY;
-          s[nb][r] = x;
-        }
-        mx = fmaxf(mx, x);
-      }
+  for (int d = 0; d < DB; ++d) st.acc[d] = zero16();
+
+  wait_vmem_all();
+  __syncthreads();
+
+  // Main loop, unrolled by two so that each half reads a fixed buffer (constant
+  // LDS offsets) while the next tile streams into the other one.
+  auto half_step = [&](auto bufc) -> bool {
+    constexpr int B = decltype(bufc)::value;
+    // Nothing is in flight here (the previous step ended with vmcnt(0) and a
+    // barrier); saying so to the compiler keeps it from waiting on the tile
+    // loads below when it checks the index registers.
+    wait_vmem_all();
+    const bool has_next = nxt.sp < nspan;
+    // loads of the next tile (indices fetched one tile ago) and indices of the one after
+    if (has_next) {
+      TL::issue(sK[B ^ 1], sV[B ^ 1], kg, vg, idx, kstride, vstride, tid, wave_off);
+      const TileCursor nn = next_tile(nxt, sSpan, nspan);
+      if (nn.sp < nspan) TL::fetch_index(idx, kvi, nn.t * kBN, kv_len, tid);
     }
-    mx = fmaxf(mx, swap_halves(mx)) * sl2;
-    // lazy rescale: move the exponent base only when the max grew by more than 2^8
-    if (__ballot(mx > m_run + kRescaleThreshold) != 0) {
-      const float m_new = fmaxf(m_run, mx);
-      const float nb_ = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_base - nb_);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[d][r] *= alpha;
-      m_run = m_new;
-      m_base = nb_;
-    }
-    const float nbase = -m_base;
-    uint32_t pk[2][2][4];  // [nb][16-key step][packed pairs]
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, nbase));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[nb][r + 1], sl2, nbase));
-        l_run += p0 + p1;
-        pk[nb][r >> 3][(r & 7) >> 1] = pack2<E>(p0, p1);
-      }
-    }
-    // ---- O^T += V^T P^T: 4 reduction steps of 16 keys, one 16-byte V^T read each ----
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const u32x4_t pv = {pk[nb][st][0], pk[nb][st][1], pk[nb][st][2], pk[nb][st][3]};
-        const typename E::vec8 bfrag = as_vec8<E>(pv);
-        const int kofs = nb * 32 + st * 16 + 8 * half;
-#pragma unroll
-        for (int d = 0; d < DB; ++d) {
-          const u32x4_t af = *(const u32x4_t*)(svt + (d * 32 + col) * VT_LD + kofs);
-          acc[d] = E::mfma32(as_vec8<E>(af), bfrag, acc[d]);
-        }
-      }
-    }
-    if (!has_next) break;
-    store_vt<DV>(sVt[buf ^ 1], vr, tid);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (cur.partial)
+      tile_step<E, DQK, DV, true>(st, qf, sK[B], sV[B], koff, voff, cur.t * kBN, half, lo1, hi1, lo2, hi2);
+    else
+      tile_step<E, DQK, DV, false>(st, qf, sK[B], sV[B], koff, voff, cur.t * kBN, half, lo1, hi1, lo2, hi2);
+    if (!has_next) return false;
+    wait_vmem_all();
     __syncthreads();
-    sp = nsp; t = nt; t_end = nt_end; partial = npartial;
+    cur = nxt;
+    nxt = next_tile(nxt, sSpan, nspan);
+    return true;
+  };
+  while (half_step(std::integral_constant<int, 0>{}) && half_step(std::integral_constant<int, 1>{})) {
   }
 
   // ---- epilogue: normalise, write O and LSE ----
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = wave_half_sum(st.l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (valid) {
     uint16_t* orow = (uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV;
@@ -275,13 +442,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int dd = d * 32 + 8 * i + 4 * half;
-        u32x2_t w = {pack2<E>(acc[d][4 * i] * inv, acc[d][4 * i + 1] * inv),
-                     pack2<E>(acc[d][4 * i + 2] * inv, acc[d][4 * i + 3] * inv)};
+        u32x2_t w = {pack2<E>(st.acc[d][4 * i] * inv, st.acc[d][4 * i + 1] * inv),
+                     pack2<E>(st.acc[d][4 * i + 2] * inv, st.acc[d][4 * i + 3] * inv)};
         *(u32x2_t*)(orow + dd) = w;
       }
     }
     if (half == 0) {
-      const float lse = l_tot > 0.f ? (m_base + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+      const float lse = l_tot > 0.f ? (st.base + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
       P.lse[(int64_t)head * P.t_loc + row] = lse;
     }
   }
