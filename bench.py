@@ -110,6 +110,46 @@ def kernel_bytes(w):
     return {"bwd_pre": 2 * t_loc * w.hq * w.d_v * esz + t_loc * w.hq * 4}
 
 
+KERNEL_SOURCES = {
+    "fwd": ["kernels/fwd.hip"],
+    "bwd_pre": ["kernels/bwd.hip"], "bwd_zero": ["kernels/bwd.hip"],
+    "bwd_dkdv": ["kernels/bwd.hip"], "bwd_dq": ["kernels/bwd.hip"],
+}
+COMMON_SOURCES = ["kernels/common.hpp", "kernels/launch.hpp", "host/plan.hpp", "host/schedule.cpp"]
+
+
+def kernel_source_hash(kernel):
+    """sha256 over the sources a kernel's memory traffic depends on."""
+    import hashlib
+    h = hashlib.sha256()
+    base = os.path.join(ROOT, "context_varlen_attention_amd", "csrc")
+    for rel in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
+        with open(os.path.join(base, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary under profiles/.
+
+    Summaries carry lines ``<!-- traffic kernel=K workload=W sha=S bytes=B -->``
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the factor a plain
+    copy of known size gives).  Returns None when no summary matches the
+    kernel's current sources.
+    """
+    import glob
+    import re
+    want = kernel_source_hash(kernel)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for m in re.finditer(r"<!-- traffic (.*?) -->", f.read()):
+                kv = dict(x.split("=", 1) for x in m.group(1).split())
+                if kv.get("kernel") == kernel and kv.get("workload") == workload \
+                        and kv.get("sha") == want:
+                    return float(kv["bytes"])
+    return None
+
+
 def cpu_baseline(w, budget_s=12.0):
     """fp64 oracle forward+backward on a bounded sample: whole K/V head groups."""
     import oracle
@@ -267,12 +307,13 @@ def main():
                        peak=PEAK_HBM_GBS)
         if "achieved" in rec:
             rec["frac"] = rec["achieved"] / rec["peak"]
+        rec["source_sha"] = kernel_source_hash(name)
         kernels[name] = rec
     dom = max(kernels, key=lambda n: kernels[n]["ms_per_step"])
     d = kernels[dom]
     roofline = {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"),
                 "peak": d.get("peak"), "unit": d.get("unit"), "frac": d.get("frac"),
-                "traffic": None,
+                "traffic": measured_traffic(dom, w.name),
                 "per_launch": (f"{kfl[dom]:.4e} flop" if dom in kfl else f"{kby.get(dom, 0)} B")}
     fwd_ms = kernels.get("fwd", {}).get("ms_per_step")
     bwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("bwd"))

@@ -104,8 +104,11 @@ struct FwdShape {
   int32_t tile_kv;
 };
 FwdShape forward_shape(const Plan& p);
+// Query positions per dQ work-group (4 waves of 32 rows, heads_per_tile heads).
+int32_t dq_tile_q(const Plan& p);
 
-constexpr int32_t kWavesPerFwdTile = 4;
+constexpr int32_t kWavesPerFwdTile = 8;  // forward: two groups of 4 waves (ping-pong)
+constexpr int32_t kWavesPerDqTile = 4;
 constexpr int32_t kFwdMaxSpans = 8;   // forward kernel keeps a work item's spans in LDS
 constexpr int32_t kRowsPerWave = 32;
 constexpr int32_t kFwdTileKv = 64;

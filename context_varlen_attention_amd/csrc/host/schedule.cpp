@@ -288,6 +288,10 @@ FwdShape forward_shape(const Plan& p) {
   return s;
 }
 
+int32_t dq_tile_q(const Plan& p) {
+  return kRowsPerWave * (kWavesPerDqTile / forward_shape(p).heads_per_tile);
+}
+
 cva_status build_schedules(Plan& p) {
   // per-row visible intervals and the useful pair count
   const int32_t nseg = (int32_t)(p.segs.size() / SEG_INTS);
@@ -312,10 +316,11 @@ cva_status build_schedules(Plan& p) {
       return CVA_E_UNSUPPORTED;
     }
   }
-  if (kDqTileKv == fs.tile_kv)
+  const int32_t dq_q = dq_tile_q(p);
+  if (kDqTileKv == fs.tile_kv && dq_q == fs.tile_q)
     p.dq = p.fwd;  // same tile shape: the dQ kernel walks the forward schedule
   else
-    build_q_schedule(p, p.dq, fs.tile_q, kDqTileKv);
+    build_q_schedule(p, p.dq, dq_q, kDqTileKv);
   build_kv_schedule(p, p.dkdv, kDkvTileQ, kDkvTileKv);
 
   // rank-major rows outside every prefix are zero in dK/dV

@@ -43,19 +43,32 @@ namespace cva {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;              // 8 waves: two ping-pong groups of 4
 constexpr int kBN = 64;                    // keys per K/V tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: the base may lag the row max by 2^8
 
-// LDS layouts (16-byte chunks, XOR-swizzled so the MFMA operand reads hit
-// distinct banks):
-//   K: row r, logical chunk c at physical chunk c ^ (r & 7); read with
-//      ds_read_b128, 32 consecutive rows per instruction.
+// LDS layouts (16-byte chunks, XOR-swizzled so that the MFMA operand reads are
+// bank-conflict free on gfx950's 64 x 4-byte-bank LDS, as measured with the
+// SQ_LDS_BANK_CONFLICT counter):
+//   K: row r, logical chunk c at physical chunk c ^ k_swz(r); read with
+//      ds_read_b128, 32 consecutive rows per instruction (16 rows per pass).
+//      Rows of 256 bytes start on the same bank, so the XOR takes r & 15; rows
+//      of 128 or 384 bytes alternate bank halves, so it takes (r >> 1) & 7.
 //   V: row r, logical 32-byte group G at physical group G ^ f(r) with
 //      f(r) = (r & 3) ^ ((r & 1) << 2) for rows of 8+ groups (else r & 3); read
 //      with ds_read_b64_tr_b16, which takes 4 consecutive rows x 32 bytes per
 //      16 lanes.
-__device__ __forceinline__ int k_swz(int r) { return r & 7; }
+template <int DQK>
+__device__ __forceinline__ int k_swz(int r) {
+  if constexpr (DQK == 128)
+    return r & 15;
+  else
+    return (r >> 1) & 7;
+}
+// Per-lane K read offsets kept live: the swizzle permutes chunks inside aligned
+// groups of 2*kKoff chunks.
+template <int DQK>
+constexpr int kKoff = (DQK == 128) ? 8 : 4;
 
 template <int VCH>
 __device__ __forceinline__ int v_swz(int r) {  // XOR applied to the 16-byte chunk index
@@ -111,12 +124,51 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 // vmcnt 0, expcnt 7, lgkmcnt 15).
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// 4 bytes per lane from global memory into LDS (global_load_lds_dword): lane l's
+// word lands at LDS byte address lds + 4*l.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63].
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  switch (n) {
+#define CVA_WAIT_CASE(k) \
+  case k:                \
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (k & 15) | ((k >> 4) << 14)); \
+    break;
+    CVA_WAIT_CASE(0) CVA_WAIT_CASE(1) CVA_WAIT_CASE(2) CVA_WAIT_CASE(3) CVA_WAIT_CASE(4)
+    CVA_WAIT_CASE(5) CVA_WAIT_CASE(6) CVA_WAIT_CASE(7) CVA_WAIT_CASE(8) CVA_WAIT_CASE(9)
+    CVA_WAIT_CASE(10) CVA_WAIT_CASE(11) CVA_WAIT_CASE(12) CVA_WAIT_CASE(13) CVA_WAIT_CASE(14)
+    CVA_WAIT_CASE(15) CVA_WAIT_CASE(16) CVA_WAIT_CASE(17) CVA_WAIT_CASE(18) CVA_WAIT_CASE(19)
+    CVA_WAIT_CASE(20) CVA_WAIT_CASE(21) CVA_WAIT_CASE(22) CVA_WAIT_CASE(23) CVA_WAIT_CASE(24)
+    CVA_WAIT_CASE(25) CVA_WAIT_CASE(26) CVA_WAIT_CASE(27) CVA_WAIT_CASE(28) CVA_WAIT_CASE(29)
+    CVA_WAIT_CASE(30) CVA_WAIT_CASE(31) CVA_WAIT_CASE(32) CVA_WAIT_CASE(33) CVA_WAIT_CASE(34)
+    CVA_WAIT_CASE(35) CVA_WAIT_CASE(36) CVA_WAIT_CASE(37) CVA_WAIT_CASE(38) CVA_WAIT_CASE(39)
+    CVA_WAIT_CASE(40)
+#undef CVA_WAIT_CASE
+    default:
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      break;
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int NT>
 struct TileLoader {
+  static constexpr int kThreads = NT;              // threads that issue the tile loads
   static constexpr int KCH = DQK / 8, VCH = DV / 8;
   static constexpr int KN = kBN * KCH / kThreads;  // K slots per thread
   static constexpr int VN = kBN * VCH / kThreads;  // V slots per thread
@@ -129,7 +181,7 @@ struct TileLoader {
   // byte offset of this thread's 16-byte chunk inside its row (swizzled position)
   __device__ static uint32_t kchunk(int i, int tid) {
     const int s = i * kThreads + tid;
-    return (uint32_t)(((s % KCH) ^ k_swz(s / KCH)) * 16);
+    return (uint32_t)(((s % KCH) ^ k_swz<DQK>(s / KCH)) * 16);
   }
   __device__ static uint32_t vchunk(int i, int tid) {
     const int s = i * kThreads + tid;
@@ -148,17 +200,29 @@ struct TileLoader {
     }
   }
 
-  // Issue the direct-to-LDS loads of one K tile and one V tile.  kg / vg point at
+  // The same entries, read from a tile's 64-entry index slot in LDS.
+  __device__ static void read_index(int (&idx)[NIDX], const int32_t* sidx, int tid) {
+#pragma unroll
+    for (int i = 0; i < KN; ++i) idx[i] = sidx[krow(i, tid)];
+    if constexpr (!kShared) {
+#pragma unroll
+      for (int i = 0; i < VN; ++i) idx[KN + i] = sidx[vrow(i, tid)];
+    }
+  }
+
+  // Issue the direct-to-LDS loads of one K tile / one V tile.  kg / vg point at
   // the K/V head's first element; strides are bytes between gathered rows.
   // wave_off is the wave's first slot (uniform), so the LDS base is scalar.
-  __device__ static void issue(uint16_t* sk, uint16_t* sv, const char* kg, const char* vg,
-                               const int (&idx)[NIDX], uint32_t kstride, uint32_t vstride, int tid,
-                               int wave_off) {
+  __device__ static void issue_k(uint16_t* sk, const char* kg, const int (&idx)[NIDX],
+                                 uint32_t kstride, int tid, int wave_off) {
     const uint32_t kl = lds_addr(sk) + (uint32_t)wave_off * 16;
-    const uint32_t vl = lds_addr(sv) + (uint32_t)wave_off * 16;
 #pragma unroll
     for (int i = 0; i < KN; ++i)
       dma16(kg + ((uint64_t)(uint32_t)idx[i] * kstride + kchunk(i, tid)), kl + i * kThreads * 16);
+  }
+  __device__ static void issue_v(uint16_t* sv, const char* vg, const int (&idx)[NIDX],
+                                 uint32_t vstride, int tid, int wave_off) {
+    const uint32_t vl = lds_addr(sv) + (uint32_t)wave_off * 16;
 #pragma unroll
     for (int i = 0; i < VN; ++i) {
       const int id = kShared ? idx[i] : idx[KN + i];
@@ -172,13 +236,14 @@ struct TileLoader {
 // of a tile is one of a few per-lane offsets plus a compile-time constant.
 //
 // K (S^T A operand): step kt of 32-key block nb reads logical chunk 2kt + half of
-// row nb*32 + col, i.e. byte  koff[kt & 3] + 128*(kt >> 2) + nb*32*rowbytes.
+// row nb*32 + col, i.e. byte  koff[kt % KO] + 32*KO*(kt / KO) + nb*32*rowbytes
+// with KO = kKoff<DQK>.
 template <int DQK>
-__device__ __forceinline__ void k_offsets(uint32_t (&koff)[4], int col, int half) {
-  const int sw = k_swz(col);  // rows nb*32 + col share (row & 7) = col & 7
+__device__ __forceinline__ void k_offsets(uint32_t (&koff)[kKoff<DQK>], int col, int half) {
+  const int sw = k_swz<DQK>(col);  // rows nb*32 + col share the swizzle of row col
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    koff[u] = (uint32_t)(col * DQK * 2 + 32 * (u ^ (sw >> 1)) + 16 * (half ^ (sw & 1)));
+  for (int u = 0; u < kKoff<DQK>; ++u)
+    koff[u] = (uint32_t)(col * DQK * 2 + 16 * ((2 * u + half) ^ sw));
 }
 
 // V (PV A operand, transposing read): lane (s = lane & 15, g = lane >> 4) reads
@@ -243,67 +308,71 @@ struct SoftmaxState {
   f32x16_t acc[DB];
 };
 
-// One K/V tile, as two blocks of 32 keys, each: S^T, (mask), max / lazy rescale,
-// P, row sum, O^T += V^T P^T.  Working on 32 keys at a time keeps the score and
-// probability registers small enough for two waves per SIMD.
-template <typename E, int DQK, int DV, bool kPartial>
-__device__ __forceinline__ void tile_step(SoftmaxState<DV / 32>& st, const typename E::vec8 (&qf)[DQK / 16],
-                                          const uint16_t* sk, const uint16_t* sv,
-                                          const uint32_t (&koff)[4], const uint32_t (&voff)[DV / 32],
-                                          int kb0, int half, int lo1, int hi1, int lo2, int hi2) {
+// S^T = K (scaled Q)^T - base for the 64 keys of a tile (two 32-key blocks).
+template <typename E, int DQK>
+__device__ __forceinline__ void tile_scores(f32x16_t (&s)[2], const typename E::vec8 (&qf)[DQK / 16],
+                                            const uint16_t* sk, const uint32_t (&koff)[kKoff<DQK>],
+                                            float init) {
   constexpr int KSTEPS = DQK / 16;
+  constexpr int KO = kKoff<DQK>;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[nb][r] = init;
+#pragma unroll
+    for (int kt = 0; kt < KSTEPS; ++kt) {
+      const u32x4_t x = lds_read128(sk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
+      s[nb] = E::mfma32(as_vec8<E>(x), qf[kt], s[nb]);
+    }
+  }
+}
+
+// Element-wise mask of a partial tile: lane (query column, half) holds keys
+// kb0 + 32*nb + 8*(r/4) + 4*half + r%4; visible iff inside [lo1,hi1) or [lo2,hi2).
+__device__ __forceinline__ void tile_mask(f32x16_t (&s)[2], int kb0, int half, int lo1, int hi1,
+                                          int lo2, int hi2) {
+  int x = kb0 + 4 * half;
+  asm volatile("" : "+v"(x));  // keep x + constant per element (no hoisted per-element registers)
+  const uint32_t y1 = (uint32_t)(x - lo1), n1 = (uint32_t)(hi1 - lo1);
+  const uint32_t y2 = (uint32_t)(x - lo2), n2 = (uint32_t)(hi2 - lo2);
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t c = (uint32_t)(nb * 32 + 8 * (r >> 2) + (r & 3));
+      const bool vis = ((y1 + c) < n1) | ((y2 + c) < n2);
+      s[nb][r] = vis ? s[nb][r] : -INFINITY;
+    }
+  }
+}
+
+// Row max of a tile's scores relative to the base, both half-waves combined.
+__device__ __forceinline__ float tile_max(const f32x16_t (&s)[2]) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[nb][r], s[nb][r + 1]));
+  return wave_half_max(mx);
+}
+
+// P = exp2(S^T), packed to 16 bits, row sums from the packed values, and
+// O^T += V^T P^T over the tile's 64 keys (4 reduction steps of 16).
+template <typename E, int DV>
+__device__ __forceinline__ void tile_pv(SoftmaxState<DV / 32>& st, const f32x16_t (&s)[2],
+                                        const uint16_t* sv, const uint32_t (&voff)[DV / 32]) {
   constexpr int DB = DV / 32;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    // ---- S^T = K (scaled Q)^T - base for keys nb*32 .. nb*32+31 ----
-    f32x16_t s;
-    const float init = -st.base;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] = init;
-#pragma unroll
-    for (int kt = 0; kt < KSTEPS; ++kt) {
-      const u32x4_t x = lds_read128(sk + nb * 32 * DQK + (kt >> 2) * 64, koff[kt & 3]);
-      s = E::mfma32(as_vec8<E>(x), qf[kt], s);
-    }
-    if constexpr (kPartial) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int b = kb0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool vis = ((b >= lo1) & (b < hi1)) | ((b >= lo2) & (b < hi2));
-        s[r] = vis ? s[r] : -INFINITY;
-      }
-    }
-    // ---- row max relative to the base; move the base when it grew by > 2^8 ----
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[r], s[r + 1]));
-    mx = wave_half_max(mx);
-    // a row with nothing accumulated yet (l == 0) takes its first finite max as base
-    const bool grow = (mx > kRescaleThreshold) | ((st.l == 0.f) & (mx > -INFINITY));
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float shift = grow ? mx : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-shift);
-      st.base += shift;
-      st.l *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.acc[d][r] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] -= shift;
-    }
-    // ---- P = exp2(S^T), packed to 16 bits; row sum from the packed values ----
-    uint32_t pk[2][4];  // [16-key step][packed pairs]
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const uint32_t w = pack2<E>(__builtin_amdgcn_exp2f(s[r]), __builtin_amdgcn_exp2f(s[r + 1]));
-      pk[r >> 3][(r & 7) >> 1] = w;
-      st.l = dot2_acc<E>(w, st.l);
-    }
-    // ---- O^T += V^T P^T: 2 reduction steps of 16 keys ----
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const u32x4_t pv = {pk[ks][0], pk[ks][1], pk[ks][2], pk[ks][3]};
+      u32x4_t pv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 8 * ks + 2 * j;
+        pv[j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
+        st.l = dot2_acc<E>(pv[j], st.l);
+      }
       const typename E::vec8 bfrag = as_vec8<E>(pv);
       const int key0 = nb * 32 + ks * 16;
 #pragma unroll
@@ -316,19 +385,44 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DV / 32>& st, const typen
   }
 }
 
+// Forward work-group: 8 waves in two groups of 4 (group g = wave / 4; waves w and
+// w + 4 share a SIMD).  Each wave owns 32 query rows of one head.  Both groups
+// run the same sequence of steps, group 1 one phase behind group 0:
+//     X(-1) = S(0), Y(0), X(0), Y(1), X(1), ..., Y(N-1), X(N-1)
+// where X(n) = MFMA work (O += V(n)^T P(n), then the scores S(n+1) of the next
+// tile) and Y(n) = vector work (mask, max, lazy rescale, P(n) = exp2 S(n), row
+// sums).  A barrier ends every phase, so on every SIMD one wave is in an MFMA
+// step while the other is in a vector step.
+//
+// Group 0 also streams the tiles through an NS-deep LDS ring: at the start of
+// X(n) it issues K(n+NS) and V(n+NS-1) into the slots K(n) and V(n-1) used, plus
+// the prefix indices of tile n+2NS-1 into a small index ring, and at the end of
+// Y(n+1) waits only for the batch holding K(n+2) and V(n+1): NS-2 batches stay
+// in flight across every barrier.
+template <int DQK>
+constexpr int kStages = DQK > 128 ? 3 : 4;
+
 template <typename E, int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
-  using TL = TileLoader<DQK, DV>;
+__global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
+  using TL = TileLoader<DQK, DV, kThreads / 2>;
   constexpr int KSTEPS = DQK / 16;  // 16-wide reduction steps of S^T
   constexpr int DB = DV / 32;       // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kBN * DQK];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kBN * DV];
+  constexpr int NI = TL::NIDX;
+  constexpr int NS = kStages<DQK>;
+  constexpr int NIR = 2 * NS;       // index ring slots
+  constexpr int PER_BATCH = TL::KN + TL::VN + 1;  // loads per wave per full batch
+  constexpr uint32_t KBUF = kBN * DQK * 2, VBUF = kBN * DV * 2;  // bytes per tile buffer
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NS][kBN * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NS][kBN * DV];
+  __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][kBN];
   __shared__ __attribute__((aligned(16))) int32_t sSpan[kMaxSpans * 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, w4 = wave & 3;
   const int col = lane & 31, half = lane >> 5;
+  const int ltid = w4 * 64 + lane;  // thread index inside the group
 
   const int tile = blockIdx.x / P.n_head_groups;
   const int hg = blockIdx.x % P.n_head_groups;
@@ -337,11 +431,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
   const int32_t* sg = P.t.segs + seg * 8;
   const int q_len = sg[2], kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
   const int hpt = P.heads_per_tile;
-  const int head = hg * hpt + (wave % hpt);
+  const int head = hg * hpt + (w4 % hpt);
   const int kvh = head / P.group;
-  const int a = q0 + (wave / hpt) * 32 + col;  // segment-relative query index of this lane
+  const int rowblk = w4 / hpt + grp * (4 / hpt);
+  const int a = q0 + rowblk * 32 + col;  // segment-relative query index of this lane
   const bool valid = a < q_len;
-  const int row = q_row0 + a;                   // local row
+  const int row = q_row0 + a;             // local row
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
   const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
@@ -358,15 +453,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
   }
   if (tid < 4 * nspan) sSpan[tid] = P.t.fwd_spans[span0 * 4 + tid];
   __syncthreads();
+  int n_tiles = 0;
+  for (int sp = 0; sp < nspan; ++sp) {
+    const TileCursor c = span_start(sSpan, sp);
+    n_tiles += c.t_end - c.t;
+  }
 
-  // first tile's indices and loads, second tile's indices
-  const int wave_off = wave * 64;
-  TileCursor cur = span_start(sSpan, 0);
-  int idx[TL::NIDX];
-  TL::fetch_index(idx, kvi, cur.t * kBN, kv_len, tid);
-  TL::issue(sK[0], sV[0], kg, vg, idx, kstride, vstride, tid, wave_off);
-  TileCursor nxt = next_tile(cur, sSpan, nspan);
-  if (nxt.sp < nspan) TL::fetch_index(idx, kvi, nxt.t * kBN, kv_len, tid);
+  // ---- tile streaming (group 0) ----
+  // batch(n), n >= -NS: K(n+NS), V(n+NS-1), indices of tile n+2NS-1 (each if it exists)
+  TileCursor cI = span_start(sSpan, 0);  // next tile whose indices get fetched
+  int next_idx = 0;                      // its number
+  int bcount[NS];                        // loads per wave of the last batches (ring by n mod NS)
+#pragma unroll
+  for (int i = 0; i < NS; ++i) bcount[i] = 0;
+  auto fetch_idx = [&]() {  // indices of tile next_idx into ring slot next_idx % NIR
+    const int kb0 = cI.t * kBN;
+    dma4(kvi + min(kb0 + lane, kv_len - 1), lds_addr(sIdx[next_idx % NIR]));
+    ++next_idx;
+    cI = next_tile(cI, sSpan, nspan);
+  };
+  auto issue_batch = [&](int n) {
+    int cnt = 0;
+    int idx[NI];
+    const int mk = n + NS, mv = n + NS - 1, mi = n + 2 * NS - 1;
+    if (mk >= 0 && mk < n_tiles) {
+      TL::read_index(idx, sIdx[mk % NIR], ltid);
+      TL::issue_k(sK[mk % NS], kg, idx, kstride, ltid, w4 * 64);
+      cnt += TL::KN;
+    }
+    if (mv >= 0 && mv < n_tiles) {
+      TL::read_index(idx, sIdx[mv % NIR], ltid);
+      TL::issue_v(sV[mv % NS], vg, idx, vstride, ltid, w4 * 64);
+      cnt += TL::VN;
+    }
+    if (mi >= 2 * NS - 1 && mi < n_tiles) {  // earlier tiles' indices come with the prologue
+      fetch_idx();
+      cnt += 1;
+    }
+    bcount[(n + NS) % NS] = cnt;
+  };
+  // after this, the loads needed by X(n+1) (batch n+2-NS) have landed
+  auto wait_batch = [&](int n) {
+    int allowed = 0;
+#pragma unroll
+    for (int b = 0; b < NS - 2; ++b) allowed += bcount[(n - b + NS) % NS];
+    wait_vmem_le(allowed);
+  };
 
   // Q fragments, pre-scaled by scale*log2(e): lane holds Q[row][16t + 8*half .. +7].
   typename E::vec8 qf[KSTEPS];
@@ -389,8 +521,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
     const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
     lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
   }
+  wait_vmem_all();  // Q and row intervals, before any tile load is in flight
+  if (grp == 0) {
+    // indices of tiles 0 .. 2NS-2, then batches -NS .. -2
+    for (int m = 0; m < 2 * NS - 1 && m < n_tiles; ++m) fetch_idx();
+    wait_vmem_all();
+    for (int n = -NS; n <= -2; ++n) issue_batch(n);
+    wait_batch(-2);  // batch -NS: K(0)
+  }
 
-  uint32_t koff[4], voff[DB];
+  uint32_t koff[kKoff<DQK>], voff[DB];
   k_offsets<DQK>(koff, col, half);
   v_offsets<DV>(voff, lane);
 
@@ -399,38 +539,88 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
   st.l = 0.f;
 #pragma unroll
   for (int d = 0; d < DB; ++d) st.acc[d] = zero16();
+  f32x16_t s[2];      // scores of a tile between its X step and its Y step
+  u32x4_t pk[2][2];   // packed P of a tile between its Y step and its X step
 
-  wait_vmem_all();
-  __syncthreads();
-
-  // Main loop, unrolled by two so that each half reads a fixed buffer (constant
-  // LDS offsets) while the next tile streams into the other one.
-  auto half_step = [&](auto bufc) -> bool {
-    constexpr int B = decltype(bufc)::value;
-    // Nothing is in flight here (the previous step ended with vmcnt(0) and a
-    // barrier); saying so to the compiler keeps it from waiting on the tile
-    // loads below when it checks the index registers.
-    wait_vmem_all();
-    const bool has_next = nxt.sp < nspan;
-    // loads of the next tile (indices fetched one tile ago) and indices of the one after
-    if (has_next) {
-      TL::issue(sK[B ^ 1], sV[B ^ 1], kg, vg, idx, kstride, vstride, tid, wave_off);
-      const TileCursor nn = next_tile(nxt, sSpan, nspan);
-      if (nn.sp < nspan) TL::fetch_index(idx, kvi, nn.t * kBN, kv_len, tid);
-    }
-    if (cur.partial)
-      tile_step<E, DQK, DV, true>(st, qf, sK[B], sV[B], koff, voff, cur.t * kBN, half, lo1, hi1, lo2, hi2);
-    else
-      tile_step<E, DQK, DV, false>(st, qf, sK[B], sV[B], koff, voff, cur.t * kBN, half, lo1, hi1, lo2, hi2);
-    if (!has_next) return false;
-    wait_vmem_all();
-    __syncthreads();
-    cur = nxt;
-    nxt = next_tile(nxt, sSpan, nspan);
-    return true;
+  auto pv = [&](int n) {
+    const uint16_t* sv = (const uint16_t*)((const char*)sV + (n % NS) * VBUF);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const typename E::vec8 bfrag = as_vec8<E>(pk[nb][ks]);
+        const int key0 = nb * 32 + ks * 16;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const u32x2_t lo = lds_read_tr(sv + key0 * DV, voff[d]);
+          const u32x2_t hi = lds_read_tr(sv + (key0 + 8) * DV, voff[d]);
+          st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bfrag, st.acc[d]);
+        }
+      }
   };
-  while (half_step(std::integral_constant<int, 0>{}) && half_step(std::integral_constant<int, 1>{})) {
+  auto scores = [&](int n) {  // S(n) from K ring slot n % NS
+    tile_scores<E, DQK>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, -st.base);
+  };
+  auto softmax = [&](const TileCursor& c) {
+    if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
+    const float mx = tile_max(s);
+    // a row with nothing accumulated yet (l == 0) takes its first finite max as base
+    const bool grow = (mx > kRescaleThreshold) | ((st.l == 0.f) & (mx > -INFINITY));
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float shift = grow ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      st.base += shift;
+      st.l *= alpha;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[d][r] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][r] -= shift;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * ks + 2 * j;
+          pk[nb][ks][j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
+          st.l = dot2_acc<E>(pk[nb][ks][j], st.l);
+        }
+  };
+
+  TileCursor cY = span_start(sSpan, 0);  // tile whose Y step comes next
+  __syncthreads();                       // K(0) is in LDS
+  if (grp == 1) __syncthreads();         // group 1 runs one phase behind
+
+  // X(-1) = S(0); Y(0)
+  if (grp == 0) issue_batch(-1);
+  scores(0);
+  __syncthreads();
+  softmax(cY);
+  cY = next_tile(cY, sSpan, nspan);
+  if (grp == 0) wait_batch(-1);
+  __syncthreads();
+  // X(n) = PV(n) + S(n+1); Y(n+1)
+  for (int n = 0; n + 1 < n_tiles; ++n) {
+    if (grp == 0) issue_batch(n);
+    pv(n);
+    __builtin_amdgcn_sched_barrier(0);
+    scores(n + 1);
+    __syncthreads();
+    softmax(cY);
+    cY = next_tile(cY, sSpan, nspan);
+    if (grp == 0) wait_batch(n);
+    __syncthreads();
   }
+  // X(N-1) = PV(N-1)
+  pv(n_tiles - 1);
+  __syncthreads();
+  if (grp == 0) __syncthreads();  // matches group 1's extra barrier
+  if (grp == 0) wait_vmem_all();  // nothing may stay in flight past the kernel's end
 
   // ---- epilogue: normalise, write O and LSE ----
   const float l_tot = wave_half_sum(st.l);
@@ -457,7 +647,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_mfma_kernel(FwdParams P) {
 // fp32 correctness kernel: one thread per (query row, head), keys one at a time,
 // plain online softmax in fp32 on the VALU.  Uses the same tile schedule.
 template <int DQK, int DV>
-__global__ __launch_bounds__(128) void fwd_fp32_kernel(FwdParams P) {
+__global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdParams P) {
   const int tile = blockIdx.x / P.n_head_groups;
   const int hg = blockIdx.x % P.n_head_groups;
   const int32_t* tr = P.t.fwd_tiles + tile * 5;
@@ -521,7 +711,7 @@ hipError_t launch_fp32(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.n_head_groups;
   if (grid == 0) return hipSuccess;
   if (hook) hook->before(K_FWD, s);
-  hipLaunchKernelGGL((fwd_fp32_kernel<DQK, DV>), dim3(grid), dim3(128), 0, s, p);
+  hipLaunchKernelGGL((fwd_fp32_kernel<DQK, DV>), dim3(grid), dim3(256), 0, s, p);
   if (hook) hook->after(K_FWD, s);
   return hipGetLastError();
 }
