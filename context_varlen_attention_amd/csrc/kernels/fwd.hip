@@ -309,7 +309,7 @@ struct SoftmaxState {
 };
 
 // S^T = K (scaled Q)^T - base for the 64 keys of a tile (two 32-key blocks).
-template <typename E, int DQK>
+template <typename E, int DQK, bool kInit = true>
 __device__ __forceinline__ void tile_scores(f32x16_t (&s)[2], const typename E::vec8 (&qf)[DQK / 16],
                                             const uint16_t* sk, const uint32_t (&koff)[kKoff<DQK>],
                                             float init) {
@@ -317,8 +317,10 @@ __device__ __forceinline__ void tile_scores(f32x16_t (&s)[2], const typename E::
   constexpr int KO = kKoff<DQK>;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
+    if constexpr (kInit) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[nb][r] = init;
+      for (int r = 0; r < 16; ++r) s[nb][r] = init;
+    }
 #pragma unroll
     for (int kt = 0; kt < KSTEPS; ++kt) {
       const u32x4_t x = lds_read128(sk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
@@ -396,7 +398,7 @@ __device__ __forceinline__ void tile_pv(SoftmaxState<DV / 32>& st, const f32x16_
 //
 // Group 0 also streams the tiles through an NS-deep LDS ring: at the start of
 // X(n) it issues K(n+NS) and V(n+NS-1) into the slots K(n) and V(n-1) used, plus
-// the prefix indices of tile n+2NS-1 into a small index ring, and at the end of
+// the prefix indices of tile n+2NS into a small index ring, and at the end of
 // Y(n+1) waits only for the batch holding K(n+2) and V(n+1): NS-2 batches stay
 // in flight across every barrier.
 template <int DQK>
@@ -472,21 +474,26 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     ++next_idx;
     cI = next_tile(cI, sSpan, nspan);
   };
+  // Indices of batch n's K and V tiles, read from the index ring ahead of the
+  // batch (in the vector step before it) so that the loads issue at once.
+  int idxK[NI], idxV[NI];
+  auto prepare_batch = [&](int n) {
+    const int mk = n + NS, mv = n + NS - 1;
+    if (mk >= 0 && mk < n_tiles) TL::read_index(idxK, sIdx[mk % NIR], ltid);
+    if (mv >= 0 && mv < n_tiles) TL::read_index(idxV, sIdx[mv % NIR], ltid);
+  };
   auto issue_batch = [&](int n) {
     int cnt = 0;
-    int idx[NI];
-    const int mk = n + NS, mv = n + NS - 1, mi = n + 2 * NS - 1;
+    const int mk = n + NS, mv = n + NS - 1, mi = n + 2 * NS;
     if (mk >= 0 && mk < n_tiles) {
-      TL::read_index(idx, sIdx[mk % NIR], ltid);
-      TL::issue_k(sK[mk % NS], kg, idx, kstride, ltid, w4 * 64);
+      TL::issue_k(sK[mk % NS], kg, idxK, kstride, ltid, w4 * 64);
       cnt += TL::KN;
     }
     if (mv >= 0 && mv < n_tiles) {
-      TL::read_index(idx, sIdx[mv % NIR], ltid);
-      TL::issue_v(sV[mv % NS], vg, idx, vstride, ltid, w4 * 64);
+      TL::issue_v(sV[mv % NS], vg, idxV, vstride, ltid, w4 * 64);
       cnt += TL::VN;
     }
-    if (mi >= 2 * NS - 1 && mi < n_tiles) {  // earlier tiles' indices come with the prologue
+    if (mi >= 2 * NS && mi < n_tiles) {  // earlier tiles' indices come with the prologue
       fetch_idx();
       cnt += 1;
     }
@@ -523,11 +530,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   }
   wait_vmem_all();  // Q and row intervals, before any tile load is in flight
   if (grp == 0) {
-    // indices of tiles 0 .. 2NS-2, then batches -NS .. -2
-    for (int m = 0; m < 2 * NS - 1 && m < n_tiles; ++m) fetch_idx();
+    // indices of tiles 0 .. 2NS-1, then batches -NS .. -2
+    for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
     wait_vmem_all();
-    for (int n = -NS; n <= -2; ++n) issue_batch(n);
+    for (int n = -NS; n <= -2; ++n) {
+      prepare_batch(n);
+      issue_batch(n);
+    }
     wait_batch(-2);  // batch -NS: K(0)
+    prepare_batch(-1);
   }
 
   uint32_t koff[kKoff<DQK>], voff[DB];
@@ -558,8 +569,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         }
       }
   };
-  auto scores = [&](int n) {  // S(n) from K ring slot n % NS
-    tile_scores<E, DQK>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, -st.base);
+  auto scores = [&](int n) {  // S(n) from K ring slot n % NS; s holds -base already
+    tile_scores<E, DQK, false>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, 0.f);
+  };
+  auto init_scores = [&]() {  // next tile's accumulators start at -base
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
   };
   auto softmax = [&](const TileCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
@@ -592,35 +609,46 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         }
   };
 
+  // Group 0 streams the tiles: it issues batch n at the start of its MFMA step
+  // X(n) (phase 2n+2), and at the end of its vector step Y(n+1) waits for batch
+  // n+2-NS and reads the indices of batch n+1.
   TileCursor cY = span_start(sSpan, 0);  // tile whose Y step comes next
   __syncthreads();                       // K(0) is in LDS
   if (grp == 1) __syncthreads();         // group 1 runs one phase behind
 
   // X(-1) = S(0); Y(0)
   if (grp == 0) issue_batch(-1);
+  init_scores();
   scores(0);
   __syncthreads();
   softmax(cY);
   cY = next_tile(cY, sSpan, nspan);
-  if (grp == 0) wait_batch(-1);
+  init_scores();
+  if (grp == 0) {
+    wait_batch(-1);
+    prepare_batch(0);
+  }
   __syncthreads();
   // X(n) = PV(n) + S(n+1); Y(n+1)
   for (int n = 0; n + 1 < n_tiles; ++n) {
     if (grp == 0) issue_batch(n);
     pv(n);
-    __builtin_amdgcn_sched_barrier(0);
     scores(n + 1);
     __syncthreads();
     softmax(cY);
     cY = next_tile(cY, sSpan, nspan);
-    if (grp == 0) wait_batch(n);
+    init_scores();
+    if (grp == 0) {
+      wait_batch(n);
+      prepare_batch(n + 1);
+    }
     __syncthreads();
   }
   // X(N-1) = PV(N-1)
   pv(n_tiles - 1);
   __syncthreads();
   if (grp == 0) __syncthreads();  // matches group 1's extra barrier
-  if (grp == 0) wait_vmem_all();  // nothing may stay in flight past the kernel's end
+  wait_vmem_all();                // nothing may stay in flight past the kernel's end
 
   // ---- epilogue: normalise, write O and LSE ----
   const float l_tot = wave_half_sum(st.l);
