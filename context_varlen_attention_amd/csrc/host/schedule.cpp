@@ -206,7 +206,11 @@ void build_kv_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_
       for (int32_t a0 = 0, qt = 0; a0 < q_len; a0 += tile_q, ++qt) {
         tile_sets(p, sg, a0, std::min(q_len, a0 + tile_q), w);
         tile_spans(w, tile_kv);
-        for (const SpanOut& x : w.spans) {
+        // a Q tile that runs past the segment's end takes the element-wise
+        // path, which also masks the rows past the end
+        const bool short_tile = a0 + tile_q > q_len;
+        for (SpanOut x : w.spans) {
+          if (short_tile) x.partial = 1;
           qspans.push_back({sg, qt, x});
           for (int32_t t = x.t0; t < std::min(x.t1, nkt); ++t) ++count[t];
         }
@@ -322,6 +326,12 @@ cva_status build_schedules(Plan& p) {
   else
     build_q_schedule(p, p.dq, dq_q, kDqTileKv);
   build_kv_schedule(p, p.dkdv, kDkvTileQ, kDkvTileKv);
+  for (int32_t t = 0; t < p.dkdv.n_tiles(); ++t) {
+    if (p.dkdv.tiles[(size_t)t * KT_INTS + KT_NSPAN] > kDkvMaxSpans) {
+      set_error("mask gives a K/V tile more query spans than the dK/dV kernel supports");
+      return CVA_E_UNSUPPORTED;
+    }
+  }
 
   // rank-major rows outside every prefix are zero in dK/dV
   std::vector<char> covered((size_t)p.T, 0);

@@ -26,6 +26,7 @@
 //                     accumulators.
 //   dq_kernel         Q-stationary like the forward: S^T = K Q^T, dP^T = V dO^T,
 //                     dQ^T += K^T dS^T.
+#include "../host/plan.hpp"
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -82,23 +83,111 @@ __global__ __launch_bounds__(kThreads) void zero_rows_kernel(BwdParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// dK / dV, K/V-stationary
+// LDS layout of streamed row tiles (Q, dO, K): rows padded to a power of two
+// (128, 256 or 512 bytes) and 16-byte chunks XOR-swizzled by bwd_swz(row), so
+// that both the row reads (ds_read_b128, 16 consecutive rows per pass) and the
+// transposing reads (ds_read_b64_tr_b16, 4 rows x 32 bytes per 16 lanes) are
+// bank-conflict free on the 64-bank LDS.
 // ---------------------------------------------------------------------------
+template <int D>
+constexpr int kRowBytes = D * 2 <= 128 ? 128 : (D * 2 <= 256 ? 256 : 512);
+
+template <int RB>
+__device__ __forceinline__ int bwd_swz(int r) {
+  if constexpr (RB >= 256)
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  else
+    return (r >> 1) & 7;
+}
+
+template <int RB>
+__device__ __forceinline__ uint32_t swz_off(int r, int colbytes) {
+  return (uint32_t)(r * RB + (((colbytes >> 4) ^ bwd_swz<RB>(r)) << 4) + (colbytes & 15));
+}
+
+// Per-lane offsets of the two operand reads of a streamed tile with D columns.
+//  rows:  A operand = 32 rows x 16 columns, lane (row 32*qs + l%32, half h) reads
+//         columns 16*kt + 8h .. +7:  row_off[kt % KO] + (kt / KO) * 32*KO + qs*32*RB
+//  trans: A operand = 32 columns x 16 rows (transposed), lane (s = l&15, g = l>>4)
+//         reads 4 rows (row0 + s>>2 ...) of column 32*blk + 16*(g&1) + 4*(s&3) where
+//         row0 = 32*qs + 16*st + 4*h + 8*hi:  tr_off[hi][blk] + (32*qs + 16*st)*RB
+template <int D>
+struct TileOffsets {
+  static constexpr int RB = kRowBytes<D>;
+  static constexpr int KO = RB >= 256 ? 8 : 4;
+  static constexpr int NB = D / 32;
+  uint32_t row_off[KO];
+  uint32_t tr_off[2][NB];
+  __device__ void init(int lane) {
+    const int col = lane & 31, half = lane >> 5;
+#pragma unroll
+    for (int u = 0; u < KO; ++u) row_off[u] = swz_off<RB>(col, (2 * u + half) * 16);
+    const int s = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi)
+#pragma unroll
+      for (int blk = 0; blk < NB; ++blk)
+        tr_off[hi][blk] = swz_off<RB>(4 * (g >> 1) + 8 * hi + (s >> 2), (blk * 32 + 16 * (g & 1) + 4 * (s & 3)) * 2);
+  }
+  __device__ u32x4_t row(const char* base, int qs, int kt) const {
+    return *(const u32x4_t*)(base + qs * 32 * RB + (kt / KO) * 32 * KO + row_off[kt % KO]);
+  }
+  __device__ u32x2_t trans(const char* base, int rows0, int hi, int blk) const {
+    return lds_read_tr16((const uint16_t*)(base + rows0 * RB + tr_off[hi][blk]));
+  }
+};
+
+// DMA of a 64-row tile with D columns into LDS (kRowBytes layout) by 256 threads;
+// row_src(r) gives the global address of row r's first element.
+template <int D, typename RowSrc>
+__device__ __forceinline__ void dma_rows(char* lds, RowSrc row_src, int tid, int wave) {
+  constexpr int RB = kRowBytes<D>, CH = RB / 16, VC = D / 8;
+  constexpr int N = 64 * CH / 256;
+  const uint32_t base = lds_addr(lds) + (uint32_t)wave * 64 * 16;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int s = i * 256 + tid;
+    const int r = s / CH;
+    int c = (s % CH) ^ bwd_swz<RB>(r);
+    if (c >= VC) c = 0;  // row padding: any in-bounds source
+    dma16(row_src(r) + c * 16, base + i * 256 * 16);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV, K/V-stationary.  A work-group owns 128 keys of one K/V head (4 waves x
+// 32 keys, K and V of the lane's key in registers) and walks, for every query
+// head of the group, the 64-row Q tiles of both local chunks that see its keys.
+// Q, dO, LSE, Delta and the row intervals of those tiles stream through an
+// NS-deep LDS ring (DMA issued NS-1 tiles ahead).  Per 32 query rows:
+//   S = Q K^T, dP = dO V^T (A = rows from LDS, B = K / V from registers),
+//   P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - Delta),
+//   dV^T += dO^T P, dK^T += Q^T dS (A = transposing reads, B = P / dS in place).
+// Each rank-major key row is written once: no atomics, deterministic.
+// ---------------------------------------------------------------------------
+template <int DQK>
+constexpr int kDkvStages = DQK > 128 ? 3 : 4;
+
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
-  constexpr int BQ = 64;          // queries per Q tile
-  constexpr int QS = DQK / 16;    // reduction steps over Dqk
-  constexpr int VS = DV / 16;     // reduction steps over Dv
-  constexpr int QLD = DQK + 8;    // LDS row strides (elements): 16-byte aligned rows
-  constexpr int OLD = DV + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[BQ * QLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sO[BQ * OLD];
-  __shared__ float sL[BQ];
-  __shared__ float sD[BQ];
-  __shared__ int32_t sIv[BQ * 4];
+  constexpr int BQ = 64;           // queries per Q tile
+  constexpr int QS = DQK / 16;     // reduction steps over Dqk
+  constexpr int VS = DV / 16;      // reduction steps over Dv
+  constexpr int NS = kDkvStages<DQK>;
+  using QO = TileOffsets<DQK>;
+  using OO = TileOffsets<DV>;
+  constexpr int QB = BQ * QO::RB, OB = BQ * OO::RB;
+  constexpr int QN = 64 * (QO::RB / 16) / 256, ON = 64 * (OO::RB / 16) / 256;
+  __shared__ __attribute__((aligned(16))) char sQ[NS][QB];
+  __shared__ __attribute__((aligned(16))) char sO[NS][OB];
+  __shared__ __attribute__((aligned(16))) float sL[NS][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
+  __shared__ __attribute__((aligned(16))) int32_t sIv[NS][BQ * 4];
+  __shared__ __attribute__((aligned(16))) int32_t sSpan[kDkvMaxSpans * 4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   const int tile = blockIdx.x / P.hkv;
@@ -106,7 +195,9 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
   const int32_t* tr = P.t.kv_tiles + tile * 5;
   const int seq = tr[0], k0 = tr[1], keys = tr[2], span0 = tr[3], nspan = tr[4];
   // the longer prefix of the sub-sequence (its second segment) indexes every key of the tile
+  const int32_t* segA = P.t.segs + (2 * seq) * 8;
   const int32_t* segB = P.t.segs + (2 * seq + 1) * 8;
+  const int qlenA = segA[2], row0A = segA[4], qlenB = segB[2], row0B = segB[4];
   const int32_t* kvi = P.t.kv_index + segB[5];
   const int kl = wave * 32 + col;          // key of this lane within the tile
   const int kpos = k0 + kl;                // in-sequence key position
@@ -115,8 +206,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
 
   const uint16_t* __restrict__ kg = (const uint16_t*)P.k;
   const uint16_t* __restrict__ vg = (const uint16_t*)P.v;
-  const uint16_t* __restrict__ qg = (const uint16_t*)P.q;
-  const uint16_t* __restrict__ og = (const uint16_t*)P.dout;
 
   // K^T and V^T operands in registers: lane holds K[key][16s + 8*half .. +7]
   typename E::vec8 kf[QS], vf[VS];
@@ -136,115 +225,162 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
       vf[s] = as_vec8<E>(x);
     }
   }
+  if (tid < 4 * nspan) sSpan[tid] = P.t.kv_spans[span0 * 4 + tid];
+  wait_vmem_all();
+  __syncthreads();
+
+  // ---- cursor over the work item's Q tiles: heads of the group x spans x q tiles ----
+  struct Cur {
+    int hh, sp, qt, qt_end, seg, partial;
+  };
+  auto span_at = [&](Cur c, int sp) {
+    const int4 r = *(const int4*)(sSpan + 4 * sp);
+    c.sp = sp;
+    c.seg = __builtin_amdgcn_readfirstlane(r.x);
+    c.qt = __builtin_amdgcn_readfirstlane(r.y);
+    c.qt_end = __builtin_amdgcn_readfirstlane(r.z);
+    c.partial = __builtin_amdgcn_readfirstlane(r.w);
+    return c;
+  };
+  auto advance = [&](Cur c) {
+    if (++c.qt >= c.qt_end) {
+      int sp = c.sp + 1;
+      if (sp >= nspan) {
+        sp = 0;
+        ++c.hh;
+      }
+      c = span_at(c, sp);
+    }
+    return c;
+  };
+  int n_tiles = 0;
+  for (int sp = 0; sp < nspan; ++sp) {
+    Cur c = span_at(Cur{0, 0, 0, 0, 0, 0}, sp);
+    n_tiles += c.qt_end - c.qt;
+  }
+  n_tiles *= P.group;
+
+  // ---- streaming: batch for tile m -> ring slot m % NS ----
+  const char* qgb = (const char*)P.q;
+  const char* ogb = (const char*)P.dout;
+  // loads per wave and batch (the same for every batch)
+  const int per_batch = QN + ON + (wave < 3 ? 1 : 0);
+  auto issue = [&](const Cur& c, int m) {
+    const int slot = m % NS;
+    const int head = kvh * P.group + c.hh;
+    const bool isB = (c.seg & 1) != 0;
+    const int q_len = isB ? qlenB : qlenA, q_row0 = isB ? row0B : row0A;
+    const int a0 = c.qt * BQ;
+    auto lrow = [&](int r) { return q_row0 + min(a0 + r, q_len - 1); };
+    dma_rows<DQK>(sQ[slot], [&](int r) { return qgb + ((int64_t)lrow(r) * P.hq + head) * (DQK * 2); }, tid, wave);
+    dma_rows<DV>(sO[slot], [&](int r) { return ogb + ((int64_t)lrow(r) * P.hq + head) * (DV * 2); }, tid, wave);
+    if (wave == 0)
+      dma4(P.lse + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
+    else if (wave == 1)
+      dma4(P.delta + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sD[slot]));
+    else if (wave == 2)
+      dma16(P.t.row_iv + (int64_t)lrow(lane) * 4, lds_addr(sIv[slot]));
+  };
+  // wait until tile m's batch has landed; the batches issued after it (tiles
+  // m+1 .. m+NS-2, those that exist) may stay in flight
+  auto wait_for = [&](int m) {
+    const int later = min(m + NS - 1, n_tiles) - (m + 1);
+    wait_vmem_le(later > 0 ? later * per_batch : 0);
+  };
+
+  QO qo;
+  OO oo;
+  qo.init(lane);
+  oo.init(lane);
 
   f32x16_t dk[DQK / 32], dv[DV / 32];
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) dk[d] = zero16();
 #pragma unroll
   for (int d = 0; d < DV / 32; ++d) dv[d] = zero16();
-
   const float sl2 = P.scale_log2;
 
-  for (int hh = 0; hh < P.group; ++hh) {
-    const int head = kvh * P.group + hh;
-    for (int sp = 0; sp < nspan; ++sp) {
-      const int32_t* spr = P.t.kv_spans + (span0 + sp) * 4;
-      const int seg = spr[0], qt0 = spr[1], qt1 = spr[2];
-      const bool partial = spr[3] != 0;
-      const int32_t* sg = P.t.segs + seg * 8;
-      const int q_len = sg[2], q_row0 = sg[4];
-      for (int qt = qt0; qt < qt1; ++qt) {
-        const int a0 = qt * BQ;
-        __syncthreads();
-        // ---- stage the Q tile, dO tile, LSE, Delta and row intervals ----
-        {
-          constexpr int CQ = DQK / 8;
-          for (int idx = tid; idx < BQ * CQ; idx += kThreads) {
-            const int r = idx / CQ, c = idx % CQ;
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (a0 + r < q_len)
-              x = *(const u32x4_t*)(qg + ((int64_t)(q_row0 + a0 + r) * P.hq + head) * DQK + c * 8);
-            *(u32x4_t*)(sQ + r * QLD + c * 8) = x;
-          }
-          constexpr int CO = DV / 8;
-          for (int idx = tid; idx < BQ * CO; idx += kThreads) {
-            const int r = idx / CO, c = idx % CO;
-            u32x4_t x = {0u, 0u, 0u, 0u};
-            if (a0 + r < q_len)
-              x = *(const u32x4_t*)(og + ((int64_t)(q_row0 + a0 + r) * P.hq + head) * DV + c * 8);
-            *(u32x4_t*)(sO + r * OLD + c * 8) = x;
-          }
-          if (tid < BQ) {
-            const int r = tid;
-            const bool ok = a0 + r < q_len;
-            const int64_t lr = (int64_t)head * P.t_loc + q_row0 + a0 + r;
-            sL[r] = ok ? P.lse[lr] * kLog2e : INFINITY;
-            sD[r] = ok ? P.delta[lr] : 0.f;
-            const int32_t* iv = P.t.row_iv + (int64_t)(q_row0 + a0 + r) * 4;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sIv[r * 4 + j] = ok ? iv[j] : 0;
-          }
-        }
-        __syncthreads();
+  Cur cI = span_at(Cur{0, 0, 0, 0, 0, 0}, 0);  // next tile to issue
+  Cur cC = cI;                                  // tile being computed
+  for (int m = 0; m < NS - 1 && m < n_tiles; ++m) {
+    issue(cI, m);
+    cI = advance(cI);
+  }
+  wait_for(0);
+  __syncthreads();
 
+  for (int n = 0; n < n_tiles; ++n) {
+    if (n + NS - 1 < n_tiles) {
+      issue(cI, n + NS - 1);  // into the slot tile n-1 used
+      cI = advance(cI);
+    }
+    const int slot = n % NS;
+    const char* q_s = sQ[slot];
+    const char* o_s = sO[slot];
+    const bool isB = (cC.seg & 1) != 0;
+    const int q_rem = (isB ? qlenB : qlenA) - cC.qt * BQ;  // valid rows of this tile
+    const bool partial = cC.partial != 0;
 #pragma unroll
-        for (int qs = 0; qs < BQ / 32; ++qs) {
-          // S[q][key] = Q K^T and dP = dO V^T for 32 queries x this wave's 32 keys
-          f32x16_t s = zero16(), dp = zero16();
-          {
-            const uint16_t* qrow = sQ + (qs * 32 + col) * QLD + 8 * half;
+    for (int qs = 0; qs < BQ / 32; ++qs) {
+      // S[q][key] and dP[q][key] for 32 queries x this wave's 32 keys
+      f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
-            for (int st = 0; st < QS; ++st)
-              s = E::mfma32(as_vec8<E>(*(const u32x4_t*)(qrow + 16 * st)), kf[st], s);
-            const uint16_t* orow = sO + (qs * 32 + col) * OLD + 8 * half;
+      for (int st = 0; st < QS; ++st) s = E::mfma32(as_vec8<E>(qo.row(q_s, qs, st)), kf[st], s);
 #pragma unroll
-            for (int st = 0; st < VS; ++st)
-              dp = E::mfma32(as_vec8<E>(*(const u32x4_t*)(orow + 16 * st)), vf[st], dp);
+      for (int st = 0; st < VS; ++st) dp = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), vf[st], dp);
+      // lane holds query qs*32 + 8i + 4*half + j (r = 4i + j) for key kpos
+      f32x4_t lv[4], dv4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        lv[i] = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i + 4 * half);
+        dv4[i] = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * i + 4 * half);
+      }
+      uint32_t pp[2][4], pd[2][4];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float pv[2], dsv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int i = (r + u) >> 2, j = (r + u) & 3;
+          float x = fmaf(s[r + u], sl2, -lv[i][j] * kLog2e);
+          if (partial) {
+            const int q = qs * 32 + 8 * i + 4 * half + j;
+            const int4 iv = *(const int4*)(sIv[slot] + 4 * q);
+            const bool vis = (q < q_rem) & (((kpos >= iv.x) & (kpos < iv.y)) | ((kpos >= iv.z) & (kpos < iv.w)));
+            x = vis ? x : -INFINITY;
           }
-          // lane holds query qs*32 + 8i + 4*half + j (r = 4i + j) for key kpos
-          uint32_t pp[2][4], pd[2][4];
+          const float p = __builtin_amdgcn_exp2f(x);
+          pv[u] = p;
+          dsv[u] = p * (dp[r + u] - dv4[i][j]);
+        }
+        pp[r >> 3][(r & 7) >> 1] = pack2<E>(pv[0], pv[1]);
+        pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
+      }
+      // dV^T[d][key] += sum_q dO^T[d][q] P[q][key];  dK^T += Q^T dS
 #pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            float pv[2], dsv[2];
+      for (int st = 0; st < 2; ++st) {
+        const int rows0 = qs * 32 + st * 16;
+        const typename E::vec8 bp = as_vec8<E>(u32x4_t{pp[st][0], pp[st][1], pp[st][2], pp[st][3]});
+        const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const int q = qs * 32 + 8 * ((r + u) >> 2) + 4 * half + ((r + u) & 3);
-              float x = s[r + u] * sl2 - sL[q];
-              if (partial) {
-                const int32_t* iv = sIv + q * 4;
-                const bool vis = (kpos >= iv[0] && kpos < iv[1]) || (kpos >= iv[2] && kpos < iv[3]);
-                x = vis ? x : -INFINITY;
-              }
-              const float p = __builtin_amdgcn_exp2f(x);
-              pv[u] = p;
-              dsv[u] = p * (dp[r + u] - sD[q]);
-            }
-            pp[r >> 3][(r & 7) >> 1] = pack2<E>(pv[0], pv[1]);
-            pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
-          }
-          // dV^T[d][key] += sum_q dO^T[d][q] P[q][key];  dK^T += Q^T dS
+        for (int d = 0; d < DV / 32; ++d) {
+          const u32x2_t lo = oo.trans(o_s, rows0, 0, d);
+          const u32x2_t hi = oo.trans(o_s, rows0, 1, d);
+          dv[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bp, dv[d]);
+        }
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int qb = qs * 32 + st * 16 + 4 * half;
-            const typename E::vec8 bp = as_vec8<E>(u32x4_t{pp[st][0], pp[st][1], pp[st][2], pp[st][3]});
-            const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
-#pragma unroll
-            for (int d = 0; d < DV / 32; ++d) {
-              const u32x2_t lo = tr_operand(sO, OLD, qb, d * 32, lane);
-              const u32x2_t hi = tr_operand(sO, OLD, qb + 8, d * 32, lane);
-              dv[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bp, dv[d]);
-            }
-#pragma unroll
-            for (int d = 0; d < DQK / 32; ++d) {
-              const u32x2_t lo = tr_operand(sQ, QLD, qb, d * 32, lane);
-              const u32x2_t hi = tr_operand(sQ, QLD, qb + 8, d * 32, lane);
-              dk[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, dk[d]);
-            }
-          }
+        for (int d = 0; d < DQK / 32; ++d) {
+          const u32x2_t lo = qo.trans(q_s, rows0, 0, d);
+          const u32x2_t hi = qo.trans(q_s, rows0, 1, d);
+          dk[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, dk[d]);
         }
       }
     }
+    cC = advance(cC);
+    if (n + 1 < n_tiles) wait_for(n + 1);
+    __syncthreads();
   }
+  wait_vmem_all();
 
   // ---- write this lane's key row: dK^T / dV^T lane holds d = 32*blk + 8i + 4*half + j ----
   if (kvalid) {

@@ -94,6 +94,71 @@ __device__ inline u32x2_t tr_operand(const uint16_t* X, int ld, int row0, int co
   return lds_read_tr16(X + (row0 + (s >> 2)) * ld + col0 + 16 * (g & 1) + 4 * (s & 3));
 }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4):
+// lane l's bytes land at LDS byte address lds + 16*l (lds is wave-uniform).
+// Issued through inline assembly so that the compiler does not make LDS reads
+// of the other buffer wait for this load; completion is awaited explicitly
+// (s_waitcnt vmcnt(0) + barrier) before the destination buffer is read.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(0) through the builtin, so that the compiler's own wait
+// bookkeeping knows every vector memory load has completed here (encoding:
+// vmcnt 0, expcnt 7, lgkmcnt 15).
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 4 bytes per lane from global memory into LDS (global_load_lds_dword): lane l's
+// word lands at LDS byte address lds + 4*l.
+__device__ __forceinline__ void dma4(const void* src, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 63].
+__device__ __forceinline__ void wait_vmem_le(int n) {
+  switch (n) {
+#define CVA_WAIT_CASE(k) \
+  case k:                \
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (k & 15) | ((k >> 4) << 14)); \
+    break;
+    CVA_WAIT_CASE(0) CVA_WAIT_CASE(1) CVA_WAIT_CASE(2) CVA_WAIT_CASE(3) CVA_WAIT_CASE(4)
+    CVA_WAIT_CASE(5) CVA_WAIT_CASE(6) CVA_WAIT_CASE(7) CVA_WAIT_CASE(8) CVA_WAIT_CASE(9)
+    CVA_WAIT_CASE(10) CVA_WAIT_CASE(11) CVA_WAIT_CASE(12) CVA_WAIT_CASE(13) CVA_WAIT_CASE(14)
+    CVA_WAIT_CASE(15) CVA_WAIT_CASE(16) CVA_WAIT_CASE(17) CVA_WAIT_CASE(18) CVA_WAIT_CASE(19)
+    CVA_WAIT_CASE(20) CVA_WAIT_CASE(21) CVA_WAIT_CASE(22) CVA_WAIT_CASE(23) CVA_WAIT_CASE(24)
+    CVA_WAIT_CASE(25) CVA_WAIT_CASE(26) CVA_WAIT_CASE(27) CVA_WAIT_CASE(28) CVA_WAIT_CASE(29)
+    CVA_WAIT_CASE(30) CVA_WAIT_CASE(31) CVA_WAIT_CASE(32) CVA_WAIT_CASE(33) CVA_WAIT_CASE(34)
+    CVA_WAIT_CASE(35) CVA_WAIT_CASE(36) CVA_WAIT_CASE(37) CVA_WAIT_CASE(38) CVA_WAIT_CASE(39)
+    CVA_WAIT_CASE(40)
+#undef CVA_WAIT_CASE
+    default:
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      break;
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
 __device__ inline f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
