@@ -111,6 +111,7 @@ constexpr int32_t kWavesPerFwdTile = 8;  // forward: two groups of 4 waves (ping
 constexpr int32_t kWavesPerDqTile = 4;
 constexpr int32_t kFwdMaxSpans = 8;   // forward kernel keeps a work item's spans in LDS
 constexpr int32_t kDkvMaxSpans = 16;  // dK/dV kernel keeps a work item's spans in LDS
+constexpr int32_t kDqMaxSpans = 8;    // dQ kernel keeps a work item's spans in LDS
 constexpr int32_t kRowsPerWave = 32;
 constexpr int32_t kFwdTileKv = 64;
 constexpr int32_t kDqTileKv = 64;     // dQ kernel: keys per K/V tile (query tile as forward)

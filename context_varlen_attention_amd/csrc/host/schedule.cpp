@@ -325,6 +325,12 @@ cva_status build_schedules(Plan& p) {
     p.dq = p.fwd;  // same tile shape: the dQ kernel walks the forward schedule
   else
     build_q_schedule(p, p.dq, dq_q, kDqTileKv);
+  for (int32_t t = 0; t < p.dq.n_tiles(); ++t) {
+    if (p.dq.tiles[(size_t)t * QT_INTS + QT_NSPAN] > kDqMaxSpans) {
+      set_error("mask gives a query tile more K/V spans than the dQ kernel supports");
+      return CVA_E_UNSUPPORTED;
+    }
+  }
   build_kv_schedule(p, p.dkdv, kDkvTileQ, kDkvTileKv);
   for (int32_t t = 0; t < p.dkdv.n_tiles(); ++t) {
     if (p.dkdv.tiles[(size_t)t * KT_INTS + KT_NSPAN] > kDkvMaxSpans) {

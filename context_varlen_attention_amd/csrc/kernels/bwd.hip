@@ -407,18 +407,41 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
 }
 
 // ---------------------------------------------------------------------------
-// dQ, Q-stationary (same work-group shape and schedule form as the forward)
+// dQ, Q-stationary.  A work-group holds 32 query rows of 4/heads_per_tile row
+// blocks x heads_per_tile heads of one K/V group (one wave each; Q and dO of the
+// lane's query in registers) and walks the 64-key K/V tiles of its schedule.  K
+// and V stream through an NS-deep LDS ring by direct-to-LDS loads issued NS-1
+// tiles ahead; the prefix-index entries of each tile come through a ring of
+// their own, fetched 2NS-1 tiles ahead so that the loads never wait on them.
+// Per 32 keys:  S^T = K Q^T, dP^T = V dO^T (A = K / V rows from LDS),
+// dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T (A = transposing reads of K).
 // ---------------------------------------------------------------------------
+template <int DQK>
+constexpr int kDqStages = DQK > 128 ? 3 : 2;
+template <int DQK>
+constexpr int kDqBlocksPerCu = DQK > 128 ? 1 : 2;
+
 template <typename E, int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams P) {
-  constexpr int BN = 64;
+__global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdParams P) {
+  constexpr int BN = kDqTileKv;
   constexpr int QS = DQK / 16, VS = DV / 16;
-  constexpr int KLD = DQK + 8, VLD = DV + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[BN * VLD];
+  constexpr int NS = kDqStages<DQK>;
+  constexpr int NIR = 2 * NS;  // index ring slots
+  using KO = TileOffsets<DQK>;
+  using VO = TileOffsets<DV>;
+  constexpr int CHK = KO::RB / 16, CHV = VO::RB / 16;  // 16-byte chunks per LDS row
+  constexpr int NK = BN * CHK / kThreads, NV = BN * CHV / kThreads;
+  constexpr bool kSharedRows = CHK == CHV;
+  constexpr int NI = kSharedRows ? NK : NK + NV;
+  static_assert(BN == 64, "the index fetch covers 64 keys per tile");
+  __shared__ __attribute__((aligned(16))) char sK[NS][BN * KO::RB];
+  __shared__ __attribute__((aligned(16))) char sV[NS][BN * VO::RB];
+  __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][BN];
+  __shared__ __attribute__((aligned(16))) int32_t sSpan[kDqMaxSpans * 4];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, half = lane >> 5;
 
   const int tile = blockIdx.x / P.dq_head_groups;
@@ -434,10 +457,12 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams P) {
   const bool valid = a < q_len;
   const int row = q_row0 + a;
 
-  const uint16_t* __restrict__ kg = (const uint16_t*)P.k;
-  const uint16_t* __restrict__ vg = (const uint16_t*)P.v;
+  const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
+  const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
+  const uint32_t kstride = (uint32_t)P.hkv * DQK * 2, vstride = (uint32_t)P.hkv * DV * 2;
   const int32_t* __restrict__ kvi = P.t.kv_index + kv_off;
 
+  // Q^T and dO^T operands in registers: lane holds row[16s + 8*half .. +7]
   typename E::vec8 qf[QS], of[VS];
   {
     const uint16_t* qr = (const uint16_t*)P.q + ((int64_t)row * P.hq + head) * DQK + 8 * half;
@@ -463,81 +488,148 @@ __global__ __launch_bounds__(kThreads, 1) void dq_kernel(BwdParams P) {
     lse2 = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
     delta = P.delta[(int64_t)head * P.t_loc + row];
   }
+  if (tid < 4 * nspan) sSpan[tid] = P.t.dq_spans[span0 * 4 + tid];
+  wait_vmem_all();
+  __syncthreads();
+  int n_tiles = 0;
+  for (int sp = 0; sp < nspan; ++sp) {
+    const int4 r = *(const int4*)(sSpan + 4 * sp);
+    n_tiles += __builtin_amdgcn_readfirstlane(r.y) - __builtin_amdgcn_readfirstlane(r.x);
+  }
+
+  // ---- cursor over the work item's K/V tiles ----
+  struct Cur {
+    int sp, t, t_end, partial;
+  };
+  auto span_at = [&](int sp) {
+    const int4 r = *(const int4*)(sSpan + 4 * sp);
+    return Cur{sp, __builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+               __builtin_amdgcn_readfirstlane(r.z)};
+  };
+  auto advance = [&](Cur c) {
+    if (++c.t >= c.t_end && c.sp + 1 < nspan) c = span_at(c.sp + 1);
+    return c;
+  };
+
+  // ---- streaming.  batch(m): K and V of tile m into ring slot m % NS (all waves)
+  // and, by wave 0, the prefix-index entries of tile m + NIR - 1 (clamped to a
+  // valid address when that tile does not exist: the slot is then never read).
+  Cur cF = nspan > 0 ? span_at(0) : Cur{0, 0, 0, 0};  // next tile whose indices get fetched
+  int next_f = 0;
+  auto fetch_idx = [&]() {
+    const int kb0 = next_f < n_tiles ? cF.t * BN : 0;
+    dma4(kvi + min(kb0 + lane, kv_len - 1), lds_addr(sIdx[next_f % NIR]));
+    if (next_f < n_tiles) cF = advance(cF);
+    ++next_f;
+  };
+  const int per_batch = NK + NV + (wave == 0 ? 1 : 0);  // loads per wave and batch
+  auto issue = [&](int m) {
+    const int32_t* si = sIdx[m % NIR];
+    int idx[NI];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) idx[i] = si[(i * kThreads + tid) / CHK];
+    if constexpr (!kSharedRows) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) idx[NK + i] = si[(i * kThreads + tid) / CHV];
+    }
+    const uint32_t kl = lds_addr(sK[m % NS]) + (uint32_t)wave * 64 * 16;
+    const uint32_t vl = lds_addr(sV[m % NS]) + (uint32_t)wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int s = i * kThreads + tid;
+      int c = (s % CHK) ^ bwd_swz<KO::RB>(s / CHK);
+      if (c >= DQK / 8) c = 0;  // row padding: any in-bounds source
+      dma16(kg + ((uint64_t)(uint32_t)idx[i] * kstride + c * 16), kl + i * kThreads * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int s = i * kThreads + tid;
+      int c = (s % CHV) ^ bwd_swz<VO::RB>(s / CHV);
+      if (c >= DV / 8) c = 0;
+      const int id = kSharedRows ? idx[i] : idx[NK + i];
+      dma16(vg + ((uint64_t)(uint32_t)id * vstride + c * 16), vl + i * kThreads * 16);
+    }
+    if (wave == 0) fetch_idx();
+  };
+  // wait until tile m's batch has landed; the batches issued after it (tiles
+  // m+1 .. m+NS-2, those that exist) may stay in flight
+  auto wait_for = [&](int m) {
+    const int later = min(m + NS - 1, n_tiles) - (m + 1);
+    wait_vmem_le(later > 0 ? later * per_batch : 0);
+  };
+
+  KO ko;
+  VO vo;
+  ko.init(lane);
+  vo.init(lane);
 
   f32x16_t acc[DQK / 32];
 #pragma unroll
   for (int d = 0; d < DQK / 32; ++d) acc[d] = zero16();
   const float sl2 = P.scale_log2;
 
-  for (int sp = 0; sp < nspan; ++sp) {
-    const int32_t* spr = P.t.dq_spans + (span0 + sp) * 4;
-    const int t_begin = spr[0], t_end = spr[1];
-    const bool partial = spr[2] != 0;
-    for (int t = t_begin; t < t_end; ++t) {
-      const int kb0 = t * BN;
-      __syncthreads();
-      {
-        constexpr int CK = DQK / 8;
-        for (int idx = tid; idx < BN * CK; idx += kThreads) {
-          const int r = idx / CK, c = idx % CK;
-          const int b = kb0 + r;
-          u32x4_t x = {0u, 0u, 0u, 0u};
-          if (b < kv_len) x = *(const u32x4_t*)(kg + ((int64_t)kvi[b] * P.hkv + kvh) * DQK + c * 8);
-          *(u32x4_t*)(sK + r * KLD + c * 8) = x;
+  if (n_tiles > 0) {
+    if (wave == 0)
+      for (int m = 0; m < NIR - 1; ++m) fetch_idx();
+    wait_vmem_all();
+    __syncthreads();
+    for (int m = 0; m < NS - 1 && m < n_tiles; ++m) {
+      issue(m);
+      __syncthreads();  // batch m+1 overwrites the index slot batch m has just read
+    }
+    wait_for(0);
+    __syncthreads();
+  }
+  Cur cC = nspan > 0 ? span_at(0) : Cur{0, 0, 0, 0};  // tile being computed
+  for (int n = 0; n < n_tiles; ++n) {
+    if (n + NS - 1 < n_tiles) issue(n + NS - 1);  // into the slot tile n-1 used
+    const char* k_s = sK[n % NS];
+    const char* v_s = sV[n % NS];
+    const int kb0 = cC.t * BN;
+    const bool partial = cC.partial != 0;
+#pragma unroll
+    for (int nb = 0; nb < BN / 32; ++nb) {
+      f32x16_t s = zero16(), dp = zero16();
+#pragma unroll
+      for (int st = 0; st < QS; ++st) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
+#pragma unroll
+      for (int st = 0; st < VS; ++st) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
+      // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
+      uint32_t pd[2][4];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        float dsv[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float x = fmaf(s[r + u], sl2, -lse2);
+          if (partial) {
+            const int b = kb0 + nb * 32 + 8 * ((r + u) >> 2) + 4 * half + ((r + u) & 3);
+            const bool vis = ((b >= lo1) & (b < hi1)) | ((b >= lo2) & (b < hi2));
+            x = vis ? x : -INFINITY;
+          }
+          const float p = __builtin_amdgcn_exp2f(x);
+          dsv[u] = p * (dp[r + u] - delta);
         }
-        constexpr int CV = DV / 8;
-        for (int idx = tid; idx < BN * CV; idx += kThreads) {
-          const int r = idx / CV, c = idx % CV;
-          const int b = kb0 + r;
-          u32x4_t x = {0u, 0u, 0u, 0u};
-          if (b < kv_len) x = *(const u32x4_t*)(vg + ((int64_t)kvi[b] * P.hkv + kvh) * DV + c * 8);
-          *(u32x4_t*)(sV + r * VLD + c * 8) = x;
-        }
+        pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
       }
-      __syncthreads();
+      // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
 #pragma unroll
-      for (int nb = 0; nb < BN / 32; ++nb) {
-        f32x16_t s = zero16(), dp = zero16();
-        const uint16_t* kr = sK + (nb * 32 + col) * KLD + 8 * half;
+      for (int st = 0; st < 2; ++st) {
+        const int rows0 = nb * 32 + st * 16;
+        const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
 #pragma unroll
-        for (int st = 0; st < QS; ++st)
-          s = E::mfma32(as_vec8<E>(*(const u32x4_t*)(kr + 16 * st)), qf[st], s);
-        const uint16_t* vr = sV + (nb * 32 + col) * VLD + 8 * half;
-#pragma unroll
-        for (int st = 0; st < VS; ++st)
-          dp = E::mfma32(as_vec8<E>(*(const u32x4_t*)(vr + 16 * st)), of[st], dp);
-        uint32_t pd[2][4];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          float dsv[2];
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            float x = s[r + u] * sl2 - lse2;
-            if (partial) {
-              const int b = kb0 + nb * 32 + 8 * ((r + u) >> 2) + 4 * half + ((r + u) & 3);
-              const bool vis = (b >= lo1 && b < hi1) || (b >= lo2 && b < hi2);
-              x = vis ? x : -INFINITY;
-            }
-            const float p = __builtin_amdgcn_exp2f(x);
-            dsv[u] = p * (dp[r + u] - delta);
-          }
-          pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
-        }
-        // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int kb = nb * 32 + st * 16 + 4 * half;
-          const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
-#pragma unroll
-          for (int d = 0; d < DQK / 32; ++d) {
-            const u32x2_t lo = tr_operand(sK, KLD, kb, d * 32, lane);
-            const u32x2_t hi = tr_operand(sK, KLD, kb + 8, d * 32, lane);
-            acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
-          }
+        for (int d = 0; d < DQK / 32; ++d) {
+          const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
+          const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
+          acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
         }
       }
     }
+    cC = advance(cC);
+    if (n + 1 < n_tiles) wait_for(n + 1);
+    __syncthreads();
   }
+  wait_vmem_all();
 
   if (valid) {
     uint16_t* dqr = (uint16_t*)P.dq + ((int64_t)row * P.hq + head) * DQK;
