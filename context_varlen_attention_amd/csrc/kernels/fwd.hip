@@ -21,11 +21,14 @@
 // with the transposing LDS read ds_read_b64_tr_b16.
 //
 // Per K/V tile the vector ALU does only what the softmax needs:
-//   * Q is pre-multiplied by scale*log2(e) when it is loaded, and the S^T
-//     accumulators start at -base (the row's exponent base), so P = exp2(acc)
-//     with no extra arithmetic;
-//   * the row maximum uses v_max3, the base moves only when the maximum grows
-//     by more than 2^8 (lazy rescaling), so the O rescale is rare;
+//   * Q is pre-multiplied by scale*log2(e) when it is loaded, and the first
+//     MFMA of every S^T chain takes a register block holding -base (the row's
+//     exponent base) as its accumulator input, so P = exp2(acc) with no extra
+//     arithmetic and no per-tile initialisation;
+//   * P = exp2(acc) is formed at once; the row maximum (v_max3) is computed and
+//     the base moved only when some P of the tile may exceed 2^8 (the sum of a
+//     lane's P values exceeds 2^8) or the row has no base yet (lazy rescaling),
+//     so both the maximum and the O rescale are rare;
 //   * P is packed to 16 bits with v_cvt_pk and the row sum is accumulated from
 //     the packed values with v_dot2 (the sum of exactly the values the PV MFMA
 //     consumes);
@@ -46,6 +49,8 @@ namespace {
 constexpr int kThreads = 512;              // 8 waves: two ping-pong groups of 4
 constexpr int kBN = 64;                    // keys per K/V tile
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: the base may lag the row max by 2^8
+constexpr float kRescaleLimit = 256.0f;    // 2^kRescaleThreshold
+constexpr int kReadAhead = 6;              // MFMAs between an LDS operand read and its use
 
 // LDS layouts (16-byte chunks, XOR-swizzled so that the MFMA operand reads are
 // bank-conflict free on gfx950's 64 x 4-byte-bank LDS, as measured with the
@@ -244,23 +249,22 @@ struct SoftmaxState {
   f32x16_t acc[DB];
 };
 
-// S^T = K (scaled Q)^T - base for the 64 keys of a tile (two 32-key blocks).
-template <typename E, int DQK, bool kInit = true>
+// S^T = K (scaled Q)^T - base for the 64 keys of a tile (two 32-key blocks); the
+// first MFMA of each chain takes its accumulator input from nbase (-base in every
+// entry), so the scores never need initialising.
+// (kFromBase = false: the chains start from s, which holds -base already.)
+template <typename E, int DQK, bool kFromBase>
 __device__ __forceinline__ void tile_scores(f32x16_t (&s)[2], const typename E::vec8 (&qf)[DQK / 16],
                                             const uint16_t* sk, const uint32_t (&koff)[kKoff<DQK>],
-                                            float init) {
+                                            const f32x16_t& nbase) {
   constexpr int KSTEPS = DQK / 16;
   constexpr int KO = kKoff<DQK>;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    if constexpr (kInit) {
+  for (int kt = 0; kt < KSTEPS; ++kt) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[nb][r] = init;
-    }
-#pragma unroll
-    for (int kt = 0; kt < KSTEPS; ++kt) {
+    for (int nb = 0; nb < 2; ++nb) {
       const u32x4_t x = lds_read128(sk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
-      s[nb] = E::mfma32(as_vec8<E>(x), qf[kt], s[nb]);
+      s[nb] = E::mfma32(as_vec8<E>(x), qf[kt], (kFromBase && kt == 0) ? nbase : s[nb]);
     }
   }
 }
@@ -505,34 +509,28 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         }
       }
   };
-  auto scores = [&](int n) {  // S(n) from K ring slot n % NS; s holds -base already
-    tile_scores<E, DQK, false>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, 0.f);
+  // -base in every entry: the accumulator input of each score chain (for the
+  // widest Q/K head dimension the registers are short, and the chains start from
+  // scores initialised in the vector step instead)
+  constexpr bool kFromBase = DQK <= 128;
+  f32x16_t nbase;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nbase[r] = 0.f;
+  auto scores = [&](int n) {  // S(n) - base from K ring slot n % NS
+    tile_scores<E, DQK, kFromBase>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, nbase);
   };
-  auto init_scores = [&]() {  // next tile's accumulators start at -base
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
-  };
-  auto softmax = [&](const TileCursor& c) {
-    if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
-    const float mx = tile_max(s);
-    // a row with nothing accumulated yet (l == 0) takes its first finite max as base
-    const bool grow = (mx > kRescaleThreshold) | ((st.l == 0.f) & (mx > -INFINITY));
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-      const float shift = grow ? mx : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-shift);
-      st.base += shift;
-      st.l *= alpha;
-#pragma unroll
-      for (int d = 0; d < DB; ++d)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) st.acc[d][r] *= alpha;
+  auto init_scores = [&]() {
+    if constexpr (!kFromBase) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][r] -= shift;
+        for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
     }
+  };
+  // P = exp2(S - base) straight away; the row maximum is only computed (and the
+  // base moved) when some P exceeds 2^threshold, or on a valid row's first tile.
+  auto exp_pack = [&](float& lt) {
+    lt = 0.f;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -541,8 +539,38 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         for (int j = 0; j < 4; ++j) {
           const int r = 8 * ks + 2 * j;
           pk[nb][ks][j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
-          st.l = dot2_acc<E>(pk[nb][ks][j], st.l);
+          lt = dot2_acc<E>(pk[nb][ks][j], lt);
         }
+  };
+  auto softmax = [&](const TileCursor& c) {
+    if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
+    float lt;
+    exp_pack(lt);
+    // this lane's 32 values sum beyond 2^threshold iff one P may be too large for
+    // the 16-bit P operand; a valid row with nothing accumulated has no base yet
+    const bool slow = valid & ((lt > kRescaleLimit) | (st.l == 0.f));
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+      // both half-waves of a query column take the same decision: combined max and sum
+      const float mx = tile_max(s);
+      const bool empty = wave_half_sum(st.l) == 0.f;
+      const bool grow = (mx > 0.f) | (empty & (mx > -INFINITY));
+      const float shift = grow ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      st.base += shift;
+      st.l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nbase[r] = -st.base;  // (unused when !kFromBase)
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[d][r] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][r] -= shift;
+      exp_pack(lt);
+    }
+    st.l += lt;
   };
 
   // Group 0 streams the tiles: it issues batch n at the start of its MFMA step
@@ -570,6 +598,24 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     if (grp == 0) issue_batch(n);
     pv(n);
     scores(n + 1);
+    {
+      // operand reads run kReadAhead MFMAs ahead of their MFMA (the compiler
+      // would otherwise issue each read just before its use and stall on it)
+      constexpr int PVM = 4 * DB, SM = 2 * KSTEPS, AHEAD = DQK > 128 ? 2 : kReadAhead;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+      for (int i = 0; i < PVM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        const int next = i + AHEAD;
+        if (next < PVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        else if (next - PVM < SM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < SM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (PVM + i + AHEAD < PVM + SM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
     __syncthreads();
     softmax(cY);
     cY = next_tile(cY, sSpan, nspan);
