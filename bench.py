@@ -114,6 +114,7 @@ KERNEL_SOURCES = {
     "fwd": ["kernels/fwd.hip"],
     "bwd_pre": ["kernels/bwd.hip"], "bwd_zero": ["kernels/bwd.hip"],
     "bwd_dkdv": ["kernels/bwd.hip"], "bwd_dq": ["kernels/bwd.hip"],
+    "fwd_merge": ["kernels/fwd.hip"],
 }
 COMMON_SOURCES = ["kernels/common.hpp", "kernels/launch.hpp", "host/plan.hpp", "host/schedule.cpp"]
 
@@ -215,6 +216,8 @@ def main():
     ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix"])
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
     ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
+    ap.add_argument("--split", action="store_true",
+                    help="forward with split K/V ranges (cva_fwd_split) instead of cva_fwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -255,12 +258,15 @@ def main():
     pairs = ref_plan.visible_pairs()
     ws = torch.empty(max(int(cva.load_library().cva_bwd_workspace_bytes(ref_plan.handle)), 4),
                      dtype=torch.uint8, device=dev)
+    fwd_ws = None
+    if args.split and ref_plan.fwd_workspace_bytes() > 0:
+        fwd_ws = torch.empty(ref_plan.fwd_workspace_bytes(), dtype=torch.uint8, device=dev)
     fwd_only = args.fwd_only or w.dtype == "fp32"
     log(f"workload {w.name}: T={T} T_loc={T_loc} seqs={len(w.lengths)} pairs/head={pairs} "
         f"fwd_only={fwd_only}")
 
     def step(plan):
-        cva.fwd(plan, q, k, v, out=o, lse=lse)
+        cva.fwd(plan, q, k, v, out=o, lse=lse, workspace=fwd_ws)
         if not fwd_only:
             cva.bwd(plan, q, k, v, o, lse, do, dq=dq, dk_rm=dk, dv_rm=dv, workspace=ws)
 
@@ -315,7 +321,7 @@ def main():
                 "peak": d.get("peak"), "unit": d.get("unit"), "frac": d.get("frac"),
                 "traffic": measured_traffic(dom, w.name),
                 "per_launch": (f"{kfl[dom]:.4e} flop" if dom in kfl else f"{kby.get(dom, 0)} B")}
-    fwd_ms = kernels.get("fwd", {}).get("ms_per_step")
+    fwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("fwd")) or None
     bwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("bwd"))
     out = {
         "metric": METRIC,
@@ -333,7 +339,8 @@ def main():
         "config": {"workload": w.name, "description": DESCRIPTIONS[w.name], "tokens": T,
                    "sub_sequences": int(len(w.lengths)), "cp_size": w.cp_size, "rank": w.rank,
                    "hq": w.hq, "hkv": w.hkv, "d_qk": w.d_qk, "d_v": w.d_v, "mask": w.mask,
-                   "step": "plan (look-ahead) + upload + fwd" + ("" if fwd_only else " + bwd")},
+                   "step": "plan (look-ahead) + upload + fwd" + ("" if fwd_only else " + bwd"),
+                   "fwd_split": fwd_ws is not None},
         "pct_of_peak": 100.0 * value / peak,
         "useful_tflop_per_step": (fl_fwd + fl_bwd) / 1e12,
         "fwd_tflops": fl_fwd / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,

@@ -77,14 +77,15 @@ class _Schedule(ctypes.Structure):
 
 
 EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_get_metadata",
-           "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_bwd_workspace_bytes",
+           "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_fwd_workspace_bytes",
+           "cva_fwd_split", "cva_bwd_workspace_bytes",
            "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read"]
 
-KERNEL_NAMES = ["fwd", "bwd_pre", "bwd_zero", "bwd_dkdv", "bwd_dq"]
+KERNEL_NAMES = ["fwd", "bwd_pre", "bwd_zero", "bwd_dkdv", "bwd_dq", "fwd_merge"]
 
 
 class _KernelTimes(ctypes.Structure):
-    _fields_ = [("launches", ctypes.c_int64 * 5), ("total_ms", ctypes.c_double * 5)]
+    _fields_ = [("launches", ctypes.c_int64 * 6), ("total_ms", ctypes.c_double * 6)]
 
 
 def library_path() -> str:
@@ -116,6 +117,10 @@ def load_library():
     L.cva_plan_upload.argtypes = [vp, vp, sz, vp]
     L.cva_fwd.restype = i32
     L.cva_fwd.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp]
+    L.cva_fwd_workspace_bytes.restype = sz
+    L.cva_fwd_workspace_bytes.argtypes = [vp]
+    L.cva_fwd_split.restype = i32
+    L.cva_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
     L.cva_bwd_workspace_bytes.restype = sz
     L.cva_bwd_workspace_bytes.argtypes = [vp]
     L.cva_bwd.restype = i32
@@ -217,12 +222,17 @@ class Plan:
         return self._cu.astype(np.int64)
 
     def schedule(self, which):
-        """(tile_q, tile_kv, tiles [n,5], spans [m,4]) of schedule 0 fwd, 1 dQ, 2 dK/dV."""
+        """(tile_q, tile_kv, tiles [n,5], spans [m,4]) of schedule 0 fwd, 1 dQ, 2 dK/dV,
+        3 forward with split K/V ranges."""
         s = _Schedule()
         _check(load_library().cva_plan_get_schedule(self._h, int(which), ctypes.byref(s)))
         tiles = _arr(s.tiles, s.n_tiles * 5, np.int64).reshape(-1, 5)
         spans = _arr(s.spans, s.n_spans * 4, np.int64).reshape(-1, 4)
         return s.tile_q, s.tile_kv, tiles, spans
+
+    def fwd_workspace_bytes(self):
+        """Bytes of the workspace ``cva_fwd_split`` needs (0: the plan splits nothing)."""
+        return int(load_library().cva_fwd_workspace_bytes(self._h))
 
     def device_bytes(self):
         return int(load_library().cva_plan_device_bytes(self._h))
@@ -279,8 +289,14 @@ def _scale(plan, softmax_scale):
     return float(softmax_scale)
 
 
-def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, stream=None):
-    """``cva_fwd``: returns (o [T_loc, Hq, Dv], lse [Hq, T_loc] float32)."""
+def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, stream=None,
+        workspace=None):
+    """``cva_fwd``: returns (o [T_loc, Hq, Dv], lse [Hq, T_loc] float32).
+
+    With ``workspace`` (a device uint8 tensor of at least
+    ``plan.fwd_workspace_bytes()`` bytes, or ``True`` to allocate one) this calls
+    ``cva_fwd_split`` instead: the long K/V ranges are split and merged.
+    """
     import torch
     if not plan.uploaded:
         plan.upload(q.device)
@@ -297,9 +313,18 @@ def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, strea
         lse = torch.empty((plan.hq, Tl), dtype=torch.float32, device=dev)
     _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
     vp = ctypes.c_void_p
-    _check(load_library().cva_fwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()),
-                                  vp(v_rm.data_ptr()), vp(out.data_ptr()), vp(lse.data_ptr()),
-                                  _scale(plan, softmax_scale), _stream_ptr(stream, dev)))
+    L = load_library()
+    if workspace is None:
+        _check(L.cva_fwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
+                         vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
+                         _stream_ptr(stream, dev)))
+        return out, lse
+    if workspace is True:
+        workspace = torch.empty(max(plan.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    _check(L.cva_fwd_split(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
+                           vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
+                           vp(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+                           _stream_ptr(stream, dev)))
     return out, lse
 
 

@@ -7,6 +7,7 @@
 // enqueues nothing (MindSpeed RFC section 3.4: validate before any operator
 // call).
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <new>
 #include <sstream>
@@ -46,6 +47,8 @@ cva::PlanTables tables(const Plan& p) {
   t.kv_tiles = b + L.kv_tiles;
   t.kv_spans = b + L.kv_spans;
   t.zero_rows = b + L.zero_rows;
+  t.fwds_slot = b + L.fwds_slot;
+  t.fwds_combine = b + L.fwds_combine;
   return t;
 }
 
@@ -209,14 +212,35 @@ cva_status cva_plan_upload(cva_plan* plan, void* dev_buf, size_t bytes, void* st
   return CVA_OK;
 }
 
-cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
-                   void* o, float* lse, float softmax_scale, void* stream) {
-  const Plan* p = reinterpret_cast<const Plan*>(plan);
+namespace {
+
+bool splits(const Plan& p) { return p.n_split_slots > 0 && p.dtype != CVA_FP32; }
+
+size_t split_bytes(const Plan& p) {
+  if (!splits(p)) return 0;
+  const size_t rows = (size_t)p.n_split_slots * p.hq * p.fwds.tile_q;  // (slot, head, row)
+  const size_t o_bytes = (rows * p.d_v * sizeof(float) + 255) / 256 * 256;
+  return o_bytes + rows * sizeof(float);
+}
+
+cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v_rm, void* o,
+                   float* lse, float softmax_scale, void* workspace, size_t ws_bytes,
+                   bool split, void* stream) {
   cva_status st = check_ready(p);
   if (st != CVA_OK) return st;
   if (q == nullptr || k_rm == nullptr || v_rm == nullptr || o == nullptr || lse == nullptr)
     return fail(CVA_E_ARG, "a tensor pointer is NULL");
   if ((st = check_scale(softmax_scale)) != CVA_OK) return st;
+  split = split && splits(*p);
+  if (split) {
+    const size_t need = split_bytes(*p);
+    if (workspace == nullptr || ws_bytes < need) {
+      std::ostringstream os;
+      os << "forward workspace needs " << need << " bytes";
+      return fail(CVA_E_WORKSPACE, os.str());
+    }
+    if (((uintptr_t)workspace & 255) != 0) return fail(CVA_E_WORKSPACE, "forward workspace must be 256-byte aligned");
+  }
   cva::FwdParams fp;
   fp.q = q;
   fp.k = k_rm;
@@ -234,9 +258,46 @@ cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   fp.tile_q = p->fwd.tile_q;
   fp.tile_kv = p->fwd.tile_kv;
   fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  fp.slot = nullptr;
+  fp.ws_o = nullptr;
+  fp.ws_lse = nullptr;
+  fp.combine = nullptr;
+  fp.n_combine = 0;
+  if (split) {
+    const int32_t* b = (const int32_t*)p->dev;
+    fp.t.fwd_tiles = b + p->layout.fwds_tiles;
+    fp.t.fwd_spans = b + p->layout.fwds_spans;
+    fp.n_tiles = p->fwds.n_tiles();
+    fp.slot = fp.t.fwds_slot;
+    fp.combine = fp.t.fwds_combine;
+    fp.n_combine = (int32_t)(p->fwds_combine.size() / cva::CB_INTS);
+    const size_t rows = (size_t)p->n_split_slots * p->hq * p->fwds.tile_q;
+    fp.ws_o = (float*)workspace;
+    fp.ws_lse = (float*)((char*)workspace + (rows * p->d_v * sizeof(float) + 255) / 256 * 256);
+  }
   hipError_t e = cva::launch_fwd(p->dtype, p->d_qk, p->d_v, fp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return CVA_OK;
+}
+
+}  // namespace
+
+cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                   void* o, float* lse, float softmax_scale, void* stream) {
+  return run_fwd(reinterpret_cast<const Plan*>(plan), q, k_rm, v_rm, o, lse, softmax_scale,
+                 nullptr, 0, false, stream);
+}
+
+size_t cva_fwd_workspace_bytes(const cva_plan* plan) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  return p == nullptr ? 0 : split_bytes(*p);
+}
+
+cva_status cva_fwd_split(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                         void* o, float* lse, float softmax_scale, void* workspace,
+                         size_t ws_bytes, void* stream) {
+  return run_fwd(reinterpret_cast<const Plan*>(plan), q, k_rm, v_rm, o, lse, softmax_scale,
+                 workspace, ws_bytes, true, stream);
 }
 
 size_t cva_bwd_workspace_bytes(const cva_plan* plan) {
@@ -295,8 +356,12 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
 cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out) {
   const Plan* p = reinterpret_cast<const Plan*>(plan);
   if (p == nullptr || out == nullptr) return fail(CVA_E_ARG, "plan or out is NULL");
-  const cva::Schedule* s = which == 0 ? &p->fwd : which == 1 ? &p->dq : which == 2 ? &p->dkdv : nullptr;
-  if (s == nullptr) return fail(CVA_E_ARG, "which must be 0, 1 or 2");
+  const cva::Schedule* s = which == 0   ? &p->fwd
+                           : which == 1 ? &p->dq
+                           : which == 2 ? &p->dkdv
+                           : which == 3 ? &p->fwds
+                                        : nullptr;
+  if (s == nullptr) return fail(CVA_E_ARG, "which must be 0, 1, 2 or 3");
   out->tile_q = s->tile_q;
   out->tile_kv = s->tile_kv;
   out->n_tiles = s->n_tiles();

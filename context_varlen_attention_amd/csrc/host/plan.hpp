@@ -49,8 +49,13 @@ struct BlobLayout {
   int64_t dq_tiles = 0, dq_spans = 0;
   int64_t kv_tiles = 0, kv_spans = 0;
   int64_t zero_rows = 0;
+  int64_t fwds_tiles = 0, fwds_spans = 0, fwds_slot = 0, fwds_combine = 0;
   int64_t total = 0;
 };
+
+// Combine record of a Q tile whose K/V range was split over several forward
+// work items: {segment, first query, rows, first partial slot, pieces}.
+enum CombineField { CB_SEG = 0, CB_Q0 = 1, CB_ROWS = 2, CB_SLOT0 = 3, CB_NPIECE = 4, CB_INTS = 5 };
 
 struct Plan {
   // request
@@ -71,6 +76,14 @@ struct Plan {
   // kernel configuration + schedules
   int32_t fwd_heads_per_tile = 1;  // query heads of one K/V group sharing a forward work-group
   Schedule fwd, dq, dkdv;
+  // Forward with split K/V ranges: the forward schedule with every Q tile that
+  // walks more than fwd_split_cap K/V tiles cut into pieces, each writing an
+  // fp32 partial result to a slot of the forward workspace, merged by LSE.
+  Schedule fwds;
+  std::vector<int32_t> fwds_slot;     // [n items]: partial slot, or -1 (writes o/lse directly)
+  std::vector<int32_t> fwds_combine;  // [m][CB_INTS]
+  int32_t n_split_slots = 0;
+  int32_t fwd_split_cap = 0;
   std::vector<int32_t> zero_rows;  // [m][2] rank-major row ranges no local query sees
 
   // device copy
@@ -96,6 +109,7 @@ cva_status build_metadata(Plan& p);
 void row_intervals(const Plan& p, int seg, int32_t a, int32_t iv[4]);
 cva_status build_schedules(Plan& p);
 void build_blob(Plan& p);
+void build_fwd_split(Plan& p);
 
 // Tile shape of the forward kernel for a plan's head shape.
 struct FwdShape {
@@ -117,5 +131,8 @@ constexpr int32_t kFwdTileKv = 64;
 constexpr int32_t kDqTileKv = 64;     // dQ kernel: keys per K/V tile (query tile as forward)
 constexpr int32_t kDkvTileQ = 64;     // dK/dV kernel: queries per Q tile
 constexpr int32_t kDkvTileKv = 128;   // dK/dV kernel: keys per work-group (4 waves x 32)
+constexpr int32_t kSplitCUs = 256;        // compute units the split balances over (MI355X)
+constexpr int32_t kSplitMinSteps = 8;     // never cut a piece shorter than this many K/V tiles
+constexpr int32_t kSplitMaxPieces = 8;    // pieces per Q tile (merge keeps their weights in registers)
 
 }  // namespace cva

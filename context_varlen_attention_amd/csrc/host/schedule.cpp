@@ -339,6 +339,8 @@ cva_status build_schedules(Plan& p) {
     }
   }
 
+  build_fwd_split(p);
+
   // rank-major rows outside every prefix are zero in dK/dV
   std::vector<char> covered((size_t)p.T, 0);
   for (int32_t x : p.kv_index) covered[x] = 1;
@@ -358,19 +360,101 @@ void build_blob(Plan& p) {
   BlobLayout& L = p.layout;
   const std::vector<int32_t>* parts[] = {&p.segs, &p.kv_index, &p.row_iv, &p.fwd.tiles, &p.fwd.spans,
                                          &p.dq.tiles, &p.dq.spans, &p.dkdv.tiles, &p.dkdv.spans,
-                                         &p.zero_rows};
+                                         &p.zero_rows, &p.fwds.tiles, &p.fwds.spans, &p.fwds_slot,
+                                         &p.fwds_combine};
   int64_t* offs[] = {&L.segs, &L.kv_index, &L.row_iv, &L.fwd_tiles, &L.fwd_spans,
-                     &L.dq_tiles, &L.dq_spans, &L.kv_tiles, &L.kv_spans, &L.zero_rows};
+                     &L.dq_tiles, &L.dq_spans, &L.kv_tiles, &L.kv_spans, &L.zero_rows,
+                     &L.fwds_tiles, &L.fwds_spans, &L.fwds_slot, &L.fwds_combine};
+  constexpr int kParts = (int)(sizeof(parts) / sizeof(parts[0]));
   int64_t total = 0;
-  for (int k = 0; k < 10; ++k) {
+  for (int k = 0; k < kParts; ++k) {
     *offs[k] = total;
     total += ((int64_t)parts[k]->size() + 63) / 64 * 64;  // every table 256-byte aligned
   }
   L.total = total;
   p.blob.assign((size_t)total, 0);
-  for (int k = 0; k < 10; ++k)
+  for (int k = 0; k < kParts; ++k)
     if (!parts[k]->empty())
       std::memcpy(p.blob.data() + *offs[k], parts[k]->data(), parts[k]->size() * sizeof(int32_t));
+}
+
+
+// Forward schedule with split K/V ranges (DCP paper, background: the block-wise
+// computation of one query block can be cut along the K/V dimension and the
+// partial outputs merged through their log-sum-exp).  The forward's work items
+// run one per CU (longest first); a Q tile whose K/V walk is longer than the
+// average work per CU bounds the whole launch, so such tiles are cut into
+// pieces of at most `cap` K/V tiles (cap = that average, at least
+// kSplitMinSteps), each piece an item of its own writing an fp32 partial result
+// to its slot of the forward workspace.
+void build_fwd_split(Plan& p) {
+  p.fwds = Schedule{};
+  p.fwds.tile_q = p.fwd.tile_q;
+  p.fwds.tile_kv = p.fwd.tile_kv;
+  p.fwds_slot.clear();
+  p.fwds_combine.clear();
+  p.n_split_slots = 0;
+  const int32_t n = p.fwd.n_tiles();
+  const int32_t groups = p.hq / p.fwd_heads_per_tile;
+  std::vector<int64_t> steps(n, 0);
+  int64_t total = 0;
+  for (int32_t t = 0; t < n; ++t) {
+    const int32_t* tr = &p.fwd.tiles[(size_t)t * QT_INTS];
+    for (int32_t k = 0; k < tr[QT_NSPAN]; ++k) {
+      const int32_t* sp = &p.fwd.spans[(size_t)(tr[QT_SPAN0] + k) * SPAN_INTS];
+      steps[t] += sp[1] - sp[0];
+    }
+    total += steps[t] * groups;
+  }
+  const int64_t cap = std::max<int64_t>(kSplitMinSteps, (total + kSplitCUs - 1) / kSplitCUs);
+  p.fwd_split_cap = (int32_t)cap;
+  struct Item { std::array<int32_t, QT_INTS> rec; std::vector<int32_t> spans; int32_t slot; int64_t cost; };
+  std::vector<Item> items;
+  for (int32_t t = 0; t < n; ++t) {
+    const int32_t* tr = &p.fwd.tiles[(size_t)t * QT_INTS];
+    std::vector<int32_t> sp(&p.fwd.spans[(size_t)tr[QT_SPAN0] * SPAN_INTS],
+                            &p.fwd.spans[(size_t)(tr[QT_SPAN0] + tr[QT_NSPAN]) * SPAN_INTS]);
+    const int64_t pieces = std::min<int64_t>(kSplitMaxPieces, (steps[t] + cap - 1) / cap);
+    if (pieces <= 1) {
+      items.push_back({{tr[0], tr[1], tr[2], 0, tr[QT_NSPAN]}, sp, -1, steps[t]});
+      continue;
+    }
+    p.fwds_combine.insert(p.fwds_combine.end(),
+                          {tr[QT_SEG], tr[QT_Q0], tr[QT_ROWS], p.n_split_slots, (int32_t)pieces});
+    // cut the K/V tiles of the span list into `pieces` consecutive runs of
+    // near-equal length (a span may be cut in the middle)
+    int64_t done = 0;
+    size_t k = 0;
+    int32_t pos = sp.empty() ? 0 : sp[0];  // next K/V tile of span k
+    for (int64_t i = 0; i < pieces; ++i) {
+      const int64_t want = steps[t] * (i + 1) / pieces - done;
+      Item it{{tr[0], tr[1], tr[2], 0, 0}, {}, p.n_split_slots + (int32_t)i, want};
+      int64_t got = 0;
+      while (got < want) {
+        const int32_t end = sp[k * SPAN_INTS + 1];
+        const int32_t take = (int32_t)std::min<int64_t>(end - pos, want - got);
+        it.spans.insert(it.spans.end(), {pos, pos + take, sp[k * SPAN_INTS + 2], 0});
+        ++it.rec[QT_NSPAN];
+        pos += take;
+        got += take;
+        if (pos == end && k + 1 < sp.size() / SPAN_INTS) {
+          ++k;
+          pos = sp[k * SPAN_INTS];
+        }
+      }
+      done += got;
+      items.push_back(std::move(it));
+    }
+    p.n_split_slots += (int32_t)pieces;
+  }
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+  for (Item& it : items) {
+    it.rec[QT_SPAN0] = p.fwds.n_spans();
+    p.fwds.tiles.insert(p.fwds.tiles.end(), it.rec.begin(), it.rec.end());
+    p.fwds.spans.insert(p.fwds.spans.end(), it.spans.begin(), it.spans.end());
+    p.fwds_slot.push_back(it.slot);
+    p.fwds.tile_pairs += it.cost;
+  }
 }
 
 }  // namespace cva

@@ -377,6 +377,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   const int kvh = head / P.group;
   const int rowblk = w4 / hpt + grp * (4 / hpt);
   const int a = q0 + rowblk * 32 + col;  // segment-relative query index of this lane
+  const int split_slot = P.slot != nullptr ? P.slot[tile] : -1;  // piece of a split K/V range
   const bool valid = a < q_len;
   const int row = q_row0 + a;             // local row
 
@@ -635,6 +636,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   // ---- epilogue: normalise, write O and LSE ----
   const float l_tot = wave_half_sum(st.l);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (P.slot != nullptr && split_slot >= 0) {  // one piece of a split K/V range: fp32 partials
+    if (valid) {
+      const int64_t srow =
+          ((int64_t)(split_slot * P.n_head_groups + hg) * hpt + (w4 % hpt)) * P.tile_q + (a - q0);
+      float* orow = P.ws_o + srow * DV;
+#pragma unroll
+      for (int d = 0; d < DB; ++d) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dd = d * 32 + 8 * i + 4 * half;
+          *(f32x4_t*)(orow + dd) = f32x4_t{st.acc[d][4 * i] * inv, st.acc[d][4 * i + 1] * inv,
+                                           st.acc[d][4 * i + 2] * inv, st.acc[d][4 * i + 3] * inv};
+        }
+      }
+      if (half == 0)
+        P.ws_lse[srow] = l_tot > 0.f ? (st.base + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    }
+    return;
+  }
   if (valid) {
     uint16_t* orow = (uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV;
 #pragma unroll
@@ -651,6 +671,66 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       const float lse = l_tot > 0.f ? (st.base + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
       P.lse[(int64_t)head * P.t_loc + row] = lse;
     }
+  }
+}
+
+// Merge of the pieces of split K/V ranges: for every (query row, head) of a split
+// Q tile, O = sum_p w_p O_p / sum_p w_p and LSE = m + ln(sum_p w_p) with
+// w_p = exp(LSE_p - m), m = max_p LSE_p (the log-sum-exp combination of
+// partial softmax results).  One thread per (row, head); HBM-bound and small.
+template <typename E, int DV>
+__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams P) {
+  const int item = blockIdx.x / P.n_head_groups;
+  const int hg = blockIdx.x % P.n_head_groups;
+  const int32_t* cb = P.combine + item * 5;
+  const int seg = cb[0], q0 = cb[1], slot0 = cb[3], npiece = cb[4];
+  const int32_t* sg = P.t.segs + seg * 8;
+  const int q_len = sg[2], q_row0 = sg[4];
+  const int hpt = P.heads_per_tile;
+  for (int x = threadIdx.x; x < hpt * P.tile_q; x += blockDim.x) {
+    const int hh = x / P.tile_q, r = x % P.tile_q;
+    const int a = q0 + r;
+    if (a >= q_len) continue;
+    const int head = hg * hpt + hh;
+    const int64_t row = q_row0 + a;
+    auto srow = [&](int pc) {
+      return ((int64_t)((slot0 + pc) * P.n_head_groups + hg) * hpt + hh) * P.tile_q + r;
+    };
+    float lp[kSplitMaxPieces];
+    float m = -INFINITY;
+#pragma unroll
+    for (int pc = 0; pc < kSplitMaxPieces; ++pc) {
+      lp[pc] = pc < npiece ? P.ws_lse[srow(pc)] : -INFINITY;
+      m = fmaxf(m, lp[pc]);
+    }
+    uint16_t* orow = (uint16_t*)P.o + (row * P.hq + head) * DV;
+    if (m == -INFINITY) {  // no visible key in any piece
+      for (int d = 0; d < DV; d += 8) *(u32x4_t*)(orow + d) = u32x4_t{0u, 0u, 0u, 0u};
+      P.lse[(int64_t)head * P.t_loc + row] = -INFINITY;
+      continue;
+    }
+    float w[kSplitMaxPieces];
+    float wsum = 0.f;
+#pragma unroll
+    for (int pc = 0; pc < kSplitMaxPieces; ++pc) {
+      w[pc] = pc < npiece ? expf(lp[pc] - m) : 0.f;
+      wsum += w[pc];
+    }
+    const float inv = 1.f / wsum;
+    for (int d = 0; d < DV; d += 8) {
+      f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int pc = 0; pc < kSplitMaxPieces; ++pc) {
+        if (pc < npiece) {
+          const float* src = P.ws_o + srow(pc) * DV + d;
+          lo += w[pc] * *(const f32x4_t*)src;
+          hi += w[pc] * *(const f32x4_t*)(src + 4);
+        }
+      }
+      *(u32x4_t*)(orow + d) = u32x4_t{pack2<E>(lo[0] * inv, lo[1] * inv), pack2<E>(lo[2] * inv, lo[3] * inv),
+                                      pack2<E>(hi[0] * inv, hi[1] * inv), pack2<E>(hi[2] * inv, hi[3] * inv)};
+    }
+    P.lse[(int64_t)head * P.t_loc + row] = m + logf(wsum);
   }
 }
 
@@ -713,6 +793,12 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   if (hook) hook->before(K_FWD, s);
   hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV>), dim3(grid), dim3(kThreads), 0, s, p);
   if (hook) hook->after(K_FWD, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.n_combine == 0) return e;
+  if (hook) hook->before(K_FWD_MERGE, s);
+  hipLaunchKernelGGL((fwd_merge_kernel<E, DV>), dim3((unsigned)p.n_combine * (unsigned)p.n_head_groups),
+                     dim3(256), 0, s, p);
+  if (hook) hook->after(K_FWD_MERGE, s);
   return hipGetLastError();
 }
 

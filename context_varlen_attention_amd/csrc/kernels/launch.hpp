@@ -19,6 +19,8 @@ struct PlanTables {
   const int32_t* kv_tiles;
   const int32_t* kv_spans;
   const int32_t* zero_rows;
+  const int32_t* fwds_slot;     // split forward: partial slot per item (-1: direct)
+  const int32_t* fwds_combine;  // split forward: merge records
 };
 
 struct FwdParams {
@@ -36,6 +38,12 @@ struct FwdParams {
   int32_t tile_q;
   int32_t tile_kv;
   float scale_log2;        // softmax_scale * log2(e)
+  // split forward (slot == nullptr: every item writes o/lse directly)
+  const int32_t* slot;     // [n_tiles] partial slot of each item, or -1
+  float* ws_o;             // [slots * hq * tile_q][Dv] fp32 partial outputs
+  float* ws_lse;           // [slots * hq * tile_q] partial LSE (natural log)
+  const int32_t* combine;  // [n_combine][5] merge records
+  int32_t n_combine;
 };
 
 struct BwdParams {
@@ -60,7 +68,7 @@ struct BwdParams {
 };
 
 // Optional hook around every kernel launch (timing); ids as in cva.h.
-enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_ZERO = 2, K_BWD_DKDV = 3, K_BWD_DQ = 4 };
+enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_ZERO = 2, K_BWD_DKDV = 3, K_BWD_DQ = 4, K_FWD_MERGE = 5 };
 struct LaunchHook {
   virtual void before(int kernel, hipStream_t s) = 0;
   virtual void after(int kernel, hipStream_t s) = 0;

@@ -157,6 +157,23 @@ cva_status cva_plan_upload(cva_plan* plan, void* dev_buf, size_t bytes, void* st
 cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
                    void* o, float* lse, float softmax_scale, void* stream);
 
+/* Forward with split K/V ranges (DCP paper, background: block-wise attention
+ * with online softmax; a query block's K/V range is cut into pieces whose
+ * partial outputs are merged through their log-sum-exp).  The plan cuts every
+ * forward Q tile whose K/V walk is longer than the average work per compute
+ * unit into up to 8 pieces; each piece writes an fp32 partial output and LSE
+ * to the workspace and a second kernel merges them into o and lse.  Same
+ * arguments and results as cva_fwd, plus a caller-owned device workspace of at
+ * least cva_fwd_workspace_bytes bytes (256-byte aligned) that must not be used
+ * by another call while this one may run.  When the plan cuts nothing (the
+ * workspace size is 0) or dtype is fp32, this is exactly cva_fwd and workspace
+ * may be NULL.  Errors: CVA_E_WORKSPACE if the workspace is missing or too
+ * small, otherwise as cva_fwd. */
+size_t cva_fwd_workspace_bytes(const cva_plan* plan);
+cva_status cva_fwd_split(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                         void* o, float* lse, float softmax_scale, void* workspace,
+                         size_t ws_bytes, void* stream);
+
 /* Workspace bytes cva_bwd needs (fp32 row statistics). */
 size_t cva_bwd_workspace_bytes(const cva_plan* plan);
 
@@ -172,7 +189,9 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
                     void* stream);
 
 /* Schedule introspection for tests and tools.  which: 0 forward, 1 backward dQ,
- * 2 backward dK/dV.  Returns the tile sizes and a host view of the schedule:
+ * 2 backward dK/dV, 3 forward with split K/V ranges (the items of
+ * cva_fwd_split, same record layout as 0; pieces of one Q tile share its
+ * segment and first query).  Returns the tile sizes and a host view of the schedule:
  *   forward / dQ:  q tiles {segment, first local query of the tile (segment-relative),
  *                  rows in tile, span_begin, span_count}; spans {first K/V tile,
  *                  end K/V tile, partial flag} in units of tile_kv keys.
@@ -197,9 +216,9 @@ cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedu
  * folds their elapsed times into per-kernel totals and returns the totals
  * since the last cva_timing_enable(1) (which resets them).  Kernel ids:
  *   0 forward, 1 backward Delta, 2 backward zero fill, 3 backward dK/dV,
- *   4 backward dQ.
+ *   4 backward dQ, 5 forward merge of split pieces.
  * Process-wide state; use from one thread at a time. */
-#define CVA_N_KERNELS 5
+#define CVA_N_KERNELS 6
 typedef struct {
   int64_t launches[CVA_N_KERNELS];
   double total_ms[CVA_N_KERNELS];

@@ -109,7 +109,7 @@ def _mask_rows(w, i, pos):
 
 
 @pytest.mark.parametrize("ci", range(len(MASK_CASES)))
-@pytest.mark.parametrize("which", [0, 1])
+@pytest.mark.parametrize("which", [0, 1, 3])
 def test_q_schedule_covers_exactly_nonempty_tiles(ci, which):
     lens, R, r, mask, ex = MASK_CASES[ci]
     w = _wl(lens, R, r, mask, **ex)
@@ -254,3 +254,40 @@ def test_zero_rows_complement_prefixes():
         covered[md["kv_index"]] = True
         # chunks of positions >= (2R - r) c belong to ranks < r (their second chunk)
         assert covered.sum() == sum((2 * R - r) * (cu[i + 1] - cu[i]) // (2 * R) for i in range(3))
+
+
+def _item_steps(spans, s0, ns):
+    return int(sum(b - a for a, b, _, _ in spans[s0: s0 + ns]))
+
+
+@pytest.mark.parametrize("name", ["gqa16k", "long128k", "mla32k"])
+def test_fwd_split_pieces(name):
+    """Split forward: a Q tile is cut only when it walks more K/V tiles than the
+    average per compute unit (at least 8), into at most 8 pieces of near-equal
+    length; the workspace holds one fp32 row (Dv values + LSE) per piece, head
+    and tile row."""
+    w = synth.make_workload(name)
+    plan = _plan(w)
+    tq, tk, t0, s0 = plan.schedule(0)
+    _, _, t3, s3 = plan.schedule(3)
+    hpt = 4 if (w.hq // w.hkv) % 4 == 0 else (2 if (w.hq // w.hkv) % 2 == 0 else 1)
+    steps0 = {(int(t[0]), int(t[1])): _item_steps(s0, t[3], t[4]) for t in t0}
+    total = sum(steps0.values()) * (w.hq // hpt)
+    cap = max(8, -(-total // 256))
+    pieces = {}
+    for t in t3:
+        pieces.setdefault((int(t[0]), int(t[1])), []).append(_item_steps(s3, t[3], t[4]))
+    assert pieces.keys() == steps0.keys()
+    n_slots = 0
+    for key, pc in pieces.items():
+        assert sum(pc) == steps0[key]
+        expect = min(8, -(-steps0[key] // cap))
+        assert len(pc) == expect
+        assert max(pc) - min(pc) <= 1
+        if len(pc) > 1:
+            n_slots += len(pc)
+    rows = n_slots * w.hq * tq
+    expect_bytes = 0 if n_slots == 0 else (-(-rows * w.d_v * 4 // 256)) * 256 + rows * 4
+    assert plan.fwd_workspace_bytes() == expect_bytes
+    if name == "gqa16k":
+        assert n_slots > 0  # its longest tiles exceed the per-CU average

@@ -15,14 +15,16 @@ from tests.gpu_helpers import assert_close, device_inputs, plan_for
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, q, k, v, rows=None, scale=None):
+def _run(w, q, k, v, rows=None, scale=None, split=False):
     import torch
     import context_varlen_attention_amd as cva
     print(f"[fwd] {w.name} {w.dtype} mask={w.mask} R={w.cp_size} r={w.rank} T={w.total_tokens} "
-          f"H={w.hq}/{w.hkv} D={w.d_qk}/{w.d_v}", flush=True)
+          f"H={w.hq}/{w.hkv} D={w.d_qk}/{w.d_v} split={split}", flush=True)
     plan = plan_for(w)
     dq_, dk_, dv_ = device_inputs(w, q, k, v)
-    o, lse = cva.fwd(plan, dq_, dk_, dv_, softmax_scale=scale)
+    if split:
+        assert plan.fwd_workspace_bytes() > 0, "the case was meant to split K/V ranges"
+    o, lse = cva.fwd(plan, dq_, dk_, dv_, softmax_scale=scale, workspace=True if split else None)
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()
@@ -65,6 +67,27 @@ def test_small_cases(ci, dtype):
                               branch_bounds=ex.get("bounds"), name=f"small{ci}")
     q, k, v = synth.random_tensors(w, 100 + ci, with_dout=False)
     _run(w, q, k, v)
+
+
+# cases whose forward Q tiles walk more than 8 K/V tiles: cva_fwd_split cuts them
+SPLIT = [1, 2, 3, 5]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("ci", SPLIT)
+def test_small_cases_split(ci, dtype):
+    lens, R, r, hq, hkv, dqk, dv, mask, ex = SMALL[ci]
+    w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, dtype, mask=mask,
+                              sink=ex.get("sink", 0), window=ex.get("window", 0),
+                              branch_bounds=ex.get("bounds"), name=f"small{ci}")
+    q, k, v = synth.random_tensors(w, 100 + ci, with_dout=False)
+    _run(w, q, k, v, split=True)
+
+
+def test_gqa16k_split_all_rows():
+    w = synth.make_workload("gqa16k")
+    q, k, v = synth.make_tensors(w, with_dout=False)
+    _run(w, q, k, v, split=True)
 
 
 def test_tiny_custom_scale():
