@@ -58,7 +58,7 @@ def log(msg):
 
 def make_plan(cva, w):
     return cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype,
-                    mask=w.mask, sink=w.sink, window=w.window, branch_bounds=w.branch_bounds)
+                    mask=w.mask, sink=w.sink, window=w.window, branch_bounds=w.branch_bounds, block=w.block)
 
 
 class LookAheadPlanner:
@@ -213,7 +213,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gqa16k", choices=sorted(DESCRIPTIONS))
-    ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix"])
+    ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix", "blockwise"])
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
     ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
     ap.add_argument("--split", action="store_true",

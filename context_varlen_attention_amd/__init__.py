@@ -32,7 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "libcva.so")
 _lib = None
 
 DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}
-MASKS = {"causal": 0, "lambda": 1, "shared_prefix": 2}
+MASKS = {"causal": 0, "lambda": 1, "shared_prefix": 2, "blockwise": 3}
 STATUS = {
     0: "CVA_OK", 1: "CVA_E_ARG", 2: "CVA_E_CU_SEQLENS", 3: "CVA_E_ALIGN", 4: "CVA_E_RANK",
     5: "CVA_E_HEADS", 6: "CVA_E_HEADDIM", 7: "CVA_E_DTYPE", 8: "CVA_E_MASK",
@@ -53,7 +53,8 @@ class CvaError(AssertionError):
 
 class _MaskDesc(ctypes.Structure):
     _fields_ = [("type", ctypes.c_int32), ("sink", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("n_branches", ctypes.c_int32), ("branch_bounds", ctypes.POINTER(ctypes.c_int32))]
+                ("n_branches", ctypes.c_int32), ("branch_bounds", ctypes.POINTER(ctypes.c_int32)),
+                ("block", ctypes.c_int32)]
 
 
 _P32 = ctypes.POINTER(ctypes.c_int32)
@@ -67,7 +68,7 @@ class _Metadata(ctypes.Structure):
                 ("local_cu", _P32), ("actual_seq_qlen", _P32), ("actual_seq_kvlen", _P32),
                 ("kv_index", _P32), ("seg_q_pos0", _P32), ("kv_index_len", ctypes.c_int64),
                 ("workload_per_rank", _P64), ("visible_pairs", ctypes.c_int64),
-                ("fwd_tiles", ctypes.c_int64)]
+                ("fwd_tiles", ctypes.c_int64), ("visible_pairs_per_rank", _P64)]
 
 
 class _Schedule(ctypes.Structure):
@@ -155,7 +156,7 @@ class Plan:
     """
 
     def __init__(self, cu_seqlens, cp_size, rank, hq, hkv, d_qk, d_v=None, dtype="bf16",
-                 mask="causal", sink=0, window=0, branch_bounds=None):
+                 mask="causal", sink=0, window=0, branch_bounds=None, block=0):
         L = load_library()
         d_v = d_qk if d_v is None else d_v
         cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
@@ -171,7 +172,7 @@ class Plan:
         self.cp_size, self.rank = int(cp_size), int(rank)
         self.hq, self.hkv, self.d_qk, self.d_v = int(hq), int(hkv), int(d_qk), int(d_v)
         self.dtype, self.mask = dtype, mask
-        md = _MaskDesc(MASKS[mask], int(sink), int(window), 0, None)
+        md = _MaskDesc(MASKS[mask], int(sink), int(window), 0, None, int(block))
         self._bounds = None
         if branch_bounds is not None:
             bb = np.ascontiguousarray(np.asarray(branch_bounds, dtype=np.int32))
@@ -205,6 +206,7 @@ class Plan:
             "workload_per_rank": _arr(m.workload_per_rank, m.cp_size, np.int64),
             "visible_pairs": int(m.visible_pairs),
             "fwd_tiles": int(m.fwd_tiles),
+            "visible_pairs_per_rank": _arr(m.visible_pairs_per_rank, m.cp_size, np.int64),
         }
 
     def __del__(self):

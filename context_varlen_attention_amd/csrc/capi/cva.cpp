@@ -142,6 +142,7 @@ cva_status cva_plan_create(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp
       p->mask_type = mask->type;
       p->sink = mask->sink;
       p->window = mask->window;
+      if (mask->type == CVA_MASK_BLOCKWISE) p->block = mask->block;
       if (mask->type == CVA_MASK_SHARED_PREFIX) {
         p->n_branches = mask->n_branches;
         const size_t nb = (size_t)n_seqs * (mask->n_branches + 1);
@@ -182,6 +183,7 @@ cva_status cva_plan_get_metadata(const cva_plan* plan, cva_metadata* out) {
   out->workload_per_rank = p->workload.data();
   out->visible_pairs = p->visible_pairs;
   out->fwd_tiles = p->fwd.tile_pairs;
+  out->visible_pairs_per_rank = p->visible_pairs_per_rank.data();
   return CVA_OK;
 }
 

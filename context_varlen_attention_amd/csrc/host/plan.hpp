@@ -61,7 +61,7 @@ struct Plan {
   // request
   int32_t n_seqs = 0, cp_size = 1, rank = 0;
   int32_t hq = 0, hkv = 0, d_qk = 0, d_v = 0, dtype = 0;
-  int32_t mask_type = CVA_MASK_CAUSAL, sink = 0, window = 0, n_branches = 0;
+  int32_t mask_type = CVA_MASK_CAUSAL, sink = 0, window = 0, n_branches = 0, block = 0;
   std::vector<int32_t> cu;             // [n+1]
   std::vector<int32_t> branch_bounds;  // [n][n_branches+1] (shared prefix)
 
@@ -70,6 +70,7 @@ struct Plan {
   std::vector<int32_t> local_cu, aq, akv, kv_index, seg_q_pos0;
   std::vector<int64_t> workload;
   int64_t visible_pairs = 0;
+  std::vector<int64_t> visible_pairs_per_rank;  // [cp_size]
   std::vector<int32_t> segs;    // [2n][8]
   std::vector<int32_t> row_iv;  // [T_loc][4]: visible keys = [a0,a1) u [b0,b1)
 
@@ -107,6 +108,8 @@ cva_status build_metadata(Plan& p);
 
 // schedule.cpp
 void row_intervals(const Plan& p, int seg, int32_t a, int32_t iv[4]);
+// Visible keys of query position q of sub-sequence seq: [iv0, iv1) u [iv2, iv3).
+void position_intervals(const Plan& p, int32_t seq, int32_t q, int32_t iv[4]);
 cva_status build_schedules(Plan& p);
 void build_blob(Plan& p);
 void build_fwd_split(Plan& p);

@@ -7,7 +7,9 @@
 //
 // Every query row's visible keys form at most two intervals of in-sequence
 // positions (row_intervals): causal [0, q]; lambda [0, min(sink, q+1)) and
-// [q-window+1, q] (DCP Fig. 6(b)); shared prefix [0, q] inside the question,
+// [q-window+1, q] (DCP Fig. 6(b)); causal blockwise [0, sink blocks) and the
+// window of blocks ending with the query's block, the last block causal
+// (DCP Fig. 6(c)); shared prefix [0, q] inside the question,
 // else [0, prefix) and [answer start, q] (DCP Fig. 6(d)).  For a tile of
 // query rows the union U of its rows' sets says which K/V tiles are non-empty
 // and the intersection F which are full (no element-wise mask needed); tiles
@@ -260,15 +262,29 @@ void build_kv_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_
 
 void row_intervals(const Plan& p, int seg, int32_t a, int32_t iv[4]) {
   const int32_t* sg = &p.segs[(size_t)seg * SEG_INTS];
-  const int32_t q = sg[SEG_QPOS0] + a;
+  position_intervals(p, sg[SEG_SEQ], sg[SEG_QPOS0] + a, iv);
+}
+
+void position_intervals(const Plan& p, int32_t seq, int32_t q, int32_t iv[4]) {
   iv[0] = 0; iv[1] = q + 1; iv[2] = 0; iv[3] = 0;
-  if (p.mask_type == CVA_MASK_LAMBDA) {
+  if (p.mask_type == CVA_MASK_BLOCKWISE) {
+    // DCP paper, sparse masks (Fig. 6(c)) and evaluation: blocks of `block`
+    // tokens, `sink` leading blocks, a window of `window` blocks ending with the
+    // query's own block, and the last block (the test sample) sees everything
+    const int32_t L = p.cu[seq + 1] - p.cu[seq];
+    const int32_t b = q / p.block;
+    if (b != (L - 1) / p.block) {
+      iv[1] = std::min((int64_t)p.sink * p.block, (int64_t)q + 1);
+      iv[2] = std::max(0, (b - p.window + 1) * p.block);
+      iv[3] = q + 1;
+    }
+  } else if (p.mask_type == CVA_MASK_LAMBDA) {
     iv[1] = std::min(p.sink, q + 1);
     iv[2] = std::max(0, q - p.window + 1);
     iv[3] = q + 1;
   } else if (p.mask_type == CVA_MASK_SHARED_PREFIX) {
     const int32_t nb = p.n_branches + 1;
-    const int32_t* b = &p.branch_bounds[(size_t)sg[SEG_SEQ] * nb];
+    const int32_t* b = &p.branch_bounds[(size_t)seq * nb];
     if (q >= b[0]) {
       int32_t start = b[0];
       for (int32_t k = 1; k < nb; ++k) {
@@ -309,6 +325,23 @@ cva_status build_schedules(Plan& p) {
       row_intervals(p, sg, a, iv);
       const RowSet rs = row_set(iv);
       for (int k = 0; k < rs.n; ++k) p.visible_pairs += rs.v[k].second - rs.v[k].first;
+    }
+  }
+  // visible pairs of every rank (RFC section 2: rank s holds chunks s and
+  // 2R-1-s of every sub-sequence); rows are independent of the rank that holds them
+  p.visible_pairs_per_rank.assign(p.cp_size, 0);
+  for (int32_t i = 0; i < p.n_seqs; ++i) {
+    const int32_t L = p.cu[i + 1] - p.cu[i];
+    const int32_t c = L / (2 * p.cp_size);
+    for (int32_t s = 0; s < p.cp_size; ++s) {
+      for (int32_t j : {s, 2 * p.cp_size - 1 - s}) {
+        for (int32_t q = j * c; q < (j + 1) * c; ++q) {
+          int32_t iv[4];
+          position_intervals(p, i, q, iv);
+          const RowSet rs = row_set(iv);
+          for (int k = 0; k < rs.n; ++k) p.visible_pairs_per_rank[s] += rs.v[k].second - rs.v[k].first;
+        }
+      }
     }
   }
   FwdShape fs = forward_shape(p);

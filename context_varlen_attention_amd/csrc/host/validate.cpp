@@ -89,6 +89,10 @@ cva_status validate_request(const int32_t* cu, int32_t n_seqs, int32_t cp_size, 
         }
         break;
       }
+      case CVA_MASK_BLOCKWISE:
+        if (mask->block < 1 || mask->sink < 0 || mask->window < 1)
+          return fail(CVA_E_MASK, "blockwise mask needs block >= 1, sink >= 0 and window >= 1 (blocks)");
+        break;
       default:
         return fail(CVA_E_MASK, "unknown mask type");
     }

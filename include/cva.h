@@ -71,12 +71,18 @@ typedef enum { CVA_BF16 = 0, CVA_FP16 = 1, CVA_FP32 = 2 } cva_dtype;
 typedef enum {
   CVA_MASK_CAUSAL = 0,        /* key k visible to query q iff k <= q (positions within the sub-sequence) */
   CVA_MASK_LAMBDA = 1,        /* causal and (k < sink or q - k < window)                                 */
-  CVA_MASK_SHARED_PREFIX = 2  /* prefix rows causal; an answer row sees the prefix and itself causally   */
+  CVA_MASK_SHARED_PREFIX = 2, /* prefix rows causal; an answer row sees the prefix and itself causally   */
+  CVA_MASK_BLOCKWISE = 3      /* causal blockwise: blocks of `block` tokens; a query of block b sees keys
+                                 k <= q in the first `sink` blocks or in blocks b-window+1 .. b; a query
+                                 of the sub-sequence's last block (the test sample) sees every k <= q  */
 } cva_mask_type;
 
 /* Mask descriptor, copied into the plan by cva_plan_create.
  *   type          cva_mask_type
- *   sink, window  lambda mask only: sink >= 0, window >= 1
+ *   sink, window  lambda mask: tokens, sink >= 0, window >= 1 (window counts the diagonal);
+ *                 blockwise mask: blocks, sink >= 0, window >= 1 (window counts the own block)
+ *   block         blockwise mask only: tokens per block, >= 1 (DCP paper, evaluation: 256,
+ *                 window 2 blocks, one sink block, one test block)
  *   n_branches    shared-prefix only: answers per sequence, >= 1
  *   branch_bounds shared-prefix only: int32 [n_seqs][n_branches + 1], per sequence
  *                 {prefix_end, end_of_answer_0, ..., end_of_answer_{n_branches-1}}
@@ -89,6 +95,7 @@ typedef struct {
   int32_t window;
   int32_t n_branches;
   const int32_t* branch_bounds;
+  int32_t block;
 } cva_mask_desc;
 
 typedef struct cva_plan cva_plan;
@@ -104,6 +111,9 @@ typedef struct cva_plan cva_plan;
  *   seg_q_pos0        [n_segments]    in-sequence position of each segment's first query
  *   workload_per_rank [cp_size]       sum(q_len * kv_len) of every rank (all equal)
  *   visible_pairs     unmasked (query, key) pairs of this rank, per query head
+ *   visible_pairs_per_rank [cp_size] the same count for every rank: equal under the causal
+ *                     mask, unequal under the sparse masks (the zig-zag split balances
+ *                     sum(q_len*kv_len), not the visible pairs; DCP paper, sparse masks)
  *   fwd_tiles         non-empty (Q tile, K/V tile) pairs the forward schedule visits, per item head group */
 typedef struct {
   int64_t local_tokens;
@@ -121,6 +131,7 @@ typedef struct {
   const int64_t* workload_per_rank;
   int64_t visible_pairs;
   int64_t fwd_tiles;
+  const int64_t* visible_pairs_per_rank;
 } cva_metadata;
 
 /* Message for the last failed call on this thread ("" if none). */

@@ -87,7 +87,7 @@ def _local_rows_by_seq(w, rows=None):
 
 def _mask_for(w, i, L, positions):
     bounds = None if w.branch_bounds is None else w.branch_bounds[i]
-    return mask_rows_ref(w.mask, L, positions, w.sink, w.window, bounds)
+    return mask_rows_ref(w.mask, L, positions, w.sink, w.window, bounds, getattr(w, "block", 0))
 
 
 def fwd_ref(w, q, k, v, scale=None, rows=None, block=512, heads=None):

@@ -11,6 +11,13 @@ sub-sequence restarts its mask: the EOD reset of the MindSpeed RFC, section 2).
                    sink) plus a sliding window of the ``window`` most recent
                    tokens, the diagonal included (DCP paper, sparse masks,
                    Fig. 6(b); evaluation: 64 sink tokens and window 4096).
+* blockwise     -- causal blockwise: the sequence is cut into blocks of
+                   ``block`` tokens; a query sees, causally, the first ``sink``
+                   blocks (attention sink) and the ``window`` blocks ending with
+                   its own block; a query of the last block (the test example)
+                   sees every earlier token (DCP paper, sparse masks, Fig. 6(c);
+                   evaluation: block 256, window 2 blocks, one sink block, one
+                   test block).
 * shared_prefix -- one shared question followed by several answers; the
                    question is causal, every answer sees the whole question and
                    itself causally, never another answer (DCP paper, Fig. 6(d)
@@ -26,7 +33,7 @@ from __future__ import annotations
 import numpy as np
 
 
-def mask_rows_ref(kind, L, rows, sink=0, window=0, bounds=None):
+def mask_rows_ref(kind, L, rows, sink=0, window=0, bounds=None, block=0):
     """Mask rows ``rows`` (query positions) of a length-L sub-sequence: bool [len(rows), L]."""
     q = np.asarray(rows, dtype=np.int64)[:, None]
     k = np.arange(L, dtype=np.int64)[None, :]
@@ -35,6 +42,10 @@ def mask_rows_ref(kind, L, rows, sink=0, window=0, bounds=None):
         return causal
     if kind == "lambda":
         return causal & ((k < sink) | (q - k < window))
+    if kind == "blockwise":
+        bq, bk = q // block, k // block
+        test = bq == (L - 1) // block
+        return causal & (test | (bk < sink) | (bq - bk < window))
     if kind == "shared_prefix":
         b = [int(x) for x in bounds]
         P = b[0]
@@ -54,9 +65,9 @@ def mask_rows_ref(kind, L, rows, sink=0, window=0, bounds=None):
     raise ValueError(f"unknown mask {kind}")
 
 
-def mask_ref(kind, L, sink=0, window=0, bounds=None):
+def mask_ref(kind, L, sink=0, window=0, bounds=None, block=0):
     """Full [L, L] mask of one sub-sequence."""
-    return mask_rows_ref(kind, L, np.arange(L), sink, window, bounds)
+    return mask_rows_ref(kind, L, np.arange(L), sink, window, bounds, block)
 
 
 def visible_pairs_ref(workload, rows_by_seq=None, block=2048):
@@ -80,6 +91,6 @@ def visible_pairs_ref(workload, rows_by_seq=None, block=2048):
         rows = np.asarray(rows)
         for s in range(0, len(rows), block):
             M = mask_rows_ref(workload.mask, L, rows[s: s + block], workload.sink,
-                              workload.window, bounds)
+                              workload.window, bounds, getattr(workload, "block", 0))
             total += int(M.sum())
     return total

@@ -48,9 +48,10 @@ class Workload:
     d_qk: int
     d_v: int
     dtype: str                      # "fp32" | "bf16" | "fp16"
-    mask: str = "causal"            # "causal" | "lambda" | "shared_prefix"
-    sink: int = 0
-    window: int = 0
+    mask: str = "causal"            # "causal" | "lambda" | "shared_prefix" | "blockwise"
+    sink: int = 0                   # lambda: tokens; blockwise: blocks
+    window: int = 0                 # lambda: tokens; blockwise: blocks
+    block: int = 0                  # blockwise: tokens per block
     # shared-prefix layout: per sequence [prefix_end, branch_end_0, ..., branch_end_{B-1}]
     branch_bounds: Optional[np.ndarray] = None
     backward: bool = False
@@ -147,6 +148,8 @@ def make_workload(name: str, mask: Optional[str] = None, dtype: Optional[str] = 
         w = Workload(name, _cu(lens), 1, 0, 16, 16, 128, 128, dtype or "bf16", mask=m)
         if m == "lambda":
             w.sink, w.window = 64, 4096
+        elif m == "blockwise":
+            w.block, w.sink, w.window = 256, 1, 2
         elif m == "shared_prefix":
             w.branch_bounds = np.array([shared_prefix_bounds(L) for L in lens], dtype=np.int64)
         return w
@@ -174,9 +177,9 @@ def make_tensors(w: Workload, seed_tag: Optional[int] = None, with_dout: bool = 
 
 
 def custom_workload(lengths, cp_size, rank, hq, hkv, d_qk, d_v, dtype="bf16", mask="causal",
-                    sink=0, window=0, branch_bounds=None, name="custom") -> Workload:
+                    sink=0, window=0, branch_bounds=None, name="custom", block=0) -> Workload:
     w = Workload(name, _cu(lengths), cp_size, rank, hq, hkv, d_qk, d_v, dtype, mask=mask,
-                 sink=sink, window=window)
+                 sink=sink, window=window, block=block)
     if branch_bounds is not None:
         w.branch_bounds = np.asarray(branch_bounds, dtype=np.int64)
     return w

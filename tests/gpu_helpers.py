@@ -21,7 +21,7 @@ def torch_dtype(dt):
 def plan_for(w):
     bb = None if w.branch_bounds is None else np.asarray(w.branch_bounds)
     return cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype,
-                    mask=w.mask, sink=w.sink, window=w.window, branch_bounds=bb)
+                    mask=w.mask, sink=w.sink, window=w.window, branch_bounds=bb, block=w.block)
 
 
 def device_inputs(w, q, k, v, do=None, device="cuda"):

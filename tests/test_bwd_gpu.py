@@ -51,6 +51,9 @@ CASES = [
     ([1200, 400], 2, 1, 4, 2, 64, 64, "lambda", dict(sink=5, window=77)),
     ([1280, 768], 1, 0, 2, 1, 128, 128, "shared_prefix",
      dict(bounds=[[256, 512, 768, 1024, 1280], [128, 288, 448, 608, 768]])),
+    ([2048, 1280], 1, 0, 4, 2, 128, 128, "blockwise", dict(block=256, sink=1, window=2)),
+    ([1536, 640, 3072], 2, 1, 4, 4, 64, 64, "blockwise", dict(block=96, sink=2, window=3)),
+    ([1920, 960], 2, 0, 2, 2, 192, 128, "blockwise", dict(block=80, sink=1, window=1)),
 ]
 
 
@@ -60,7 +63,8 @@ def test_small_cases(ci, dtype):
     lens, R, r, hq, hkv, dqk, dv, mask, ex = CASES[ci]
     w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, dtype, mask=mask,
                               sink=ex.get("sink", 0), window=ex.get("window", 0),
-                              branch_bounds=ex.get("bounds"), name=f"bsmall{ci}")
+                              branch_bounds=ex.get("bounds"), name=f"bsmall{ci}",
+                              block=ex.get("block", 0))
     q, k, v, do = synth.random_tensors(w, 200 + ci)
     _run(w, q, k, v, do)
 

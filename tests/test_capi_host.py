@@ -75,7 +75,8 @@ def _wl(lens, R, r, mask, hq=4, hkv=4, **kw):
 def _plan(w):
     return cva.Plan(w.cu_seqlens, w.cp_size, w.rank, w.hq, w.hkv, w.d_qk, w.d_v, w.dtype,
                     mask=w.mask, sink=w.sink, window=w.window,
-                    branch_bounds=None if w.branch_bounds is None else w.branch_bounds)
+                    branch_bounds=None if w.branch_bounds is None else w.branch_bounds,
+                    block=w.block)
 
 
 MASK_CASES = [
@@ -88,6 +89,9 @@ MASK_CASES = [
      dict(branch_bounds=[[256, 512, 768, 1024, 1280], [128, 288, 448, 608, 768]])),
     ([1280, 768], 2, 1, "shared_prefix",
      dict(branch_bounds=[[200, 300, 300, 900, 1280], [0, 100, 400, 500, 768]])),
+    ([2048, 1280], 1, 0, "blockwise", dict(block=256, sink=1, window=2)),
+    ([1536, 640, 3072], 2, 1, "blockwise", dict(block=96, sink=2, window=3)),
+    ([1200, 400], 2, 0, "blockwise", dict(block=50, sink=1, window=1)),
 ]
 
 
@@ -105,7 +109,7 @@ def _oracle_segments(w):
 def _mask_rows(w, i, pos):
     L = int(w.cu_seqlens[i + 1] - w.cu_seqlens[i])
     b = None if w.branch_bounds is None else w.branch_bounds[i]
-    return oracle.masks.mask_rows_ref(w.mask, L, pos, w.sink, w.window, b)
+    return oracle.masks.mask_rows_ref(w.mask, L, pos, w.sink, w.window, b, w.block)
 
 
 @pytest.mark.parametrize("ci", range(len(MASK_CASES)))
@@ -291,3 +295,24 @@ def test_fwd_split_pieces(name):
     assert plan.fwd_workspace_bytes() == expect_bytes
     if name == "gqa16k":
         assert n_slots > 0  # its longest tiles exceed the per-CU average
+
+
+@pytest.mark.parametrize("ci", range(len(MASK_CASES)))
+def test_visible_pairs_per_rank_match_oracle(ci):
+    """Every rank's visible pairs, reported by one rank's plan (the zig-zag split
+    balances sum(q_len*kv_len); sparse masks leave the visible pairs unequal)."""
+    import dataclasses
+    lens, R, r, mask, ex = MASK_CASES[ci]
+    w = _wl(lens, R, r, mask, **ex)
+    got = _plan(w).metadata["visible_pairs_per_rank"]
+    exp = [oracle.visible_pairs_ref(dataclasses.replace(w, rank=s)) for s in range(R)]
+    assert list(got) == exp
+    assert got[r] == _plan(w).visible_pairs()
+    if mask == "causal":
+        assert len(set(exp)) == 1
+
+
+def test_blockwise_ranks_unequal():
+    w = _wl([4096, 2048], 4, 0, "blockwise", block=256, sink=1, window=2)
+    per = _plan(w).metadata["visible_pairs_per_rank"]
+    assert len(set(per.tolist())) > 1

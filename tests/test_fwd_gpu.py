@@ -55,6 +55,9 @@ SMALL = [
     ([1200, 400], 2, 1, 4, 2, 64, 64, "lambda", dict(sink=5, window=77)),
     ([1280, 768], 1, 0, 2, 1, 128, 128, "shared_prefix",
      dict(bounds=[[256, 512, 768, 1024, 1280], [128, 288, 448, 608, 768]])),
+    ([2048, 1280], 1, 0, 4, 2, 128, 128, "blockwise", dict(block=256, sink=1, window=2)),
+    ([1536, 640, 3072], 2, 1, 4, 4, 64, 64, "blockwise", dict(block=96, sink=2, window=3)),
+    ([1920, 960], 2, 0, 2, 2, 192, 128, "blockwise", dict(block=80, sink=1, window=1)),
 ]
 
 
@@ -64,13 +67,14 @@ def test_small_cases(ci, dtype):
     lens, R, r, hq, hkv, dqk, dv, mask, ex = SMALL[ci]
     w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, dtype, mask=mask,
                               sink=ex.get("sink", 0), window=ex.get("window", 0),
-                              branch_bounds=ex.get("bounds"), name=f"small{ci}")
+                              branch_bounds=ex.get("bounds"), name=f"small{ci}",
+                              block=ex.get("block", 0))
     q, k, v = synth.random_tensors(w, 100 + ci, with_dout=False)
     _run(w, q, k, v)
 
 
 # cases whose forward Q tiles walk more than 8 K/V tiles: cva_fwd_split cuts them
-SPLIT = [1, 2, 3, 5]
+SPLIT = [1, 2, 3, 5, 8, 9]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
@@ -79,7 +83,8 @@ def test_small_cases_split(ci, dtype):
     lens, R, r, hq, hkv, dqk, dv, mask, ex = SMALL[ci]
     w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, dtype, mask=mask,
                               sink=ex.get("sink", 0), window=ex.get("window", 0),
-                              branch_bounds=ex.get("bounds"), name=f"small{ci}")
+                              branch_bounds=ex.get("bounds"), name=f"small{ci}",
+                              block=ex.get("block", 0))
     q, k, v = synth.random_tensors(w, 100 + ci, with_dout=False)
     _run(w, q, k, v, split=True)
 
@@ -116,7 +121,7 @@ def test_long128k_sampled_rows():
     _run(w, q, k, v, rows=_sample_rows(w, 48, 2))
 
 
-@pytest.mark.parametrize("mask", ["lambda", "shared_prefix"])
+@pytest.mark.parametrize("mask", ["lambda", "shared_prefix", "blockwise"])
 def test_sparse8_sampled_rows(mask):
     w = synth.make_workload("sparse8", mask=mask)
     q, k, v = synth.make_tensors(w, with_dout=False)

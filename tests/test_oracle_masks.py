@@ -1,9 +1,9 @@
 """Pins for the oracle's mask predicates (CPU only).
 
 Small masks are written out by hand from the DCP paper's descriptions (sparse
-masks, Fig. 6(b) lambda = attention sink + sliding window; Fig. 6(d) shared
-question); degenerate settings must reduce to the causal mask; pair counts
-must match closed forms.
+masks, Fig. 6(b) lambda = attention sink + sliding window; Fig. 6(c) causal
+blockwise; Fig. 6(d) shared question); degenerate settings must reduce to the
+causal mask; pair counts must match closed forms.
 """
 import numpy as np
 import pytest
@@ -51,6 +51,48 @@ def test_shared_prefix_small():
         "1111000111",
     ])
     assert (mask_ref("shared_prefix", 10, bounds=[4, 7, 10]) == exp).all()
+
+
+def test_blockwise_small():
+    # L=11, blocks of 2 (the last block, position 10, is the test example),
+    # one sink block, a window of 2 blocks (the own block and the one before)
+    exp = _m([
+        "10000000000",
+        "11000000000",
+        "11100000000",
+        "11110000000",
+        "11111000000",
+        "11111100000",
+        "11001110000",
+        "11001111000",
+        "11000011100",
+        "11000011110",
+        "11111111111",
+    ])
+    assert (mask_ref("blockwise", 11, sink=1, window=2, block=2) == exp).all()
+
+
+@pytest.mark.parametrize("L", [1, 5, 33, 128])
+def test_blockwise_degenerate_reduce_to_causal(L):
+    c = mask_ref("causal", L)
+    assert (mask_ref("blockwise", L, sink=0, window=L, block=1) == c).all()   # window covers all
+    assert (mask_ref("blockwise", L, sink=L, window=1, block=1) == c).all()   # all blocks are sinks
+    assert (mask_ref("blockwise", L, sink=0, window=1, block=L) == c).all()   # one block = the test block
+
+
+def test_blockwise_row_counts_closed_form():
+    L, B, S, W = 1000, 64, 1, 2
+    M = mask_ref("blockwise", L, sink=S, window=W, block=B)
+    last = (L - 1) // B
+    for q in range(L):
+        b = q // B
+        if b == last:
+            exp = q + 1
+        else:
+            sink_end = min(S * B, q + 1)
+            ws = max(0, (b - W + 1) * B)
+            exp = q + 1 if ws <= sink_end else sink_end + (q + 1 - ws)
+        assert M[q].sum() == exp
 
 
 @pytest.mark.parametrize("L", [1, 5, 33, 128])
