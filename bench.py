@@ -107,7 +107,7 @@ def kernel_flops(w, pairs):
 def kernel_bytes(w):
     t_loc = w.total_tokens // w.cp_size
     esz = 4 if w.dtype == "fp32" else 2
-    return {"bwd_pre": 2 * t_loc * w.hq * w.d_v * esz + t_loc * w.hq * 4}
+    return {"bwd_pre": 2 * t_loc * w.hq * w.d_v * esz + t_loc * w.hq * 12}  # O, dO, LSE in; Delta, LSE*log2e out
 
 
 KERNEL_SOURCES = {

@@ -305,7 +305,7 @@ cva_status cva_fwd_split(const cva_plan* plan, const void* q, const void* k_rm, 
 size_t cva_bwd_workspace_bytes(const cva_plan* plan) {
   const Plan* p = reinterpret_cast<const Plan*>(plan);
   if (p == nullptr) return 0;
-  return (size_t)p->T_loc * p->hq * sizeof(float);
+  return 2 * (size_t)p->T_loc * p->hq * sizeof(float);  // Delta, LSE * log2(e)
 }
 
 cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
@@ -337,6 +337,7 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   bp.dk = dk_rm;
   bp.dv = dv_rm;
   bp.delta = (float*)workspace;
+  bp.lse2 = bp.delta + (size_t)p->T_loc * p->hq;
   bp.t = tables(*p);
   bp.n_dq_tiles = p->dq.n_tiles();
   bp.n_kv_tiles = p->dkdv.n_tiles();

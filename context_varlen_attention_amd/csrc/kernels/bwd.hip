@@ -38,7 +38,9 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O), one thread per (local row, head)
+// Delta = rowsum(dO * O) and LSE * log2(e), one thread per (local row, head);
+// the scaled LSE lets the gradient kernels form P = exp2(S * scale * log2 e -
+// LSE * log2 e) with one fused multiply-add
 // ---------------------------------------------------------------------------
 template <typename E, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams P) {
@@ -61,6 +63,7 @@ __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams P) {
     }
   }
   P.delta[(int64_t)head * P.t_loc + row] = acc;
+  P.lse2[(int64_t)head * P.t_loc + row] = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
 }
 
 // ---------------------------------------------------------------------------
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
     dma_rows<DQK>(sQ[slot], [&](int r) { return qgb + ((int64_t)lrow(r) * P.hq + head) * (DQK * 2); }, tid, wave);
     dma_rows<DV>(sO[slot], [&](int r) { return ogb + ((int64_t)lrow(r) * P.hq + head) * (DV * 2); }, tid, wave);
     if (wave == 0)
-      dma4(P.lse + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
+      dma4(P.lse2 + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
     else if (wave == 1)
       dma4(P.delta + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sD[slot]));
     else if (wave == 2)
@@ -328,21 +331,19 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
       for (int st = 0; st < QS; ++st) s = E::mfma32(as_vec8<E>(qo.row(q_s, qs, st)), kf[st], s);
 #pragma unroll
       for (int st = 0; st < VS; ++st) dp = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), vf[st], dp);
-      // lane holds query qs*32 + 8i + 4*half + j (r = 4i + j) for key kpos
-      f32x4_t lv[4], dv4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lv[i] = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i + 4 * half);
-        dv4[i] = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * i + 4 * half);
-      }
+      // lane holds query qs*32 + 8i + 4*half + j (r = 4i + j) for key kpos; the
+      // LSE (scaled by log2 e) and Delta of those queries are read per i
       uint32_t pp[2][4], pd[2][4];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
+        const int i0 = r >> 2;
+        const f32x4_t lv = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i0 + 4 * half);
+        const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * i0 + 4 * half);
         float pv[2], dsv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = (r + u) >> 2, j = (r + u) & 3;
-          float x = fmaf(s[r + u], sl2, -lv[i][j] * kLog2e);
+          float x = fmaf(s[r + u], sl2, -lv[j]);
           if (partial) {
             const int q = qs * 32 + 8 * i + 4 * half + j;
             const int4 iv = *(const int4*)(sIv[slot] + 4 * q);
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
           }
           const float p = __builtin_amdgcn_exp2f(x);
           pv[u] = p;
-          dsv[u] = p * (dp[r + u] - dv4[i][j]);
+          dsv[u] = p * (dp[r + u] - dv4[j]);
         }
         pp[r >> 3][(r & 7) >> 1] = pack2<E>(pv[0], pv[1]);
         pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
   if (valid) {
     const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
     lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
-    lse2 = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
+    lse2 = P.lse2[(int64_t)head * P.t_loc + row];
     delta = P.delta[(int64_t)head * P.t_loc + row];
   }
   if (tid < 4 * nspan) sSpan[tid] = P.t.dq_spans[span0 * 4 + tid];

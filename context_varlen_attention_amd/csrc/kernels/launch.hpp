@@ -56,7 +56,8 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;            // [hq, t_loc] workspace
+  float* delta;            // [hq, t_loc] workspace: Delta = rowsum(dO * O)
+  float* lse2;             // [hq, t_loc] workspace: LSE * log2(e)
   PlanTables t;
   int32_t n_dq_tiles, n_kv_tiles, n_zero_ranges;
   int32_t dq_heads_per_tile, dq_head_groups;

@@ -185,7 +185,8 @@ cva_status cva_fwd_split(const cva_plan* plan, const void* q, const void* k_rm, 
                          void* o, float* lse, float softmax_scale, void* workspace,
                          size_t ws_bytes, void* stream);
 
-/* Workspace bytes cva_bwd needs (fp32 row statistics). */
+/* Workspace bytes cva_bwd needs (fp32 row statistics: Delta and LSE*log2(e),
+ * 2 * T_loc * Hq floats). */
 size_t cva_bwd_workspace_bytes(const cva_plan* plan);
 
 /* Backward (same interface, backward half): given dout [T_loc, Hq, Dv] and the
