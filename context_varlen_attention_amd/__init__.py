@@ -24,8 +24,8 @@ import os
 
 import numpy as np
 
-__all__ = ["Plan", "fwd", "bwd", "CvaError", "local_token_ids", "rank_major_token_ids",
-           "library_path", "load_library", "timing_enable", "timing_read"]
+__all__ = ["Plan", "Placement", "fwd", "bwd", "CvaError", "local_token_ids",
+           "rank_major_token_ids", "library_path", "load_library", "timing_enable", "timing_read"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcva.so")
@@ -77,10 +77,21 @@ class _Schedule(ctypes.Structure):
                 ("tiles", _P32), ("spans", _P32)]
 
 
+class _PlacementInfo(ctypes.Structure):
+    _fields_ = [("n_devices", ctypes.c_int32), ("block", ctypes.c_int32),
+                ("n_data_blocks", ctypes.c_int32), ("n_comp_blocks", ctypes.c_int32),
+                ("data_blocks", _P32), ("comp_blocks", _P32), ("comp_pairs", _P64),
+                ("device_tokens", _P64), ("device_pairs", _P64), ("device_send_bytes", _P64),
+                ("device_recv_bytes", _P64), ("total_comm_bytes", ctypes.c_int64),
+                ("block_comm_bytes", ctypes.c_int64), ("zigzag_valid", ctypes.c_int32),
+                ("zigzag_pairs", _P64), ("zigzag_comm_bytes", ctypes.c_int64)]
+
+
 EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_get_metadata",
            "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_fwd_workspace_bytes",
            "cva_fwd_split", "cva_bwd_workspace_bytes",
-           "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read"]
+           "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read",
+           "cva_placement_create", "cva_placement_get", "cva_placement_destroy"]
 
 KERNEL_NAMES = ["fwd", "bwd_pre", "bwd_zero", "bwd_dkdv", "bwd_dq", "fwd_merge"]
 
@@ -132,6 +143,13 @@ def load_library():
     L.cva_timing_enable.argtypes = [i32]
     L.cva_timing_read.restype = i32
     L.cva_timing_read.argtypes = [ctypes.POINTER(_KernelTimes)]
+    L.cva_placement_create.restype = i32
+    L.cva_placement_create.argtypes = [_P32, i32, ctypes.POINTER(_MaskDesc), i32, i32, i32, i32,
+                                       i32, i32, i32, ctypes.c_double, ctypes.POINTER(vp)]
+    L.cva_placement_get.restype = i32
+    L.cva_placement_get.argtypes = [vp, ctypes.POINTER(_PlacementInfo)]
+    L.cva_placement_destroy.restype = None
+    L.cva_placement_destroy.argtypes = [vp]
     _lib = L
     return L
 
@@ -259,6 +277,74 @@ class Plan:
 
     def visible_pairs(self):
         return self.metadata["visible_pairs"]
+
+
+def _mask_desc(mask, sink, window, branch_bounds, block):
+    """(_MaskDesc, bounds array kept alive by the caller)."""
+    if mask not in MASKS:
+        raise CvaError(8, f"unknown mask {mask!r}")
+    md = _MaskDesc(MASKS[mask], int(sink), int(window), 0, None, int(block))
+    bb = None
+    if branch_bounds is not None:
+        bb = np.ascontiguousarray(np.asarray(branch_bounds, dtype=np.int32))
+        if bb.ndim != 2:
+            raise CvaError(8, "branch_bounds must be 2-D [n_seqs][n_branches+1]")
+        md.n_branches = bb.shape[1] - 1
+        md.branch_bounds = bb.ctypes.data_as(_P32)
+    return md, bb
+
+
+class Placement:
+    """Block placement of a packed batch over ``n_devices`` (``cva_placement_create``).
+
+    Attributes (numpy): ``data_blocks`` [n,4] {sequence, first token, tokens, device},
+    ``comp_blocks`` [m,4] {sequence, q block, k/v block, device}, ``comp_pairs`` [m],
+    ``device_tokens`` / ``device_pairs`` / ``device_send_bytes`` / ``device_recv_bytes``
+    [n_devices], ``total_comm_bytes`` (connectivity volume), ``block_comm_bytes``
+    (per-computation-block volume), ``zigzag_pairs`` [n_devices] or None when some
+    sequence length does not divide by ``2 * n_devices``, ``zigzag_comm_bytes``.
+    ``mask_block`` is the blockwise mask's block size; ``block`` the placement's.
+    """
+
+    def __init__(self, cu_seqlens, n_devices, block, hq=1, hkv=1, d_qk=128, d_v=None,
+                 dtype="bf16", mask="causal", sink=0, window=0, branch_bounds=None,
+                 mask_block=0, epsilon=0.1):
+        L = load_library()
+        d_v = d_qk if d_v is None else d_v
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        if cu.ndim != 1:
+            raise CvaError(1, "cu_seqlens must be 1-D")
+        if cu.size and (cu.max() > np.iinfo(np.int32).max or cu.min() < np.iinfo(np.int32).min):
+            raise CvaError(1, "cu_seqlens out of int32 range")
+        cu32 = np.ascontiguousarray(cu.astype(np.int32))
+        if dtype not in DTYPES:
+            raise CvaError(7, f"unknown dtype {dtype!r}")
+        md, bb = _mask_desc(mask, sink, window, branch_bounds, mask_block)
+        n_seqs = max(int(cu32.size) - 1, 0)
+        handle = ctypes.c_void_p()
+        _check(L.cva_placement_create(cu32.ctypes.data_as(_P32) if cu32.size else None, n_seqs,
+                                      ctypes.byref(md), int(n_devices), int(block), int(hq),
+                                      int(hkv), int(d_qk), int(d_v), DTYPES[dtype],
+                                      float(epsilon), ctypes.byref(handle)))
+        del bb
+        try:
+            info = _PlacementInfo()
+            _check(L.cva_placement_get(handle, ctypes.byref(info)))
+            r = info.n_devices
+            self.n_devices, self.block = int(info.n_devices), int(info.block)
+            self.data_blocks = _arr(info.data_blocks, info.n_data_blocks * 4, np.int64).reshape(-1, 4)
+            self.comp_blocks = _arr(info.comp_blocks, info.n_comp_blocks * 4, np.int64).reshape(-1, 4)
+            self.comp_pairs = _arr(info.comp_pairs, info.n_comp_blocks, np.int64)
+            self.device_tokens = _arr(info.device_tokens, r, np.int64)
+            self.device_pairs = _arr(info.device_pairs, r, np.int64)
+            self.device_send_bytes = _arr(info.device_send_bytes, r, np.int64)
+            self.device_recv_bytes = _arr(info.device_recv_bytes, r, np.int64)
+            self.total_comm_bytes = int(info.total_comm_bytes)
+            self.block_comm_bytes = int(info.block_comm_bytes)
+            self.zigzag_pairs = _arr(info.zigzag_pairs, r, np.int64) if info.zigzag_valid else None
+            self.zigzag_comm_bytes = int(info.zigzag_comm_bytes)
+        finally:
+            L.cva_placement_destroy(handle)
 
 
 def _stream_ptr(stream, device):

@@ -20,7 +20,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 LIB = os.path.join(PKG, "libcva.so")
 
-HOST_SOURCES = ["host/validate.cpp", "host/metadata.cpp", "host/schedule.cpp", "capi/cva.cpp"]
+HOST_SOURCES = ["host/validate.cpp", "host/metadata.cpp", "host/schedule.cpp", "host/placement.cpp",
+                "capi/cva.cpp"]
 HIP_SOURCES = ["kernels/fwd.hip", "kernels/bwd.hip"]
 
 HIP_FLAGS = [

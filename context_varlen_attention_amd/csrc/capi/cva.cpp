@@ -374,6 +374,86 @@ cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedu
   return CVA_OK;
 }
 
+cva_status cva_placement_create(const int32_t* cu_seqlens, int32_t n_seqs, const cva_mask_desc* mask,
+                                int32_t n_devices, int32_t block, int32_t hq, int32_t hkv,
+                                int32_t d_qk, int32_t d_v, int32_t dtype, double epsilon,
+                                cva_placement** out) {
+  if (out == nullptr) return fail(CVA_E_ARG, "out is NULL");
+  *out = nullptr;
+  if (cu_seqlens == nullptr) return fail(CVA_E_ARG, "cu_seqlens is NULL");
+  if (n_seqs < 1) return fail(CVA_E_CU_SEQLENS, "cu_seqlens must hold at least one sub-sequence");
+  if (cu_seqlens[0] != 0) return fail(CVA_E_CU_SEQLENS, "cu_seqlens must start at 0");
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (cu_seqlens[i + 1] <= cu_seqlens[i]) return fail(CVA_E_CU_SEQLENS, "cu_seqlens must be strictly increasing");
+  if (n_devices < 1 || n_devices > 64) return fail(CVA_E_RANK, "n_devices must be in [1, 64]");
+  if (!(epsilon >= 0.0) || epsilon > 1e6) return fail(CVA_E_ARG, "epsilon must be >= 0");
+  if (block < 1) return fail(CVA_E_ARG, "block must be >= 1");
+  if (hq < 1 || hkv < 1 || d_qk < 1 || d_v < 1) return fail(CVA_E_HEADS, "head counts and dims must be >= 1");
+  if (dtype != CVA_BF16 && dtype != CVA_FP16 && dtype != CVA_FP32) return fail(CVA_E_DTYPE, "unknown dtype");
+  cva_status st = cva::validate_mask(mask, cu_seqlens, n_seqs);
+  if (st != CVA_OK) return st;
+  auto* pl = new (std::nothrow) cva::Placement();
+  if (pl == nullptr) return fail(CVA_E_ARG, "out of host memory");
+  try {
+    Plan& m = pl->mask;
+    m.n_seqs = n_seqs;
+    m.cu.assign(cu_seqlens, cu_seqlens + n_seqs + 1);
+    if (mask != nullptr) {
+      m.mask_type = mask->type;
+      m.sink = mask->sink;
+      m.window = mask->window;
+      if (mask->type == CVA_MASK_BLOCKWISE) m.block = mask->block;
+      if (mask->type == CVA_MASK_SHARED_PREFIX) {
+        m.n_branches = mask->n_branches;
+        m.branch_bounds.assign(mask->branch_bounds, mask->branch_bounds + (size_t)n_seqs * (mask->n_branches + 1));
+      }
+    }
+    pl->n_devices = n_devices;
+    pl->block = block;
+    pl->hq = hq;
+    pl->hkv = hkv;
+    pl->d_qk = d_qk;
+    pl->d_v = d_v;
+    pl->dtype = dtype;
+    pl->epsilon = epsilon;
+    st = cva::build_placement(*pl);
+  } catch (const std::bad_alloc&) {
+    st = fail(CVA_E_ARG, "out of host memory while placing blocks");
+  }
+  if (st != CVA_OK) {
+    delete pl;
+    return st;
+  }
+  *out = reinterpret_cast<cva_placement*>(pl);
+  return CVA_OK;
+}
+
+cva_status cva_placement_get(const cva_placement* placement, cva_placement_info* out) {
+  const auto* pl = reinterpret_cast<const cva::Placement*>(placement);
+  if (pl == nullptr || out == nullptr) return fail(CVA_E_ARG, "placement or out is NULL");
+  out->n_devices = pl->n_devices;
+  out->block = pl->block;
+  out->n_data_blocks = (int32_t)(pl->data.size() / 4);
+  out->n_comp_blocks = (int32_t)pl->comp_pairs.size();
+  out->data_blocks = pl->data.data();
+  out->comp_blocks = pl->comp.data();
+  out->comp_pairs = pl->comp_pairs.data();
+  out->device_tokens = pl->device_tokens.data();
+  out->device_pairs = pl->device_pairs.data();
+  out->device_send_bytes = pl->device_send_bytes.data();
+  out->device_recv_bytes = pl->device_recv_bytes.data();
+  out->total_comm_bytes = pl->total_comm_bytes;
+  out->block_comm_bytes = pl->block_comm_bytes;
+  out->zigzag_valid = pl->zigzag_ok ? 1 : 0;
+  out->zigzag_pairs = pl->zigzag_pairs.data();
+  out->zigzag_comm_bytes = pl->zigzag_comm_bytes;
+  return CVA_OK;
+}
+
+void cva_placement_destroy(cva_placement* placement) {
+  delete reinterpret_cast<cva::Placement*>(placement);
+}
+
 cva_status cva_timing_enable(int32_t on) {
   if (on) {
     hipError_t e = g_timer.drain();

@@ -94,6 +94,24 @@ struct Plan {
   size_t dev_bytes = 0;
 };
 
+// Placement of data and computation blocks over devices (placement.cpp).
+struct Placement {
+  Plan mask;  // the request's sequences and mask (cu, n_seqs, mask fields)
+  int32_t n_devices = 1, block = 1;
+  int32_t hq = 1, hkv = 1, d_qk = 0, d_v = 0, dtype = 0;
+  double epsilon = 0.1;             // computation imbalance tolerance
+  std::vector<int32_t> data;        // [n][4] {sequence, first token, tokens, device}
+  std::vector<int32_t> comp;        // [m][4] {sequence, q block, k/v block, device}
+  std::vector<int64_t> comp_pairs;  // [m] visible pairs per head
+  std::vector<int64_t> device_tokens, device_pairs, device_send_bytes, device_recv_bytes;  // [n_devices]
+  int64_t total_comm_bytes = 0;     // connectivity: each remote block moved once per device
+  int64_t block_comm_bytes = 0;     // per computation block: every remote use counted
+  bool zigzag_ok = false;
+  std::vector<int64_t> zigzag_pairs;  // [n_devices]
+  int64_t zigzag_comm_bytes = 0;      // K/V all-gather of the zig-zag split
+};
+cva_status build_placement(Placement& pl);
+
 // Thread-local error message used by the C ABI.
 void set_error(const std::string& msg);
 const char* last_error();
@@ -102,6 +120,9 @@ const char* last_error();
 cva_status validate_request(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp_size,
                             int32_t rank, const cva_mask_desc* mask, int32_t hq, int32_t hkv,
                             int32_t d_qk, int32_t d_v, int32_t dtype);
+
+// Mask descriptor checks (also used by the block placement); cu is validated.
+cva_status validate_mask(const cva_mask_desc* mask, const int32_t* cu, int32_t n_seqs);
 
 // metadata.cpp
 cva_status build_metadata(Plan& p);

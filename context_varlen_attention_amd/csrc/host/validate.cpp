@@ -29,6 +29,41 @@ static bool head_dims_supported(int32_t /*dtype*/, int32_t d_qk, int32_t d_v) {
   return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
 }
 
+cva_status validate_mask(const cva_mask_desc* mask, const int32_t* cu, int32_t n_seqs) {
+  if (mask != nullptr) {
+    switch (mask->type) {
+      case CVA_MASK_CAUSAL:
+        break;
+      case CVA_MASK_LAMBDA:
+        if (mask->sink < 0 || mask->window < 1)
+          return fail(CVA_E_MASK, "lambda mask needs sink >= 0 and window >= 1");
+        break;
+      case CVA_MASK_SHARED_PREFIX: {
+        if (mask->n_branches < 1 || mask->branch_bounds == nullptr)
+          return fail(CVA_E_MASK, "shared-prefix mask needs n_branches >= 1 and branch_bounds");
+        const int32_t nb = mask->n_branches + 1;
+        for (int32_t i = 0; i < n_seqs; ++i) {
+          const int32_t* b = mask->branch_bounds + (int64_t)i * nb;
+          int32_t L = cu[i + 1] - cu[i];
+          if (b[0] < 0) return fail(CVA_E_MASK, "shared-prefix bounds must be >= 0");
+          for (int32_t k = 1; k < nb; ++k)
+            if (b[k] < b[k - 1]) return fail(CVA_E_MASK, "shared-prefix bounds must be non-decreasing");
+          if (b[nb - 1] != L)
+            return fail(CVA_E_MASK, "last shared-prefix bound must equal the sub-sequence length");
+        }
+        break;
+      }
+      case CVA_MASK_BLOCKWISE:
+        if (mask->block < 1 || mask->sink < 0 || mask->window < 1)
+          return fail(CVA_E_MASK, "blockwise mask needs block >= 1, sink >= 0 and window >= 1 (blocks)");
+        break;
+      default:
+        return fail(CVA_E_MASK, "unknown mask type");
+    }
+  }
+  return CVA_OK;
+}
+
 cva_status validate_request(const int32_t* cu, int32_t n_seqs, int32_t cp_size, int32_t rank,
                             const cva_mask_desc* mask, int32_t hq, int32_t hkv, int32_t d_qk,
                             int32_t d_v, int32_t dtype) {
@@ -66,38 +101,7 @@ cva_status validate_request(const int32_t* cu, int32_t n_seqs, int32_t cp_size, 
        << "); supported: (64,64), (128,128), (192,128)";
     return fail(CVA_E_HEADDIM, os.str());
   }
-  if (mask != nullptr) {
-    switch (mask->type) {
-      case CVA_MASK_CAUSAL:
-        break;
-      case CVA_MASK_LAMBDA:
-        if (mask->sink < 0 || mask->window < 1)
-          return fail(CVA_E_MASK, "lambda mask needs sink >= 0 and window >= 1");
-        break;
-      case CVA_MASK_SHARED_PREFIX: {
-        if (mask->n_branches < 1 || mask->branch_bounds == nullptr)
-          return fail(CVA_E_MASK, "shared-prefix mask needs n_branches >= 1 and branch_bounds");
-        const int32_t nb = mask->n_branches + 1;
-        for (int32_t i = 0; i < n_seqs; ++i) {
-          const int32_t* b = mask->branch_bounds + (int64_t)i * nb;
-          int32_t L = cu[i + 1] - cu[i];
-          if (b[0] < 0) return fail(CVA_E_MASK, "shared-prefix bounds must be >= 0");
-          for (int32_t k = 1; k < nb; ++k)
-            if (b[k] < b[k - 1]) return fail(CVA_E_MASK, "shared-prefix bounds must be non-decreasing");
-          if (b[nb - 1] != L)
-            return fail(CVA_E_MASK, "last shared-prefix bound must equal the sub-sequence length");
-        }
-        break;
-      }
-      case CVA_MASK_BLOCKWISE:
-        if (mask->block < 1 || mask->sink < 0 || mask->window < 1)
-          return fail(CVA_E_MASK, "blockwise mask needs block >= 1, sink >= 0 and window >= 1 (blocks)");
-        break;
-      default:
-        return fail(CVA_E_MASK, "unknown mask type");
-    }
-  }
-  return CVA_OK;
+  return validate_mask(mask, cu, n_seqs);
 }
 
 }  // namespace cva

@@ -222,6 +222,59 @@ typedef struct {
 
 cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out);
 
+/* Block placement over n_devices (DCP paper, section 4.1 and its placement
+ * model): data blocks are the Q, K/V and O rows (all heads) of `block`
+ * consecutive tokens of one sequence, kept on one device; computation blocks
+ * are (Q block, K/V block) pairs of one sequence whose mask is not all zero.
+ * A greedy planner stands in for the page's hypergraph partitioner: data
+ * blocks balanced in tokens, computation blocks balanced in visible pairs
+ * within (1 + epsilon) of the mean where possible, and the connectivity
+ * volume (each remote input block fetched once per computing device, each
+ * partial output block returned once per computing device) kept low.  Host
+ * only; the kernels of this library run one rank's share of the RFC's zig-zag
+ * split, whose per-rank pairs and K/V all-gather volume are reported beside it.
+ *   data_blocks    [n_data_blocks][4]  {sequence, first token, tokens, device}
+ *   comp_blocks    [n_comp_blocks][4]  {sequence, q block, k/v block, device}
+ *   comp_pairs     [n_comp_blocks]     visible (query, key) pairs per head
+ *   device_tokens / device_pairs / device_send_bytes / device_recv_bytes
+ *                  [n_devices], under the connectivity volume
+ *   total_comm_bytes  connectivity volume: sum over data blocks of size times
+ *                  (devices spanned - 1)
+ *   block_comm_bytes  the page's per-computation-block volume: sizes of the
+ *                  remote inputs and outputs of every computation block
+ *   zigzag_valid   1 when every sequence length divides by 2*n_devices
+ *   zigzag_pairs   [n_devices] visible pairs per rank under the zig-zag split
+ *   zigzag_comm_bytes  K/V bytes all ranks receive in the zig-zag all-gather
+ * Sizes come from hq, hkv, d_qk, d_v and dtype (a cva_dtype).  Sequences need
+ * not be aligned.  n_devices in [1, 64], block >= 1, epsilon >= 0.  Errors as
+ * cva_plan_create; the object owns every array until cva_placement_destroy. */
+typedef struct cva_placement cva_placement;
+typedef struct {
+  int32_t n_devices;
+  int32_t block;
+  int32_t n_data_blocks;
+  int32_t n_comp_blocks;
+  const int32_t* data_blocks;
+  const int32_t* comp_blocks;
+  const int64_t* comp_pairs;
+  const int64_t* device_tokens;
+  const int64_t* device_pairs;
+  const int64_t* device_send_bytes;
+  const int64_t* device_recv_bytes;
+  int64_t total_comm_bytes;
+  int64_t block_comm_bytes;
+  int32_t zigzag_valid;
+  const int64_t* zigzag_pairs;
+  int64_t zigzag_comm_bytes;
+} cva_placement_info;
+
+cva_status cva_placement_create(const int32_t* cu_seqlens, int32_t n_seqs, const cva_mask_desc* mask,
+                                int32_t n_devices, int32_t block, int32_t hq, int32_t hkv,
+                                int32_t d_qk, int32_t d_v, int32_t dtype, double epsilon,
+                                cva_placement** out);
+cva_status cva_placement_get(const cva_placement* placement, cva_placement_info* out);
+void cva_placement_destroy(cva_placement* placement);
+
 /* Per-kernel timing, for benchmarks.  While enabled, cva_fwd and cva_bwd
  * record a hipEvent before and after every kernel they launch, on the stream
  * the kernel is launched on.  cva_timing_read waits for the recorded events,

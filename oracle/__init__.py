@@ -21,6 +21,9 @@ materialised, softmax taken directly):
 * ``mask_ref``  -- causal (EOD reset), lambda (sink + sliding window) and
                    shared-prefix masks (DCP paper, section on sparse attention
                    masks, Fig. 6 (b) and (d); evaluation "Attention Masks").
+* ``placement`` -- data and computation blocks of a batch and the
+                   communication volumes of an assignment of them to devices
+                   (DCP paper, section 4.1 and its placement model).
 * ``fwd_ref`` / ``bwd_ref`` -- masked softmax attention and its gradients on the
                    rank's local rows, K/V read from the unsplit tensors (DCP
                    paper, background: masked self-attention; RFC section 1.3:
