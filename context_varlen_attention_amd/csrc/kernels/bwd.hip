@@ -171,6 +171,15 @@ __device__ __forceinline__ void dma_rows(char* lds, RowSrc row_src, int tid, int
 template <int DQK>
 constexpr int kDkvStages = DQK > 128 ? 3 : 4;
 
+// Bits [lo, hi) of a 32-bit word, both ends clamped to [0, 32].
+__device__ __forceinline__ uint32_t key_bits(int lo, int hi) {
+  lo = max(lo, 0);
+  hi = min(hi, 32);
+  if (hi <= lo) return 0u;
+  const uint32_t upto = hi >= 32 ? ~0u : (1u << hi) - 1u;
+  return upto & ~((1u << lo) - 1u);
+}
+
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
   constexpr int BQ = 64;           // queries per Q tile
@@ -186,6 +195,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
   __shared__ __attribute__((aligned(16))) float sL[NS][BQ];
   __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
   __shared__ __attribute__((aligned(16))) int32_t sIv[NS][BQ * 4];
+  // Partial tiles: each wave first turns the tile's row intervals into one word of
+  // key bits per query, then every element tests a bit (for the widest Q/K
+  // head dimension the registers are short and the intervals are tested per
+  // element instead).
+  constexpr bool kKeyBits = DQK <= 128;
+  __shared__ __attribute__((aligned(16))) uint32_t sMask[4][BQ];  // per wave: visible keys of each query
   __shared__ __attribute__((aligned(16))) int32_t sSpan[kDkvMaxSpans * 4];
 
   const int tid = threadIdx.x;
@@ -323,6 +338,17 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
     const bool isB = (cC.seg & 1) != 0;
     const int q_rem = (isB ? qlenB : qlenA) - cC.qt * BQ;  // valid rows of this tile
     const bool partial = cC.partial != 0;
+    if (kKeyBits && partial) {
+      // lane q: bit kk set when query q of the tile sees key k0 + 32*wave + kk
+      const int4 iv = *(const int4*)(sIv[slot] + 4 * lane);
+      const int kb = k0 + wave * 32;
+      const uint32_t m = lane < q_rem ? key_bits(iv.x - kb, iv.y - kb) | key_bits(iv.z - kb, iv.w - kb) : 0u;
+      sMask[wave][lane] = m;
+      // read back by the same wave only: LDS operations of one wave run in order
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
 #pragma unroll
     for (int qs = 0; qs < BQ / 32; ++qs) {
       // S[q][key] and dP[q][key] for 32 queries x this wave's 32 keys
@@ -339,13 +365,16 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
         const int i0 = r >> 2;
         const f32x4_t lv = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i0 + 4 * half);
         const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * i0 + 4 * half);
+        u32x2_t mq = {~0u, ~0u};  // key bits of the pair's two queries
+        if (kKeyBits && partial) mq = *(const u32x2_t*)(sMask[wave] + qs * 32 + 8 * i0 + 4 * half + (r & 3));
         float pv[2], dsv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const int i = (r + u) >> 2, j = (r + u) & 3;
+          const int j = (r + u) & 3;
           float x = fmaf(s[r + u], sl2, -lv[j]);
-          if (partial) {
-            const int q = qs * 32 + 8 * i + 4 * half + j;
+          if (kKeyBits && partial) x = ((mq[u] >> col) & 1u) ? x : -INFINITY;
+          if (!kKeyBits && partial) {  // the interval test per element (fewer registers)
+            const int q = qs * 32 + 8 * i0 + 4 * half + j;
             const int4 iv = *(const int4*)(sIv[slot] + 4 * q);
             const bool vis = (q < q_rem) & (((kpos >= iv.x) & (kpos < iv.y)) | ((kpos >= iv.z) & (kpos < iv.w)));
             x = vis ? x : -INFINITY;
