@@ -26,6 +26,8 @@
 //                     accumulators.
 //   dq_kernel         Q-stationary like the forward: S^T = K Q^T, dP^T = V dO^T,
 //                     dQ^T += K^T dS^T.
+#include <type_traits>
+
 #include "../host/plan.hpp"
 #include "common.hpp"
 #include "launch.hpp"
@@ -140,20 +142,20 @@ struct TileOffsets {
   }
 };
 
-// DMA of a 64-row tile with D columns into LDS (kRowBytes layout) by 256 threads;
+// DMA of a 64-row tile with D columns into LDS (kRowBytes layout) by NT threads;
 // row_src(r) gives the global address of row r's first element.
-template <int D, typename RowSrc>
+template <int D, int NT = 256, typename RowSrc>
 __device__ __forceinline__ void dma_rows(char* lds, RowSrc row_src, int tid, int wave) {
   constexpr int RB = kRowBytes<D>, CH = RB / 16, VC = D / 8;
-  constexpr int N = 64 * CH / 256;
+  constexpr int N = 64 * CH / NT;
   const uint32_t base = lds_addr(lds) + (uint32_t)wave * 64 * 16;
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    const int s = i * 256 + tid;
+    const int s = i * NT + tid;
     const int r = s / CH;
     int c = (s % CH) ^ bwd_swz<RB>(r);
     if (c >= VC) c = 0;  // row padding: any in-bounds source
-    dma16(row_src(r) + c * 16, base + i * 256 * 16);
+    dma16(row_src(r) + c * 16, base + i * NT * 16);
   }
 }
 
@@ -166,7 +168,8 @@ __device__ __forceinline__ void dma_rows(char* lds, RowSrc row_src, int tid, int
 //   S = Q K^T, dP = dO V^T (A = rows from LDS, B = K / V from registers),
 //   P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - Delta),
 //   dV^T += dO^T P, dK^T += Q^T dS (A = transposing reads, B = P / dS in place).
-// Each rank-major key row is written once: no atomics, deterministic.
+// Each rank-major key row is written once: no atomics, deterministic.  Used for
+// Q/K head dimensions above 128; narrower heads use dkdv_pair_kernel below.
 // ---------------------------------------------------------------------------
 template <int DQK>
 constexpr int kDkvStages = DQK > 128 ? 3 : 4;
@@ -195,12 +198,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
   __shared__ __attribute__((aligned(16))) float sL[NS][BQ];
   __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
   __shared__ __attribute__((aligned(16))) int32_t sIv[NS][BQ * 4];
-  // Partial tiles: each wave first turns the tile's row intervals into one word of
-  // key bits per query, then every element tests a bit (for the widest Q/K
-  // head dimension the registers are short and the intervals are tested per
-  // element instead).
-  constexpr bool kKeyBits = DQK <= 128;
-  __shared__ __attribute__((aligned(16))) uint32_t sMask[4][BQ];  // per wave: visible keys of each query
   __shared__ __attribute__((aligned(16))) int32_t sSpan[kDkvMaxSpans * 4];
 
   const int tid = threadIdx.x;
@@ -338,17 +335,6 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
     const bool isB = (cC.seg & 1) != 0;
     const int q_rem = (isB ? qlenB : qlenA) - cC.qt * BQ;  // valid rows of this tile
     const bool partial = cC.partial != 0;
-    if (kKeyBits && partial) {
-      // lane q: bit kk set when query q of the tile sees key k0 + 32*wave + kk
-      const int4 iv = *(const int4*)(sIv[slot] + 4 * lane);
-      const int kb = k0 + wave * 32;
-      const uint32_t m = lane < q_rem ? key_bits(iv.x - kb, iv.y - kb) | key_bits(iv.z - kb, iv.w - kb) : 0u;
-      sMask[wave][lane] = m;
-      // read back by the same wave only: LDS operations of one wave run in order
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
 #pragma unroll
     for (int qs = 0; qs < BQ / 32; ++qs) {
       // S[q][key] and dP[q][key] for 32 queries x this wave's 32 keys
@@ -365,15 +351,12 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
         const int i0 = r >> 2;
         const f32x4_t lv = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i0 + 4 * half);
         const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * i0 + 4 * half);
-        u32x2_t mq = {~0u, ~0u};  // key bits of the pair's two queries
-        if (kKeyBits && partial) mq = *(const u32x2_t*)(sMask[wave] + qs * 32 + 8 * i0 + 4 * half + (r & 3));
         float pv[2], dsv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int j = (r + u) & 3;
           float x = fmaf(s[r + u], sl2, -lv[j]);
-          if (kKeyBits && partial) x = ((mq[u] >> col) & 1u) ? x : -INFINITY;
-          if (!kKeyBits && partial) {  // the interval test per element (fewer registers)
+          if (partial) {
             const int q = qs * 32 + 8 * i0 + 4 * half + j;
             const int4 iv = *(const int4*)(sIv[slot] + 4 * q);
             const bool vis = (q < q_rem) & (((kpos >= iv.x) & (kpos < iv.y)) | ((kpos >= iv.z) & (kpos < iv.w)));
@@ -434,6 +417,311 @@ __global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
                                          pack2<E>(dv[d][4 * i + 2], dv[d][4 * i + 3])};
       }
   }
+}
+
+// ---------------------------------------------------------------------------
+// dK / dV with paired waves (Q/K head dimension up to 128).  The same work item
+// and Q-tile stream as dkdv_kernel, run by 8 waves: waves w and w+4 (one SIMD)
+// own the same 32 keys.  Wave w (the P wave) computes S = Q K^T and
+// P = exp2(S*scale*log2e - LSE*log2e), hands P to its partner through LDS and
+// accumulates dV^T += dO^T P; wave w+4 (the dS wave) computes dP = dO V^T,
+// dS = P (dP - Delta) and accumulates dK^T += Q^T dS.  Each tile runs in two
+// phases separated by a barrier -- (S, P | dP) then (dV | dS, dK) -- so that on
+// every SIMD one wave's vector work overlaps the other's MFMAs, and each wave
+// keeps one operand set and one accumulator set in registers.
+// ---------------------------------------------------------------------------
+template <typename E, int DQK, int DV>
+__global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P) {
+  constexpr int NT = 2 * kThreads;
+  constexpr int BQ = 64;           // queries per Q tile
+  constexpr int QS = DQK / 16;     // reduction steps over Dqk
+  constexpr int VS = DV / 16;      // reduction steps over Dv
+  constexpr int NS = kDkvStages<DQK>;
+  using QO = TileOffsets<DQK>;
+  using OO = TileOffsets<DV>;
+  constexpr int QB = BQ * QO::RB, OB = BQ * OO::RB;
+  constexpr int QN = 64 * (QO::RB / 16) / NT, ON = 64 * (OO::RB / 16) / NT;
+  constexpr int NA = (DQK > DV ? DQK : DV) / 32;
+  __shared__ __attribute__((aligned(16))) char sQ[NS][QB];
+  __shared__ __attribute__((aligned(16))) char sO[NS][OB];
+  __shared__ __attribute__((aligned(16))) float sL[NS][BQ];
+  __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
+  __shared__ __attribute__((aligned(16))) int32_t sIv[NS][BQ * 4];
+  __shared__ __attribute__((aligned(16))) uint32_t sMask[4][BQ];          // per P wave: visible keys of each query
+  __shared__ __attribute__((aligned(16))) u32x4_t sP[4][BQ / 32][2][64];  // packed P, in the MFMA operand layout
+  __shared__ __attribute__((aligned(16))) int32_t sSpan[kDkvMaxSpans * 4];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const bool dswave = wave >= 4;  // dP, dS, dK (else S, P, dV)
+  const int kgrp = wave & 3;      // the wave's 32 keys
+
+  const int tile = blockIdx.x / P.hkv;
+  const int kvh = blockIdx.x % P.hkv;
+  const int32_t* tr = P.t.kv_tiles + tile * 5;
+  const int seq = tr[0], k0 = tr[1], keys = tr[2], span0 = tr[3], nspan = tr[4];
+  const int32_t* segA = P.t.segs + (2 * seq) * 8;
+  const int32_t* segB = P.t.segs + (2 * seq + 1) * 8;
+  const int qlenA = segA[2], row0A = segA[4], qlenB = segB[2], row0B = segB[4];
+  const int32_t* kvi = P.t.kv_index + segB[5];
+  const int kl = kgrp * 32 + col;
+  const int kpos = k0 + kl;
+  const bool kvalid = kl < keys;
+  const int64_t grow = kvalid ? (int64_t)kvi[kpos] : 0;
+
+  // B operands in registers: K^T for the P wave, V^T for the dS wave; lane holds
+  // row[key][16s + 8*half .. +7]
+  constexpr int FS = QS > VS ? QS : VS;
+  typename E::vec8 frag[FS];
+  {
+    const uint16_t* src = dswave ? (const uint16_t*)P.v + (grow * P.hkv + kvh) * DV + 8 * half
+                                 : (const uint16_t*)P.k + (grow * P.hkv + kvh) * DQK + 8 * half;
+    const int nst = dswave ? VS : QS;
+#pragma unroll
+    for (int st = 0; st < FS; ++st) {
+      u32x4_t x = {0u, 0u, 0u, 0u};
+      if (kvalid && st < nst) x = *(const u32x4_t*)(src + 16 * st);
+      frag[st] = as_vec8<E>(x);
+    }
+  }
+  if (tid < 4 * nspan) sSpan[tid] = P.t.kv_spans[span0 * 4 + tid];
+  wait_vmem_all();
+  __syncthreads();
+
+  struct Cur {
+    int hh, sp, qt, qt_end, seg, partial;
+  };
+  auto span_at = [&](Cur c, int sp) {
+    const int4 r = *(const int4*)(sSpan + 4 * sp);
+    c.sp = sp;
+    c.seg = __builtin_amdgcn_readfirstlane(r.x);
+    c.qt = __builtin_amdgcn_readfirstlane(r.y);
+    c.qt_end = __builtin_amdgcn_readfirstlane(r.z);
+    c.partial = __builtin_amdgcn_readfirstlane(r.w);
+    return c;
+  };
+  auto advance = [&](Cur c) {
+    if (++c.qt >= c.qt_end) {
+      int sp = c.sp + 1;
+      if (sp >= nspan) {
+        sp = 0;
+        ++c.hh;
+      }
+      c = span_at(c, sp);
+    }
+    return c;
+  };
+  int n_tiles = 0;
+  for (int sp = 0; sp < nspan; ++sp) {
+    Cur c = span_at(Cur{0, 0, 0, 0, 0, 0}, sp);
+    n_tiles += c.qt_end - c.qt;
+  }
+  n_tiles *= P.group;
+
+  const char* qgb = (const char*)P.q;
+  const char* ogb = (const char*)P.dout;
+  const int per_batch = QN + ON + (wave < 3 ? 1 : 0);
+  auto issue = [&](const Cur& c, int m) {
+    const int slot = m % NS;
+    const int head = kvh * P.group + c.hh;
+    const bool isB = (c.seg & 1) != 0;
+    const int q_len = isB ? qlenB : qlenA, q_row0 = isB ? row0B : row0A;
+    const int a0 = c.qt * BQ;
+    auto lrow = [&](int r) { return q_row0 + min(a0 + r, q_len - 1); };
+    dma_rows<DQK, NT>(sQ[slot], [&](int r) { return qgb + ((int64_t)lrow(r) * P.hq + head) * (DQK * 2); }, tid, wave);
+    dma_rows<DV, NT>(sO[slot], [&](int r) { return ogb + ((int64_t)lrow(r) * P.hq + head) * (DV * 2); }, tid, wave);
+    if (wave == 0)
+      dma4(P.lse2 + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
+    else if (wave == 1)
+      dma4(P.delta + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sD[slot]));
+    else if (wave == 2)
+      dma16(P.t.row_iv + (int64_t)lrow(lane) * 4, lds_addr(sIv[slot]));
+  };
+  auto wait_for = [&](int m) {
+    const int later = min(m + NS - 1, n_tiles) - (m + 1);
+    wait_vmem_le(later > 0 ? later * per_batch : 0);
+  };
+
+  QO qo;
+  OO oo;
+  qo.init(lane);
+  oo.init(lane);
+
+  const float sl2 = P.scale_log2;
+
+  Cur cI0 = span_at(Cur{0, 0, 0, 0, 0, 0}, 0);
+  for (int m = 0; m < NS - 1 && m < n_tiles; ++m) {
+    issue(cI0, m);
+    cI0 = advance(cI0);
+  }
+  wait_for(0);
+  __syncthreads();
+
+  // The tile loop is instantiated once per role, so that each role keeps its
+  // accumulators in registers of its own across iterations.
+  auto run = [&](auto role_c) {
+  constexpr bool DSW = decltype(role_c)::value;
+  f32x16_t acc[NA];  // dV^T (P wave) or dK^T (dS wave): lane holds d = 32*blk + 8i + 4*half + j
+#pragma unroll
+  for (int d = 0; d < NA; ++d) acc[d] = zero16();
+  Cur cI = cI0;
+  Cur cC = span_at(Cur{0, 0, 0, 0, 0, 0}, 0);
+  for (int n = 0; n < n_tiles; ++n) {
+    if (n + NS - 1 < n_tiles) {
+      issue(cI, n + NS - 1);  // into the slot tile n-1 used
+      cI = advance(cI);
+    }
+    const int slot = n % NS;
+    const char* q_s = sQ[slot];
+    const char* o_s = sO[slot];
+    const bool isB = (cC.seg & 1) != 0;
+    const int q_rem = (isB ? qlenB : qlenA) - cC.qt * BQ;  // valid rows of this tile
+    if constexpr (!DSW) {
+      // ---- P wave: S, P (phase 1); dV (phase 2) ----
+      uint32_t pk[BQ / 32][2][4];
+      auto phase1 = [&](auto part_c) {
+        constexpr bool PART = decltype(part_c)::value;
+        if constexpr (PART) {
+          // lane q: bit kk set when query q of the tile sees key k0 + 32*kgrp + kk
+          const int4 iv = *(const int4*)(sIv[slot] + 4 * lane);
+          const int kb = k0 + kgrp * 32;
+          const uint32_t m = lane < q_rem ? key_bits(iv.x - kb, iv.y - kb) | key_bits(iv.z - kb, iv.w - kb) : 0u;
+          sMask[kgrp][lane] = m;
+          // read back by the same wave only: LDS operations of one wave run in order
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
+        // S of both query halves first, ahead of the partner's dP MFMAs, so that
+        // the exponentials below overlap them
+        f32x16_t sc[BQ / 32];
+        __builtin_amdgcn_s_setprio(2);
+#pragma unroll
+        for (int qs = 0; qs < BQ / 32; ++qs) {
+          sc[qs] = zero16();
+#pragma unroll
+          for (int st = 0; st < QS; ++st) sc[qs] = E::mfma32(as_vec8<E>(qo.row(q_s, qs, st)), frag[st], sc[qs]);
+        }
+        __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+        for (int qs = 0; qs < BQ / 32; ++qs) {
+          // lane holds query qs*32 + 8i + 4*half + j (r = 4i + j) for its key
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const int i0 = r >> 2;
+            const f32x4_t lv = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i0 + 4 * half);
+            u32x2_t mq = {~0u, ~0u};
+            if constexpr (PART) mq = *(const u32x2_t*)(sMask[kgrp] + qs * 32 + 8 * i0 + 4 * half + (r & 3));
+            float pv[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+              float x = fmaf(sc[qs][r + u], sl2, -lv[(r + u) & 3]);
+              if constexpr (PART) x = ((mq[u] >> col) & 1u) ? x : -INFINITY;
+              pv[u] = __builtin_amdgcn_exp2f(x);
+            }
+            pk[qs][r >> 3][(r & 7) >> 1] = pack2<E>(pv[0], pv[1]);
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            sP[kgrp][qs][st][lane] = u32x4_t{pk[qs][st][0], pk[qs][st][1], pk[qs][st][2], pk[qs][st][3]};
+        }
+      };
+      if (cC.partial) phase1(std::true_type{});
+      else phase1(std::false_type{});
+      __syncthreads();  // P is in LDS
+#pragma unroll
+      for (int qs = 0; qs < BQ / 32; ++qs)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int rows0 = qs * 32 + st * 16;
+          const typename E::vec8 bp = as_vec8<E>(u32x4_t{pk[qs][st][0], pk[qs][st][1], pk[qs][st][2], pk[qs][st][3]});
+          u32x2_t ta[DV / 32][2];
+#pragma unroll
+          for (int d = 0; d < DV / 32; ++d) {
+            ta[d][0] = oo.trans(o_s, rows0, 0, d);
+            ta[d][1] = oo.trans(o_s, rows0, 1, d);
+          }
+#pragma unroll
+          for (int d = 0; d < DV / 32; ++d)
+            acc[d] = E::mfma32(as_vec8<E>(u32x4_t{ta[d][0][0], ta[d][0][1], ta[d][1][0], ta[d][1][1]}), bp, acc[d]);
+        }
+    } else {
+      // ---- dS wave: dP (phase 1); dS, dK (phase 2) ----
+      f32x16_t dp[BQ / 32];
+#pragma unroll
+      for (int qs = 0; qs < BQ / 32; ++qs) {
+        dp[qs] = zero16();
+#pragma unroll
+        for (int st = 0; st < VS; ++st) dp[qs] = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), frag[st], dp[qs]);
+      }
+      __syncthreads();  // P is in LDS
+#pragma unroll
+      for (int qs = 0; qs < BQ / 32; ++qs) {
+        uint32_t pd[2][4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const u32x4_t pw = sP[kgrp][qs][st][lane];
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int r = 8 * st + 2 * w;  // elements r, r+1: queries 8i + 4*half + j, r = 4i + j
+            const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * (r >> 2) + 4 * half);
+            const float p0 = E::to_float((uint16_t)(pw[w] & 0xFFFFu));
+            const float p1 = E::to_float((uint16_t)(pw[w] >> 16));
+            pd[st][w] = pack2<E>(p0 * (dp[qs][r] - dv4[r & 3]), p1 * (dp[qs][r + 1] - dv4[(r + 1) & 3]));
+          }
+        }
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int rows0 = qs * 32 + st * 16;
+          const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
+          u32x2_t ta[DQK / 32][2];
+#pragma unroll
+          for (int d = 0; d < DQK / 32; ++d) {
+            ta[d][0] = qo.trans(q_s, rows0, 0, d);
+            ta[d][1] = qo.trans(q_s, rows0, 1, d);
+          }
+#pragma unroll
+          for (int d = 0; d < DQK / 32; ++d)
+            acc[d] = E::mfma32(as_vec8<E>(u32x4_t{ta[d][0][0], ta[d][0][1], ta[d][1][0], ta[d][1][1]}), bd, acc[d]);
+        }
+      }
+    }
+    cC = advance(cC);
+    if (n + 1 < n_tiles) wait_for(n + 1);
+    __syncthreads();
+  }
+  wait_vmem_all();
+
+  // ---- write this lane's key row of dV (P wave) or dK (dS wave) ----
+  if (kvalid) {
+    if constexpr (DSW) {
+      uint16_t* dkr = (uint16_t*)P.dk + (grow * P.hkv + kvh) * DQK;
+      const float sc = P.scale;
+#pragma unroll
+      for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dd = d * 32 + 8 * i + 4 * half;
+          *(u32x2_t*)(dkr + dd) = u32x2_t{pack2<E>(acc[d][4 * i] * sc, acc[d][4 * i + 1] * sc),
+                                           pack2<E>(acc[d][4 * i + 2] * sc, acc[d][4 * i + 3] * sc)};
+        }
+    } else {
+      uint16_t* dvr = (uint16_t*)P.dv + (grow * P.hkv + kvh) * DV;
+#pragma unroll
+      for (int d = 0; d < DV / 32; ++d)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int dd = d * 32 + 8 * i + 4 * half;
+          *(u32x2_t*)(dvr + dd) = u32x2_t{pack2<E>(acc[d][4 * i], acc[d][4 * i + 1]),
+                                           pack2<E>(acc[d][4 * i + 2], acc[d][4 * i + 3])};
+        }
+    }
+  }
+  };
+  if (dswave) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -678,17 +966,20 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
 template <typename E, int DQK, int DV>
 hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
   hipError_t e = hipSuccess;
-  auto launch = [&](int id, auto kernel, unsigned grid) {
+  auto launch = [&](int id, auto kernel, unsigned grid, unsigned threads = kThreads) {
     if (e != hipSuccess || grid == 0) return;
     if (hook) hook->before(id, s);
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(threads), 0, s, p);
     if (hook) hook->after(id, s);
     e = hipGetLastError();
   };
   const int64_t n_pre = (int64_t)p.t_loc * p.hq;
   launch(K_BWD_PRE, bwd_pre_kernel<E, DV>, (unsigned)((n_pre + kThreads - 1) / kThreads));
   launch(K_BWD_ZERO, zero_rows_kernel<DQK, DV>, (unsigned)p.n_zero_ranges);
-  launch(K_BWD_DKDV, dkdv_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv);
+  if constexpr (DQK <= 128)
+    launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
+  else
+    launch(K_BWD_DKDV, dkdv_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv);
   launch(K_BWD_DQ, dq_kernel<E, DQK, DV>, (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups);
   return e;
 }
