@@ -440,7 +440,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
   using QO = TileOffsets<DQK>;
   using OO = TileOffsets<DV>;
   constexpr int QB = BQ * QO::RB, OB = BQ * OO::RB;
-  constexpr int QN = 64 * (QO::RB / 16) / NT, ON = 64 * (OO::RB / 16) / NT;
+  constexpr int QN = 64 * (QO::RB / 16) / kThreads, ON = 64 * (OO::RB / 16) / kThreads;
   constexpr int NA = (DQK > DV ? DQK : DV) / 32;
   __shared__ __attribute__((aligned(16))) char sQ[NS][QB];
   __shared__ __attribute__((aligned(16))) char sO[NS][OB];
@@ -490,23 +490,27 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
   wait_vmem_all();
   __syncthreads();
 
+  // Q tiles are walked from the last one back (per head of the group): under the
+  // causal masks every work-group's range ends at the same place, so the
+  // work-groups running together on one XCD stream the same tiles at about the
+  // same time and share them in L2.
   struct Cur {
-    int hh, sp, qt, qt_end, seg, partial;
+    int hh, sp, qt, qt_lo, seg, partial;
   };
-  auto span_at = [&](Cur c, int sp) {
+  auto span_at = [&](Cur c, int sp) {  // the span's last tile
     const int4 r = *(const int4*)(sSpan + 4 * sp);
     c.sp = sp;
     c.seg = __builtin_amdgcn_readfirstlane(r.x);
-    c.qt = __builtin_amdgcn_readfirstlane(r.y);
-    c.qt_end = __builtin_amdgcn_readfirstlane(r.z);
+    c.qt_lo = __builtin_amdgcn_readfirstlane(r.y);
+    c.qt = __builtin_amdgcn_readfirstlane(r.z) - 1;
     c.partial = __builtin_amdgcn_readfirstlane(r.w);
     return c;
   };
   auto advance = [&](Cur c) {
-    if (++c.qt >= c.qt_end) {
-      int sp = c.sp + 1;
-      if (sp >= nspan) {
-        sp = 0;
+    if (--c.qt < c.qt_lo) {
+      int sp = c.sp - 1;
+      if (sp < 0) {
+        sp = nspan - 1;
         ++c.hh;
       }
       c = span_at(c, sp);
@@ -516,13 +520,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
   int n_tiles = 0;
   for (int sp = 0; sp < nspan; ++sp) {
     Cur c = span_at(Cur{0, 0, 0, 0, 0, 0}, sp);
-    n_tiles += c.qt_end - c.qt;
+    n_tiles += c.qt + 1 - c.qt_lo;
   }
   n_tiles *= P.group;
+  const int sp_last = nspan > 0 ? nspan - 1 : 0;
 
+  // Tile loads are issued where each role has slack: the P waves load Q and the
+  // LSE at the end of their dV step, the dS waves load dO, Delta and the row
+  // intervals after their dP MFMAs.
   const char* qgb = (const char*)P.q;
   const char* ogb = (const char*)P.dout;
-  const int per_batch = QN + ON + (wave < 3 ? 1 : 0);
+  const int per_batch = dswave ? ON + (kgrp < 2 ? 1 : 0) : QN + (kgrp == 0 ? 1 : 0);
   auto issue = [&](const Cur& c, int m) {
     const int slot = m % NS;
     const int head = kvh * P.group + c.hh;
@@ -530,14 +538,19 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
     const int q_len = isB ? qlenB : qlenA, q_row0 = isB ? row0B : row0A;
     const int a0 = c.qt * BQ;
     auto lrow = [&](int r) { return q_row0 + min(a0 + r, q_len - 1); };
-    dma_rows<DQK, NT>(sQ[slot], [&](int r) { return qgb + ((int64_t)lrow(r) * P.hq + head) * (DQK * 2); }, tid, wave);
-    dma_rows<DV, NT>(sO[slot], [&](int r) { return ogb + ((int64_t)lrow(r) * P.hq + head) * (DV * 2); }, tid, wave);
-    if (wave == 0)
-      dma4(P.lse2 + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
-    else if (wave == 1)
-      dma4(P.delta + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sD[slot]));
-    else if (wave == 2)
-      dma16(P.t.row_iv + (int64_t)lrow(lane) * 4, lds_addr(sIv[slot]));
+    const int rtid = tid & (kThreads - 1);
+    if (!dswave) {
+      dma_rows<DQK, kThreads>(sQ[slot], [&](int r) { return qgb + ((int64_t)lrow(r) * P.hq + head) * (DQK * 2); },
+                              rtid, kgrp);
+      if (kgrp == 0) dma4(P.lse2 + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
+    } else {
+      dma_rows<DV, kThreads>(sO[slot], [&](int r) { return ogb + ((int64_t)lrow(r) * P.hq + head) * (DV * 2); },
+                             rtid, kgrp);
+      if (kgrp == 0)
+        dma4(P.delta + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sD[slot]));
+      else if (kgrp == 1)
+        dma16(P.t.row_iv + (int64_t)lrow(lane) * 4, lds_addr(sIv[slot]));
+    }
   };
   auto wait_for = [&](int m) {
     const int later = min(m + NS - 1, n_tiles) - (m + 1);
@@ -551,7 +564,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
 
   const float sl2 = P.scale_log2;
 
-  Cur cI0 = span_at(Cur{0, 0, 0, 0, 0, 0}, 0);
+  Cur cI0 = span_at(Cur{0, 0, 0, 0, 0, 0}, sp_last);
   for (int m = 0; m < NS - 1 && m < n_tiles; ++m) {
     issue(cI0, m);
     cI0 = advance(cI0);
@@ -567,12 +580,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
 #pragma unroll
   for (int d = 0; d < NA; ++d) acc[d] = zero16();
   Cur cI = cI0;
-  Cur cC = span_at(Cur{0, 0, 0, 0, 0, 0}, 0);
+  Cur cC = span_at(Cur{0, 0, 0, 0, 0, 0}, sp_last);
   for (int n = 0; n < n_tiles; ++n) {
-    if (n + NS - 1 < n_tiles) {
-      issue(cI, n + NS - 1);  // into the slot tile n-1 used
-      cI = advance(cI);
-    }
     const int slot = n % NS;
     const char* q_s = sQ[slot];
     const char* o_s = sO[slot];
@@ -596,14 +605,15 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
         }
         // S of both query halves first, ahead of the partner's dP MFMAs, so that
         // the exponentials below overlap them
+        // (the two query halves' chains alternate, so that consecutive MFMAs are independent)
         f32x16_t sc[BQ / 32];
         __builtin_amdgcn_s_setprio(2);
 #pragma unroll
-        for (int qs = 0; qs < BQ / 32; ++qs) {
-          sc[qs] = zero16();
+        for (int qs = 0; qs < BQ / 32; ++qs) sc[qs] = zero16();
 #pragma unroll
-          for (int st = 0; st < QS; ++st) sc[qs] = E::mfma32(as_vec8<E>(qo.row(q_s, qs, st)), frag[st], sc[qs]);
-        }
+        for (int st = 0; st < QS; ++st)
+#pragma unroll
+          for (int qs = 0; qs < BQ / 32; ++qs) sc[qs] = E::mfma32(as_vec8<E>(qo.row(q_s, qs, st)), frag[st], sc[qs]);
         __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int qs = 0; qs < BQ / 32; ++qs) {
@@ -647,15 +657,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
           for (int d = 0; d < DV / 32; ++d)
             acc[d] = E::mfma32(as_vec8<E>(u32x4_t{ta[d][0][0], ta[d][0][1], ta[d][1][0], ta[d][1][1]}), bp, acc[d]);
         }
+      if (n + NS - 1 < n_tiles) issue(cI, n + NS - 1);  // into the slot tile n-1 used
     } else {
       // ---- dS wave: dP (phase 1); dS, dK (phase 2) ----
+      // the two query halves' chains alternate, so that consecutive MFMAs are independent
       f32x16_t dp[BQ / 32];
 #pragma unroll
-      for (int qs = 0; qs < BQ / 32; ++qs) {
-        dp[qs] = zero16();
+      for (int qs = 0; qs < BQ / 32; ++qs) dp[qs] = zero16();
 #pragma unroll
-        for (int st = 0; st < VS; ++st) dp[qs] = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), frag[st], dp[qs]);
-      }
+      for (int st = 0; st < VS; ++st)
+#pragma unroll
+        for (int qs = 0; qs < BQ / 32; ++qs) dp[qs] = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), frag[st], dp[qs]);
+      if (n + NS - 1 < n_tiles) issue(cI, n + NS - 1);  // into the slot tile n-1 used
       __syncthreads();  // P is in LDS
 #pragma unroll
       for (int qs = 0; qs < BQ / 32; ++qs) {
@@ -688,6 +701,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
         }
       }
     }
+    if (n + NS - 1 < n_tiles) cI = advance(cI);
     cC = advance(cC);
     if (n + 1 < n_tiles) wait_for(n + 1);
     __syncthreads();
