@@ -921,11 +921,13 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
     const bool partial = cC.partial != 0;
 #pragma unroll
     for (int nb = 0; nb < BN / 32; ++nb) {
+      // the S and dP chains alternate, so that consecutive MFMAs are independent
       f32x16_t s = zero16(), dp = zero16();
 #pragma unroll
-      for (int st = 0; st < QS; ++st) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
-#pragma unroll
-      for (int st = 0; st < VS; ++st) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
+      for (int st = 0; st < (QS > VS ? QS : VS); ++st) {
+        if (st < QS) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
+        if (st < VS) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
+      }
       // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
       uint32_t pd[2][4];
 #pragma unroll
