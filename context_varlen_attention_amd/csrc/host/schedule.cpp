@@ -20,8 +20,11 @@
 // time order) so that long causal rows do not trail at the end of a launch.
 #include <algorithm>
 #include <array>
+#include <atomic>
 #include <cstring>
+#include <new>
 #include <numeric>
+#include <thread>
 
 #include "plan.hpp"
 
@@ -139,7 +142,127 @@ void tile_sets(const Plan& p, int seg, int32_t a0, int32_t a1, Scratch& w) {
   }
 }
 
-void build_q_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_kv) {
+// Runs f(i) for i in [0, n) on up to kPlanThreads host threads when the batch is
+// large (rows >= kPlanParallelRows), else inline; every i writes only its own
+// outputs, so the result does not depend on the thread count.
+constexpr int32_t kPlanThreads = 8;
+constexpr int64_t kPlanParallelRows = 32768;
+template <typename Fn>
+void parallel_for(int32_t n, int64_t rows, Fn f) {
+  const int32_t hw = (int32_t)std::max(1u, std::thread::hardware_concurrency());
+  const int32_t nt = rows >= kPlanParallelRows ? std::min({hw, kPlanThreads, n}) : 1;
+  if (nt <= 1) {
+    for (int32_t i = 0; i < n; ++i) f(i);
+    return;
+  }
+  std::atomic<int32_t> next{0};
+  std::atomic<bool> failed{false};
+  std::vector<std::thread> th;
+  th.reserve(nt);
+  for (int32_t t = 0; t < nt; ++t)
+    th.emplace_back([&]() {
+      try {
+        for (int32_t i = next++; i < n && !failed; i = next++) f(i);
+      } catch (...) {  // out of memory in a worker: reported by the caller's thread
+        failed = true;
+      }
+    });
+  for (auto& x : th) x.join();
+  if (failed) throw std::bad_alloc();
+}
+
+// Intersection of two sorted disjoint interval lists, into F.
+void intersect_lists(IvList& F, const Iv* g, int32_t ng, IvList& tmp) {
+  tmp.clear();
+  size_t i = 0;
+  int32_t j = 0;
+  while (i < F.size() && j < ng) {
+    const int32_t lo = std::max(F[i].first, g[j].first);
+    const int32_t hi = std::min(F[i].second, g[j].second);
+    if (hi > lo) tmp.push_back({lo, hi});
+    if (F[i].second < g[j].second) ++i; else ++j;
+  }
+  F.swap(tmp);
+}
+
+// Union and intersection of the visible sets of every kBlockRows-row block of
+// every segment, computed once; the sets of a Q tile (a whole number of blocks
+// from the segment's start) are then merged from its blocks instead of being
+// recomputed row by row for each schedule.
+constexpr int32_t kBlockRows = 32;
+struct BlockSets {
+  std::vector<int32_t> seg_block0;  // [nseg + 1] first block of each segment
+  std::vector<int32_t> u_off, f_off;  // [nblocks + 1] offsets into U / F
+  IvList U, F;
+  void build(const Plan& p) {
+    const int32_t nseg = (int32_t)(p.segs.size() / SEG_INTS);
+    seg_block0.assign(nseg + 1, 0);
+    std::vector<std::pair<int32_t, int32_t>> blocks;  // (segment, first row)
+    for (int32_t sg = 0; sg < nseg; ++sg) {
+      const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
+      for (int32_t a0 = 0; a0 < q_len; a0 += kBlockRows) blocks.push_back({sg, a0});
+      seg_block0[sg + 1] = (int32_t)blocks.size();
+    }
+    // chunks of blocks (in parallel for large batches), concatenated in order
+    constexpr int32_t kChunk = 64;
+    const int32_t nb = (int32_t)blocks.size(), nchunk = (nb + kChunk - 1) / kChunk;
+    struct Part {
+      IvList U, F;
+      std::vector<int32_t> un, fn;  // intervals per block
+    };
+    std::vector<Part> parts(nchunk);
+    parallel_for(nchunk, p.T_loc, [&](int32_t c) {
+      Part& pt = parts[c];
+      Scratch w;
+      for (int32_t b = c * kChunk; b < std::min(nb, (c + 1) * kChunk); ++b) {
+        const int32_t sg = blocks[b].first, a0 = blocks[b].second;
+        const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
+        tile_sets(p, sg, a0, std::min(q_len, a0 + kBlockRows), w);
+        pt.U.insert(pt.U.end(), w.U.begin(), w.U.end());
+        pt.F.insert(pt.F.end(), w.F.begin(), w.F.end());
+        pt.un.push_back((int32_t)w.U.size());
+        pt.fn.push_back((int32_t)w.F.size());
+      }
+    });
+    u_off.assign(1, 0);
+    f_off.assign(1, 0);
+    U.clear();
+    F.clear();
+    for (const Part& pt : parts) {
+      U.insert(U.end(), pt.U.begin(), pt.U.end());
+      F.insert(F.end(), pt.F.begin(), pt.F.end());
+      for (size_t b = 0; b < pt.un.size(); ++b) {
+        u_off.push_back(u_off.back() + pt.un[b]);
+        f_off.push_back(f_off.back() + pt.fn[b]);
+      }
+    }
+  }
+  // w.U / w.F of rows [a0, a1) of segment sg (a0 a multiple of kBlockRows)
+  void tile(int32_t sg, int32_t a0, int32_t a1, Scratch& w) const {
+    const int32_t b0 = seg_block0[sg] + a0 / kBlockRows;
+    const int32_t b1 = seg_block0[sg] + (a1 + kBlockRows - 1) / kBlockRows;
+    w.all.clear();
+    bool monotone = true;
+    for (int32_t b = b0; b < b1; ++b)
+      for (int32_t k = u_off[b]; k < u_off[b + 1]; ++k) {
+        if (!w.all.empty() && U[k].first < w.all.back().first) monotone = false;
+        w.all.push_back(U[k]);
+      }
+    if (!monotone) std::sort(w.all.begin(), w.all.end());
+    w.U.clear();
+    for (const Iv& x : w.all) {
+      if (!w.U.empty() && x.first <= w.U.back().second)
+        w.U.back().second = std::max(w.U.back().second, x.second);
+      else
+        w.U.push_back(x);
+    }
+    w.F.assign(F.begin() + f_off[b0], F.begin() + f_off[b0 + 1]);
+    for (int32_t b = b0 + 1; b < b1 && !w.F.empty(); ++b)
+      intersect_lists(w.F, F.data() + f_off[b], f_off[b + 1] - f_off[b], w.tmp);
+  }
+};
+
+void build_q_schedule(const Plan& p, const BlockSets& bs, Schedule& s, int32_t tile_q, int32_t tile_kv) {
   s.tile_q = tile_q;
   s.tile_kv = tile_kv;
   s.tiles.clear();
@@ -154,7 +277,7 @@ void build_q_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_k
     const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
     for (int32_t a0 = 0; a0 < q_len; a0 += tile_q) {
       const int32_t a1 = std::min(q_len, a0 + tile_q);
-      tile_sets(p, sg, a0, a1, w);
+      bs.tile(sg, a0, a1, w);
       tile_spans(w, tile_kv);
       Rec r{sg, a0, a1 - a0, (int32_t)all_spans.size(), (int32_t)w.spans.size(), 0};
       for (const SpanOut& x : w.spans) r.cost += x.t1 - x.t0;
@@ -181,7 +304,7 @@ void build_q_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_k
 
 // K/V-stationary schedule: for every K/V tile of every sub-sequence (up to the
 // longest prefix of its two segments), the Q tiles of both segments that see it.
-void build_kv_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_kv) {
+void build_kv_schedule(const Plan& p, const BlockSets& bs, Schedule& s, int32_t tile_q, int32_t tile_kv) {
   s.tile_q = tile_q;
   s.tile_kv = tile_kv;
   s.tiles.clear();
@@ -206,7 +329,7 @@ void build_kv_schedule(const Plan& p, Schedule& s, int32_t tile_q, int32_t tile_
     for (int32_t sg : {segA, segB}) {
       const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
       for (int32_t a0 = 0, qt = 0; a0 < q_len; a0 += tile_q, ++qt) {
-        tile_sets(p, sg, a0, std::min(q_len, a0 + tile_q), w);
+        bs.tile(sg, a0, std::min(q_len, a0 + tile_q), w);
         tile_spans(w, tile_kv);
         // a Q tile that runs past the segment's end takes the element-wise
         // path, which also masks the rows past the end
@@ -316,21 +439,31 @@ cva_status build_schedules(Plan& p) {
   // per-row visible intervals and the useful pair count
   const int32_t nseg = (int32_t)(p.segs.size() / SEG_INTS);
   p.row_iv.assign((size_t)p.T_loc * 4, 0);
-  p.visible_pairs = 0;
+  // rows in chunks of 4096 (in parallel for large batches)
+  std::vector<std::array<int32_t, 3>> chunks;  // (segment, first row, end row)
   for (int32_t sg = 0; sg < nseg; ++sg) {
     const int32_t q_len = p.segs[sg * SEG_INTS + SEG_QLEN];
+    for (int32_t a0 = 0; a0 < q_len; a0 += 4096) chunks.push_back({sg, a0, std::min(q_len, a0 + 4096)});
+  }
+  std::vector<int64_t> chunk_pairs(chunks.size(), 0);
+  parallel_for((int32_t)chunks.size(), p.T_loc, [&](int32_t c) {
+    const int32_t sg = chunks[c][0];
     const int32_t row0 = p.segs[sg * SEG_INTS + SEG_QROW0];
-    for (int32_t a = 0; a < q_len; ++a) {
+    int64_t pairs = 0;
+    for (int32_t a = chunks[c][1]; a < chunks[c][2]; ++a) {
       int32_t* iv = &p.row_iv[(size_t)(row0 + a) * 4];
       row_intervals(p, sg, a, iv);
       const RowSet rs = row_set(iv);
-      for (int k = 0; k < rs.n; ++k) p.visible_pairs += rs.v[k].second - rs.v[k].first;
+      for (int k = 0; k < rs.n; ++k) pairs += rs.v[k].second - rs.v[k].first;
     }
-  }
+    chunk_pairs[c] = pairs;
+  });
+  p.visible_pairs = std::accumulate(chunk_pairs.begin(), chunk_pairs.end(), (int64_t)0);
   // visible pairs of every rank (RFC section 2: rank s holds chunks s and
   // 2R-1-s of every sub-sequence); rows are independent of the rank that holds them
   p.visible_pairs_per_rank.assign(p.cp_size, 0);
-  for (int32_t i = 0; i < p.n_seqs; ++i) {
+  if (p.cp_size == 1) p.visible_pairs_per_rank[0] = p.visible_pairs;
+  for (int32_t i = 0; i < p.n_seqs && p.cp_size > 1; ++i) {
     const int32_t L = p.cu[i + 1] - p.cu[i];
     const int32_t c = L / (2 * p.cp_size);
     for (int32_t s = 0; s < p.cp_size; ++s) {
@@ -346,7 +479,9 @@ cva_status build_schedules(Plan& p) {
   }
   FwdShape fs = forward_shape(p);
   p.fwd_heads_per_tile = fs.heads_per_tile;
-  build_q_schedule(p, p.fwd, fs.tile_q, fs.tile_kv);
+  BlockSets bs;
+  bs.build(p);
+  build_q_schedule(p, bs, p.fwd, fs.tile_q, fs.tile_kv);
   for (int32_t t = 0; t < p.fwd.n_tiles(); ++t) {
     if (p.fwd.tiles[(size_t)t * QT_INTS + QT_NSPAN] > kFwdMaxSpans) {
       set_error("mask gives a query tile more K/V spans than the forward kernel supports");
@@ -357,14 +492,14 @@ cva_status build_schedules(Plan& p) {
   if (kDqTileKv == fs.tile_kv && dq_q == fs.tile_q)
     p.dq = p.fwd;  // same tile shape: the dQ kernel walks the forward schedule
   else
-    build_q_schedule(p, p.dq, dq_q, kDqTileKv);
+    build_q_schedule(p, bs, p.dq, dq_q, kDqTileKv);
   for (int32_t t = 0; t < p.dq.n_tiles(); ++t) {
     if (p.dq.tiles[(size_t)t * QT_INTS + QT_NSPAN] > kDqMaxSpans) {
       set_error("mask gives a query tile more K/V spans than the dQ kernel supports");
       return CVA_E_UNSUPPORTED;
     }
   }
-  build_kv_schedule(p, p.dkdv, kDkvTileQ, kDkvTileKv);
+  build_kv_schedule(p, bs, p.dkdv, kDkvTileQ, kDkvTileKv);
   for (int32_t t = 0; t < p.dkdv.n_tiles(); ++t) {
     if (p.dkdv.tiles[(size_t)t * KT_INTS + KT_NSPAN] > kDkvMaxSpans) {
       set_error("mask gives a K/V tile more query spans than the dK/dV kernel supports");
