@@ -423,22 +423,34 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     if (mk >= 0 && mk < n_tiles) TL::read_index(idxK, sIdx[mk % NIR], ltid);
     if (mv >= 0 && mv < n_tiles) TL::read_index(idxV, sIdx[mv % NIR], ltid);
   };
-  auto issue_batch = [&](int n) {
+  // With a 4-deep ring a batch goes out in two parts: K and the indices at the
+  // start of the MFMA step, V after the vector step (where the streaming group
+  // has slack), so that neither step carries the whole issue cost.  With a
+  // 3-deep ring V needs the earlier start and the batch goes out whole.
+  constexpr bool kSplitIssue = NS >= 4;
+  auto issue_k_part = [&](int n) {
     int cnt = 0;
-    const int mk = n + NS, mv = n + NS - 1, mi = n + 2 * NS;
+    const int mk = n + NS, mi = n + 2 * NS;
     if (mk >= 0 && mk < n_tiles) {
       TL::issue_k(sK[mk % NS], kg, idxK, kstride, ltid, w4 * 64);
       cnt += TL::KN;
-    }
-    if (mv >= 0 && mv < n_tiles) {
-      TL::issue_v(sV[mv % NS], vg, idxV, vstride, ltid, w4 * 64);
-      cnt += TL::VN;
     }
     if (mi >= 2 * NS && mi < n_tiles) {  // earlier tiles' indices come with the prologue
       fetch_idx();
       cnt += 1;
     }
     bcount[(n + NS) % NS] = cnt;
+  };
+  auto issue_v_part = [&](int n) {
+    const int mv = n + NS - 1;
+    if (mv >= 0 && mv < n_tiles) {
+      TL::issue_v(sV[mv % NS], vg, idxV, vstride, ltid, w4 * 64);
+      bcount[(n + NS) % NS] += TL::VN;
+    }
+  };
+  auto issue_batch = [&](int n) {
+    issue_k_part(n);
+    issue_v_part(n);
   };
   // after this, the loads needed by X(n+1) (batch n+2-NS) have landed
   auto wait_batch = [&](int n) {
@@ -596,7 +608,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   __syncthreads();
   // X(n) = PV(n) + S(n+1); Y(n+1)
   for (int n = 0; n + 1 < n_tiles; ++n) {
-    if (grp == 0) issue_batch(n);
+    if (grp == 0) {
+      if constexpr (kSplitIssue) issue_k_part(n);
+      else issue_batch(n);
+    }
     pv(n);
     scores(n + 1);
     {
@@ -622,6 +637,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     cY = next_tile(cY, sSpan, nspan);
     init_scores();
     if (grp == 0) {
+      if constexpr (kSplitIssue) issue_v_part(n);
       wait_batch(n);
       prepare_batch(n + 1);
     }
