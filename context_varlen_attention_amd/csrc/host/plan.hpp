@@ -85,7 +85,7 @@ struct Plan {
   std::vector<int32_t> fwds_combine;  // [m][CB_INTS]
   int32_t n_split_slots = 0;
   int32_t fwd_split_cap = 0;
-  std::vector<int32_t> zero_rows;  // [m][2] rank-major row ranges no local query sees
+  std::vector<int32_t> zero_rows;  // [m][2] rank-major row ranges no local query sees (<= 8 rows each)
 
   // device copy
   std::vector<int32_t> blob;
@@ -155,6 +155,7 @@ constexpr int32_t kFwdTileKv = 64;
 constexpr int32_t kDqTileKv = 64;     // dQ kernel: keys per K/V tile (query tile as forward)
 constexpr int32_t kDkvTileQ = 64;     // dK/dV kernel: queries per Q tile
 constexpr int32_t kDkvTileKv = 128;   // dK/dV kernel: keys per work-group (4 waves x 32)
+constexpr int32_t kZeroRowsPerBlock = 8;  // rank-major rows per zero-fill work-group
 constexpr int32_t kSplitCUs = 256;        // compute units the split balances over (MI355X)
 constexpr int32_t kSplitMinSteps = 8;     // never cut a piece shorter than this many K/V tiles
 constexpr int32_t kSplitMaxPieces = 8;    // pieces per Q tile (merge keeps their weights in registers)

@@ -512,13 +512,17 @@ cva_status build_schedules(Plan& p) {
   // rank-major rows outside every prefix are zero in dK/dV
   std::vector<char> covered((size_t)p.T, 0);
   for (int32_t x : p.kv_index) covered[x] = 1;
+  // (in pieces of at most kZeroRowsPerBlock rows: one work-group each, so that
+  // the zero fill spreads over the chip)
   p.zero_rows.clear();
   for (int64_t t = 0; t < p.T;) {
     if (covered[t]) { ++t; continue; }
     int64_t e = t;
     while (e < p.T && !covered[e]) ++e;
-    p.zero_rows.push_back((int32_t)t);
-    p.zero_rows.push_back((int32_t)e);
+    for (int64_t a = t; a < e; a += kZeroRowsPerBlock) {
+      p.zero_rows.push_back((int32_t)a);
+      p.zero_rows.push_back((int32_t)std::min<int64_t>(e, a + kZeroRowsPerBlock));
+    }
     t = e;
   }
   return CVA_OK;

@@ -40,36 +40,48 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O) and LSE * log2(e), one thread per (local row, head);
-// the scaled LSE lets the gradient kernels form P = exp2(S * scale * log2 e -
-// LSE * log2 e) with one fused multiply-add
+// Delta = rowsum(dO * O) and LSE * log2(e) per (local row, head); the scaled
+// LSE lets the gradient kernels form P = exp2(S * scale * log2 e - LSE * log2 e)
+// with one fused multiply-add
 // ---------------------------------------------------------------------------
 template <typename E, int DV>
 __global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams P) {
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // DV/8 consecutive lanes share one (row, head): each reads 16 bytes of the O
+  // and dO rows (so a wave reads whole rows, contiguous), and the partial dot
+  // products are summed across those lanes.
+  constexpr int LPR = DV / 8;  // lanes per (row, head): 8 or 16
+  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  const int64_t idx = gid / LPR;
+  const int part = (int)(gid % LPR);
   const int64_t n = (int64_t)P.t_loc * P.hq;
-  if (idx >= n) return;
-  const int64_t row = idx / P.hq;
-  const int head = (int)(idx % P.hq);
-  const uint16_t* o = (const uint16_t*)P.o + (row * P.hq + head) * DV;
-  const uint16_t* g = (const uint16_t*)P.dout + (row * P.hq + head) * DV;
+  const bool valid = idx < n;
   float acc = 0.f;
-#pragma unroll 4
-  for (int d = 0; d < DV; d += 8) {
-    const u32x4_t a = *(const u32x4_t*)(o + d);
-    const u32x4_t b = *(const u32x4_t*)(g + d);
+  if (valid) {
+    const int64_t row = idx / P.hq;
+    const int head = (int)(idx % P.hq);
+    const uint16_t* o = (const uint16_t*)P.o + (row * P.hq + head) * DV + 8 * part;
+    const uint16_t* g = (const uint16_t*)P.dout + (row * P.hq + head) * DV + 8 * part;
+    const u32x4_t a = *(const u32x4_t*)o;
+    const u32x4_t b = *(const u32x4_t*)g;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       acc = fmaf(E::to_float((uint16_t)(a[w] & 0xFFFFu)), E::to_float((uint16_t)(b[w] & 0xFFFFu)), acc);
       acc = fmaf(E::to_float((uint16_t)(a[w] >> 16)), E::to_float((uint16_t)(b[w] >> 16)), acc);
     }
   }
-  P.delta[(int64_t)head * P.t_loc + row] = acc;
-  P.lse2[(int64_t)head * P.t_loc + row] = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
+  if (valid && part == 0) {
+    const int64_t row = idx / P.hq;
+    const int head = (int)(idx % P.hq);
+    P.delta[(int64_t)head * P.t_loc + row] = acc;
+    P.lse2[(int64_t)head * P.t_loc + row] = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// zero dK / dV on rank-major rows outside every local prefix
+// zero dK / dV on rank-major rows outside every local prefix (one work-group
+// per range of at most 8 rows)
 // ---------------------------------------------------------------------------
 template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads) void zero_rows_kernel(BwdParams P) {
@@ -990,7 +1002,7 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
     e = hipGetLastError();
   };
   const int64_t n_pre = (int64_t)p.t_loc * p.hq;
-  launch(K_BWD_PRE, bwd_pre_kernel<E, DV>, (unsigned)((n_pre + kThreads - 1) / kThreads));
+  launch(K_BWD_PRE, bwd_pre_kernel<E, DV>, (unsigned)((n_pre * (DV / 8) + kThreads - 1) / kThreads));
   launch(K_BWD_ZERO, zero_rows_kernel<DQK, DV>, (unsigned)p.n_zero_ranges);
   if constexpr (DQK <= 128)
     launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
