@@ -21,6 +21,7 @@
 #include <algorithm>
 #include <array>
 #include <atomic>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <numeric>
@@ -144,13 +145,16 @@ void tile_sets(const Plan& p, int seg, int32_t a0, int32_t a1, Scratch& w) {
 
 // Runs f(i) for i in [0, n) on up to kPlanThreads host threads when the batch is
 // large (rows >= kPlanParallelRows), else inline; every i writes only its own
-// outputs, so the result does not depend on the thread count.
+// outputs, so the result does not depend on the thread count.  CVA_PLAN_THREADS
+// in the environment lowers the cap (1: always inline).
 constexpr int32_t kPlanThreads = 8;
 constexpr int64_t kPlanParallelRows = 32768;
 template <typename Fn>
 void parallel_for(int32_t n, int64_t rows, Fn f) {
+  int32_t cap = kPlanThreads;
+  if (const char* v = std::getenv("CVA_PLAN_THREADS")) cap = std::max(1, std::min(kPlanThreads, std::atoi(v)));
   const int32_t hw = (int32_t)std::max(1u, std::thread::hardware_concurrency());
-  const int32_t nt = rows >= kPlanParallelRows ? std::min({hw, kPlanThreads, n}) : 1;
+  const int32_t nt = rows >= kPlanParallelRows ? std::min({hw, cap, n}) : 1;
   if (nt <= 1) {
     for (int32_t i = 0; i < n; ++i) f(i);
     return;

@@ -143,7 +143,8 @@ const char* cva_last_error(void);
  * Supported head dims: (Dqk, Dv) in {(64,64), (128,128), (192,128)}; fp32 is a
  * forward-only correctness path (VALU kernel), bf16/fp16 run on MFMA.
  * For 32768 or more local rows the row and block passes run on up to 8 host
- * threads (joined before the call returns; the plan does not depend on them).
+ * threads (joined before the call returns; the plan does not depend on them;
+ * the environment variable CVA_PLAN_THREADS lowers the cap, 1 = no threads).
  * On success *out owns a new plan (release with cva_plan_destroy). */
 cva_status cva_plan_create(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp_size,
                            int32_t rank, const cva_mask_desc* mask, int32_t hq, int32_t hkv,

@@ -316,3 +316,26 @@ def test_blockwise_ranks_unequal():
     w = _wl([4096, 2048], 4, 0, "blockwise", block=256, sink=1, window=2)
     per = _plan(w).metadata["visible_pairs_per_rank"]
     assert len(set(per.tolist())) > 1
+
+
+def test_plan_independent_of_planner_threads(monkeypatch):
+    """A large batch (>= 32768 local rows, planned on several threads) gives the
+    same metadata and schedules as the single-threaded planner."""
+    w = synth.make_workload("sparse8", mask="lambda")
+
+    def build():
+        p = cva.Plan(w.cu_seqlens, 1, 0, w.hq, w.hkv, w.d_qk, w.d_v, mask="lambda", sink=w.sink,
+                     window=w.window)
+        return p, [p.schedule(k) for k in range(4)]
+
+    monkeypatch.setenv("CVA_PLAN_THREADS", "1")
+    p1, s1 = build()
+    monkeypatch.setenv("CVA_PLAN_THREADS", "8")
+    p8, s8 = build()
+    assert p1.local_tokens >= 32768
+    for key in ("kv_index", "actual_seq_qlen", "actual_seq_kvlen", "visible_pairs_per_rank"):
+        assert (p1.metadata[key] == p8.metadata[key]).all(), key
+    assert p1.metadata["visible_pairs"] == p8.metadata["visible_pairs"]
+    for a, b in zip(s1, s8):
+        assert a[0] == b[0] and a[1] == b[1]
+        assert (a[2] == b[2]).all() and (a[3] == b[3]).all()
