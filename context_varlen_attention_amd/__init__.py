@@ -25,7 +25,8 @@ import os
 import numpy as np
 
 __all__ = ["Plan", "Placement", "fwd", "bwd", "CvaError", "local_token_ids",
-           "rank_major_token_ids", "library_path", "load_library", "timing_enable", "timing_read"]
+           "rank_major_token_ids", "library_path", "load_library", "timing_enable", "timing_read",
+           "timing_select"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcva.so")
@@ -90,7 +91,7 @@ class _PlacementInfo(ctypes.Structure):
 EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_get_metadata",
            "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_fwd_workspace_bytes",
            "cva_fwd_split", "cva_bwd_workspace_bytes",
-           "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read",
+           "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read", "cva_timing_select",
            "cva_placement_create", "cva_placement_get", "cva_placement_destroy"]
 
 KERNEL_NAMES = ["fwd", "bwd_pre", "bwd_zero", "bwd_dkdv", "bwd_dq", "fwd_merge"]
@@ -143,6 +144,8 @@ def load_library():
     L.cva_timing_enable.argtypes = [i32]
     L.cva_timing_read.restype = i32
     L.cva_timing_read.argtypes = [ctypes.POINTER(_KernelTimes)]
+    L.cva_timing_select.restype = i32
+    L.cva_timing_select.argtypes = [ctypes.c_uint32]
     L.cva_placement_create.restype = i32
     L.cva_placement_create.argtypes = [_P32, i32, ctypes.POINTER(_MaskDesc), i32, i32, i32, i32,
                                        i32, i32, i32, ctypes.c_double, ctypes.POINTER(vp)]
@@ -456,6 +459,12 @@ def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk
 def timing_enable(on=True):
     """``cva_timing_enable``: start (and reset) or stop per-kernel event timing."""
     _check(load_library().cva_timing_enable(1 if on else 0))
+
+
+def timing_select(kernels=None):
+    """Time only the named kernels (KERNEL_NAMES entries); None = all."""
+    mask = 0xFFFFFFFF if kernels is None else sum(1 << KERNEL_NAMES.index(k) for k in kernels)
+    _check(load_library().cva_timing_select(mask))
 
 
 def timing_read():

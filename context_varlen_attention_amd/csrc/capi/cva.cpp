@@ -71,12 +71,17 @@ struct Timer final : cva::LaunchHook {
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
   }
+  uint32_t mask = ~0u;  // kernels to time
+  bool skip = false;    // the launch in flight is not timed
   void before(int kernel, hipStream_t s) override {
+    skip = ((mask >> kernel) & 1u) == 0;
+    if (skip) return;
     Rec r{kernel, get(), get()};
     if (r.a) (void)hipEventRecord(r.a, s);
     pending.push_back(r);
   }
   void after(int, hipStream_t s) override {
+    if (skip) return;
     if (!pending.empty() && pending.back().b) (void)hipEventRecord(pending.back().b, s);
   }
   hipError_t drain() {
@@ -463,6 +468,11 @@ cva_status cva_timing_enable(int32_t on) {
   } else {
     g_timer.on = false;
   }
+  return CVA_OK;
+}
+
+cva_status cva_timing_select(uint32_t kernel_mask) {
+  g_timer.mask = kernel_mask;
   return CVA_OK;
 }
 

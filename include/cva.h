@@ -294,6 +294,10 @@ typedef struct {
 
 cva_status cva_timing_enable(int32_t on);
 cva_status cva_timing_read(cva_kernel_times* out);
+/* Restrict timing to the kernels whose id bit is set in kernel_mask (bit k =
+ * kernel id k; all kernels by default), so that a timed loop can carry events
+ * around one kernel only.  Takes effect for launches after the call. */
+cva_status cva_timing_select(uint32_t kernel_mask);
 
 #ifdef __cplusplus
 }
