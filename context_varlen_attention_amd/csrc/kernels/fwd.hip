@@ -460,6 +460,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     wait_vmem_le(allowed);
   };
 
+  // group 0: indices of tiles 0 .. 2NS-1 first, so that they load together with Q
+  if (grp == 0)
+    for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
   // Q fragments, pre-scaled by scale*log2(e): lane holds Q[row][16t + 8*half .. +7].
   typename E::vec8 qf[KSTEPS];
   {
@@ -481,11 +484,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
     lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
   }
-  wait_vmem_all();  // Q and row intervals, before any tile load is in flight
+  wait_vmem_all();  // indices, Q and row intervals, before any tile load is in flight
   if (grp == 0) {
-    // indices of tiles 0 .. 2NS-1, then batches -NS .. -2
-    for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
-    wait_vmem_all();
+    // batches -NS .. -2
     for (int n = -NS; n <= -2; ++n) {
       prepare_batch(n);
       issue_batch(n);
