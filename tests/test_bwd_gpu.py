@@ -1,8 +1,9 @@
 """Backward parity: libcva dQ / rank-major dK / dV on the GPU against the fp64 oracle.
 
 Small shapes are compared element by element on every output (all masks, GQA,
-expanded-MLA head dims, several CP ranks); the 32k MLA-shape workload runs at
-full size and is compared on a subset of heads (all rows of those heads).
+expanded-MLA head dims, several CP ranks); the 32k MLA-shape and 16k GQA
+workloads run at full size and are compared on a subset of heads (all rows of
+those heads).
 """
 import numpy as np
 import pytest
@@ -80,6 +81,15 @@ def test_mla32k_three_heads(dtype):
     w = synth.make_workload("mla32k", dtype=dtype)
     q, k, v, do = synth.make_tensors(w)
     _run(w, q, k, v, do, heads=[0, 7, 15])
+
+
+def test_gqa16k_one_group():
+    """Full 16k GQA workload in the benchmark's launch configuration: all rows of
+    one K/V group's four query heads (dQ of each, and the group's complete
+    dK / dV)."""
+    w = synth.make_workload("gqa16k")
+    q, k, v, do = synth.make_tensors(w)
+    _run(w, q, k, v, do, heads=[4, 5, 6, 7])
 
 
 def test_uncovered_rows_are_zero_and_repeat_is_bitwise():
