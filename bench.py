@@ -111,14 +111,12 @@ def kernel_flops(w, pairs):
 
 
 def kernel_bytes(w):
-    t_loc = w.total_tokens // w.cp_size
-    esz = 4 if w.dtype == "fp32" else 2
-    return {"bwd_pre": 2 * t_loc * w.hq * w.d_v * esz + t_loc * w.hq * 12}  # O, dO, LSE in; Delta, LSE*log2e out
+    """HBM-bound kernels: algorithmic bytes per launch (none left on the step's path)."""
+    return {}
 
 
 KERNEL_SOURCES = {
     "fwd": ["kernels/fwd.hip"],
-    "bwd_pre": ["kernels/bwd.hip"], "bwd_zero": ["kernels/bwd.hip"],
     "bwd_dkdv": ["kernels/bwd.hip"], "bwd_dq": ["kernels/bwd.hip"],
     "fwd_merge": ["kernels/fwd.hip"],
 }

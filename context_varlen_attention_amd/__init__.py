@@ -94,7 +94,9 @@ EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_ge
            "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read", "cva_timing_select",
            "cva_placement_create", "cva_placement_get", "cva_placement_destroy"]
 
-KERNEL_NAMES = ["fwd", "bwd_pre", "bwd_zero", "bwd_dkdv", "bwd_dq", "fwd_merge"]
+# timing ids of cva_timing_read; ids 1 and 2 are reserved (formerly separate
+# Delta and zero-fill launches, now part of the dQ kernel)
+KERNEL_NAMES = ["fwd", "reserved1", "reserved2", "bwd_dkdv", "bwd_dq", "fwd_merge"]
 
 
 class _KernelTimes(ctypes.Structure):

@@ -16,16 +16,20 @@
 // row is written exactly once, so the result is deterministic (no atomics).
 //
 // Kernels, in launch order:
-//   bwd_pre_kernel    Delta[h, row] in fp32 (HBM-bound, tiny)
-//   zero_rows_kernel  rank-major rows no local query sees get dK = dV = 0
-//   dkdv_kernel       K/V-stationary: 4 waves x 32 keys; for every Q tile of
-//                     64 rows: S and dP on MFMA (A = Q / dO rows from LDS,
-//                     B = K / V from registers), then dV^T += dO^T P and
+//   dq_kernel         Q-stationary like the forward: S^T = K Q^T, dP^T = V dO^T,
+//                     dQ^T += K^T dS^T.  Its prologue also forms the backward
+//                     preprocess of its rows, Delta = rowsum(dO * O) and
+//                     LSE * log2(e), in fp32 for the dK/dV kernel, and its last
+//                     work-groups give dK = dV = 0 to the rank-major rows no
+//                     local query sees.
+//   dkdv_pair_kernel  K/V-stationary (Q/K head dimension up to 128): paired
+//                     waves per 32 keys, see below.
+//   dkdv_kernel       K/V-stationary (wider heads): 4 waves x 32 keys; for every
+//                     Q tile of 64 rows: S and dP on MFMA (A = Q / dO rows from
+//                     LDS, B = K / V from registers), then dV^T += dO^T P and
 //                     dK^T += Q^T dS with the transposed operands read by
 //                     ds_read_b64_tr_b16 and P / dS taken in place from the
 //                     accumulators.
-//   dq_kernel         Q-stationary like the forward: S^T = K Q^T, dP^T = V dO^T,
-//                     dQ^T += K^T dS^T.
 #include <type_traits>
 
 #include "../host/plan.hpp"
@@ -40,52 +44,12 @@ constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------------------
-// Delta = rowsum(dO * O) and LSE * log2(e) per (local row, head); the scaled
-// LSE lets the gradient kernels form P = exp2(S * scale * log2 e - LSE * log2 e)
-// with one fused multiply-add
-// ---------------------------------------------------------------------------
-template <typename E, int DV>
-__global__ __launch_bounds__(kThreads) void bwd_pre_kernel(BwdParams P) {
-  // DV/8 consecutive lanes share one (row, head): each reads 16 bytes of the O
-  // and dO rows (so a wave reads whole rows, contiguous), and the partial dot
-  // products are summed across those lanes.
-  constexpr int LPR = DV / 8;  // lanes per (row, head): 8 or 16
-  const int64_t gid = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  const int64_t idx = gid / LPR;
-  const int part = (int)(gid % LPR);
-  const int64_t n = (int64_t)P.t_loc * P.hq;
-  const bool valid = idx < n;
-  float acc = 0.f;
-  if (valid) {
-    const int64_t row = idx / P.hq;
-    const int head = (int)(idx % P.hq);
-    const uint16_t* o = (const uint16_t*)P.o + (row * P.hq + head) * DV + 8 * part;
-    const uint16_t* g = (const uint16_t*)P.dout + (row * P.hq + head) * DV + 8 * part;
-    const u32x4_t a = *(const u32x4_t*)o;
-    const u32x4_t b = *(const u32x4_t*)g;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc = fmaf(E::to_float((uint16_t)(a[w] & 0xFFFFu)), E::to_float((uint16_t)(b[w] & 0xFFFFu)), acc);
-      acc = fmaf(E::to_float((uint16_t)(a[w] >> 16)), E::to_float((uint16_t)(b[w] >> 16)), acc);
-    }
-  }
-#pragma unroll
-  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LPR);
-  if (valid && part == 0) {
-    const int64_t row = idx / P.hq;
-    const int head = (int)(idx % P.hq);
-    P.delta[(int64_t)head * P.t_loc + row] = acc;
-    P.lse2[(int64_t)head * P.t_loc + row] = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // zero dK / dV on rank-major rows outside every local prefix (one work-group
-// per range of at most 8 rows)
+// per range of at most 8 rows; run by the dQ kernel's last work-groups)
 // ---------------------------------------------------------------------------
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads) void zero_rows_kernel(BwdParams P) {
-  const int32_t r0 = P.t.zero_rows[2 * blockIdx.x], r1 = P.t.zero_rows[2 * blockIdx.x + 1];
+__device__ __forceinline__ void zero_rows_block(const BwdParams& P, int range) {
+  const int32_t r0 = P.t.zero_rows[2 * range], r1 = P.t.zero_rows[2 * range + 1];
   const u32x4_t z = {0u, 0u, 0u, 0u};
   {
     const int64_t n = (int64_t)(r1 - r0) * P.hkv * DQK / 8;
@@ -767,6 +731,11 @@ constexpr int kDqBlocksPerCu = DQK > 128 ? 1 : 2;
 
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdParams P) {
+  const int n_dq_wg = P.n_dq_tiles * P.dq_head_groups;
+  if ((int)blockIdx.x >= n_dq_wg) {  // the grid's last work-groups do the zero fill
+    zero_rows_block<DQK, DV>(P, (int)blockIdx.x - n_dq_wg);
+    return;
+  }
   constexpr int BN = kDqTileKv;
   constexpr int QS = DQK / 16, VS = DV / 16;
   constexpr int NS = kDqStages<DQK>;
@@ -824,16 +793,41 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
       of[s] = as_vec8<E>(x);
     }
   }
+  // The backward preprocess of this lane's (row, head): Delta = rowsum(dO * O)
+  // (each half-wave holds half of the row; the halves are summed across lanes
+  // l and l + 32) and LSE * log2(e).  Both go to the workspace for the dK/dV
+  // kernel, which runs after this one.
+  u32x4_t ov[VS];
   int lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
-  float lse2 = INFINITY, delta = 0.f;
+  float lse2 = INFINITY;
   if (valid) {
+    const uint16_t* orow = (const uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV + 8 * half;
+#pragma unroll
+    for (int s = 0; s < VS; ++s) ov[s] = *(const u32x4_t*)(orow + 16 * s);
     const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
     lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
-    lse2 = P.lse2[(int64_t)head * P.t_loc + row];
-    delta = P.delta[(int64_t)head * P.t_loc + row];
+    lse2 = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
   }
   if (tid < 4 * nspan) sSpan[tid] = P.t.dq_spans[span0 * 4 + tid];
   wait_vmem_all();
+  float dsum = 0.f;
+  if (valid) {
+#pragma unroll
+    for (int s = 0; s < VS; ++s) {
+      const u32x4_t g = __builtin_bit_cast(u32x4_t, of[s]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dsum = fmaf(E::to_float((uint16_t)(ov[s][w] & 0xFFFFu)), E::to_float((uint16_t)(g[w] & 0xFFFFu)), dsum);
+        dsum = fmaf(E::to_float((uint16_t)(ov[s][w] >> 16)), E::to_float((uint16_t)(g[w] >> 16)), dsum);
+      }
+    }
+  }
+  const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(dsum), __float_as_uint(dsum), false, false);
+  const float delta = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+  if (valid && half == 0) {
+    P.delta[(int64_t)head * P.t_loc + row] = delta;
+    P.lse2[(int64_t)head * P.t_loc + row] = lse2;
+  }
   __syncthreads();
   int n_tiles = 0;
   for (int sp = 0; sp < nspan; ++sp) {
@@ -1001,14 +995,14 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
     if (hook) hook->after(id, s);
     e = hipGetLastError();
   };
-  const int64_t n_pre = (int64_t)p.t_loc * p.hq;
-  launch(K_BWD_PRE, bwd_pre_kernel<E, DV>, (unsigned)((n_pre * (DV / 8) + kThreads - 1) / kThreads));
-  launch(K_BWD_ZERO, zero_rows_kernel<DQK, DV>, (unsigned)p.n_zero_ranges);
+  // dQ first: it also forms Delta and LSE * log2(e), which dK/dV read, and its
+  // last n_zero_ranges work-groups zero the dK/dV rows no local query sees
+  launch(K_BWD_DQ, dq_kernel<E, DQK, DV>,
+         (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups + (unsigned)p.n_zero_ranges);
   if constexpr (DQK <= 128)
     launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
   else
     launch(K_BWD_DKDV, dkdv_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv);
-  launch(K_BWD_DQ, dq_kernel<E, DQK, DV>, (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups);
   return e;
 }
 

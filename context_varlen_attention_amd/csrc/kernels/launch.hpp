@@ -69,7 +69,9 @@ struct BwdParams {
 };
 
 // Optional hook around every kernel launch (timing); ids as in cva.h.
-enum KernelId { K_FWD = 0, K_BWD_PRE = 1, K_BWD_ZERO = 2, K_BWD_DKDV = 3, K_BWD_DQ = 4, K_FWD_MERGE = 5 };
+// (ids 1 and 2, the former Delta and zero-fill launches, are reserved: that
+// work runs inside the dQ kernel)
+enum KernelId { K_FWD = 0, K_BWD_DKDV = 3, K_BWD_DQ = 4, K_FWD_MERGE = 5 };
 struct LaunchHook {
   virtual void before(int kernel, hipStream_t s) = 0;
   virtual void after(int kernel, hipStream_t s) = 0;

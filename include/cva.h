@@ -283,8 +283,9 @@ void cva_placement_destroy(cva_placement* placement);
  * the kernel is launched on.  cva_timing_read waits for the recorded events,
  * folds their elapsed times into per-kernel totals and returns the totals
  * since the last cva_timing_enable(1) (which resets them).  Kernel ids:
- *   0 forward, 1 backward Delta, 2 backward zero fill, 3 backward dK/dV,
- *   4 backward dQ, 5 forward merge of split pieces.
+ *   0 forward, 3 backward dK/dV, 4 backward dQ (which also forms Delta and
+ *   zero-fills the uncovered dK/dV rows), 5 forward merge of split pieces;
+ *   ids 1 and 2 are reserved (no kernel of their own any more).
  * Process-wide state; use from one thread at a time. */
 #define CVA_N_KERNELS 6
 typedef struct {
