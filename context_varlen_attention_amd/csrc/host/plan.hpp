@@ -154,7 +154,7 @@ constexpr int32_t kRowsPerWave = 32;
 constexpr int32_t kFwdTileKv = 64;
 constexpr int32_t kDqTileKv = 64;     // dQ kernel: keys per K/V tile (query tile as forward)
 constexpr int32_t kDkvTileQ = 64;     // dK/dV kernel: queries per Q tile
-constexpr int32_t kDkvTileKv = 128;   // dK/dV kernel: keys per work-group (4 waves x 32)
+constexpr int32_t kDkvTileKv = 128;   // dK/dV kernel: keys per work-group (4 wave pairs x 32)
 constexpr int32_t kZeroRowsPerBlock = 8;  // rank-major rows per zero-fill work-group
 constexpr int32_t kSplitCUs = 256;        // compute units the split balances over (MI355X)
 constexpr int32_t kSplitMinSteps = 8;     // never cut a piece shorter than this many K/V tiles

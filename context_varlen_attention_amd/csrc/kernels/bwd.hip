@@ -22,14 +22,9 @@
 //                     LSE * log2(e), in fp32 for the dK/dV kernel, and its last
 //                     work-groups give dK = dV = 0 to the rank-major rows no
 //                     local query sees.
-//   dkdv_pair_kernel  K/V-stationary (Q/K head dimension up to 128): paired
+//   dkdv_pair_kernel  K/V-stationary: a work-group owns 128 keys of one K/V
+//                     head and walks the 64-row Q tiles that see them; paired
 //                     waves per 32 keys, see below.
-//   dkdv_kernel       K/V-stationary (wider heads): 4 waves x 32 keys; for every
-//                     Q tile of 64 rows: S and dP on MFMA (A = Q / dO rows from
-//                     LDS, B = K / V from registers), then dV^T += dO^T P and
-//                     dK^T += Q^T dS with the transposed operands read by
-//                     ds_read_b64_tr_b16 and P / dS taken in place from the
-//                     accumulators.
 #include <type_traits>
 
 #include "../host/plan.hpp"
@@ -135,21 +130,6 @@ __device__ __forceinline__ void dma_rows(char* lds, RowSrc row_src, int tid, int
   }
 }
 
-// ---------------------------------------------------------------------------
-// dK / dV, K/V-stationary.  A work-group owns 128 keys of one K/V head (4 waves x
-// 32 keys, K and V of the lane's key in registers) and walks, for every query
-// head of the group, the 64-row Q tiles of both local chunks that see its keys.
-// Q, dO, LSE, Delta and the row intervals of those tiles stream through an
-// NS-deep LDS ring (DMA issued NS-1 tiles ahead).  Per 32 query rows:
-//   S = Q K^T, dP = dO V^T (A = rows from LDS, B = K / V from registers),
-//   P = exp2(S*scale*log2e - LSE*log2e), dS = P (dP - Delta),
-//   dV^T += dO^T P, dK^T += Q^T dS (A = transposing reads, B = P / dS in place).
-// Each rank-major key row is written once: no atomics, deterministic.  Used for
-// Q/K head dimensions above 128; narrower heads use dkdv_pair_kernel below.
-// ---------------------------------------------------------------------------
-template <int DQK>
-constexpr int kDkvStages = DQK > 128 ? 3 : 4;
-
 // Bits [lo, hi) of a 32-bit word, both ends clamped to [0, 32].
 __device__ __forceinline__ uint32_t key_bits(int lo, int hi) {
   lo = max(lo, 0);
@@ -159,260 +139,33 @@ __device__ __forceinline__ uint32_t key_bits(int lo, int hi) {
   return upto & ~((1u << lo) - 1u);
 }
 
-template <typename E, int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 1) void dkdv_kernel(BwdParams P) {
-  constexpr int BQ = 64;           // queries per Q tile
-  constexpr int QS = DQK / 16;     // reduction steps over Dqk
-  constexpr int VS = DV / 16;      // reduction steps over Dv
-  constexpr int NS = kDkvStages<DQK>;
-  using QO = TileOffsets<DQK>;
-  using OO = TileOffsets<DV>;
-  constexpr int QB = BQ * QO::RB, OB = BQ * OO::RB;
-  constexpr int QN = 64 * (QO::RB / 16) / 256, ON = 64 * (OO::RB / 16) / 256;
-  __shared__ __attribute__((aligned(16))) char sQ[NS][QB];
-  __shared__ __attribute__((aligned(16))) char sO[NS][OB];
-  __shared__ __attribute__((aligned(16))) float sL[NS][BQ];
-  __shared__ __attribute__((aligned(16))) float sD[NS][BQ];
-  __shared__ __attribute__((aligned(16))) int32_t sIv[NS][BQ * 4];
-  __shared__ __attribute__((aligned(16))) int32_t sSpan[kDkvMaxSpans * 4];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int col = lane & 31, half = lane >> 5;
-
-  const int tile = blockIdx.x / P.hkv;
-  const int kvh = blockIdx.x % P.hkv;
-  const int32_t* tr = P.t.kv_tiles + tile * 5;
-  const int seq = tr[0], k0 = tr[1], keys = tr[2], span0 = tr[3], nspan = tr[4];
-  // the longer prefix of the sub-sequence (its second segment) indexes every key of the tile
-  const int32_t* segA = P.t.segs + (2 * seq) * 8;
-  const int32_t* segB = P.t.segs + (2 * seq + 1) * 8;
-  const int qlenA = segA[2], row0A = segA[4], qlenB = segB[2], row0B = segB[4];
-  const int32_t* kvi = P.t.kv_index + segB[5];
-  const int kl = wave * 32 + col;          // key of this lane within the tile
-  const int kpos = k0 + kl;                // in-sequence key position
-  const bool kvalid = kl < keys;
-  const int64_t grow = kvalid ? (int64_t)kvi[kpos] : 0;
-
-  const uint16_t* __restrict__ kg = (const uint16_t*)P.k;
-  const uint16_t* __restrict__ vg = (const uint16_t*)P.v;
-
-  // K^T and V^T operands in registers: lane holds K[key][16s + 8*half .. +7]
-  typename E::vec8 kf[QS], vf[VS];
-  {
-    const uint16_t* kr = kg + (grow * P.hkv + kvh) * DQK + 8 * half;
-    const uint16_t* vr = vg + (grow * P.hkv + kvh) * DV + 8 * half;
-#pragma unroll
-    for (int s = 0; s < QS; ++s) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (kvalid) x = *(const u32x4_t*)(kr + 16 * s);
-      kf[s] = as_vec8<E>(x);
-    }
-#pragma unroll
-    for (int s = 0; s < VS; ++s) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (kvalid) x = *(const u32x4_t*)(vr + 16 * s);
-      vf[s] = as_vec8<E>(x);
-    }
-  }
-  if (tid < 4 * nspan) sSpan[tid] = P.t.kv_spans[span0 * 4 + tid];
-  wait_vmem_all();
-  __syncthreads();
-
-  // ---- cursor over the work item's Q tiles: heads of the group x spans x q tiles ----
-  struct Cur {
-    int hh, sp, qt, qt_end, seg, partial;
-  };
-  auto span_at = [&](Cur c, int sp) {
-    const int4 r = *(const int4*)(sSpan + 4 * sp);
-    c.sp = sp;
-    c.seg = __builtin_amdgcn_readfirstlane(r.x);
-    c.qt = __builtin_amdgcn_readfirstlane(r.y);
-    c.qt_end = __builtin_amdgcn_readfirstlane(r.z);
-    c.partial = __builtin_amdgcn_readfirstlane(r.w);
-    return c;
-  };
-  auto advance = [&](Cur c) {
-    if (++c.qt >= c.qt_end) {
-      int sp = c.sp + 1;
-      if (sp >= nspan) {
-        sp = 0;
-        ++c.hh;
-      }
-      c = span_at(c, sp);
-    }
-    return c;
-  };
-  int n_tiles = 0;
-  for (int sp = 0; sp < nspan; ++sp) {
-    Cur c = span_at(Cur{0, 0, 0, 0, 0, 0}, sp);
-    n_tiles += c.qt_end - c.qt;
-  }
-  n_tiles *= P.group;
-
-  // ---- streaming: batch for tile m -> ring slot m % NS ----
-  const char* qgb = (const char*)P.q;
-  const char* ogb = (const char*)P.dout;
-  // loads per wave and batch (the same for every batch)
-  const int per_batch = QN + ON + (wave < 3 ? 1 : 0);
-  auto issue = [&](const Cur& c, int m) {
-    const int slot = m % NS;
-    const int head = kvh * P.group + c.hh;
-    const bool isB = (c.seg & 1) != 0;
-    const int q_len = isB ? qlenB : qlenA, q_row0 = isB ? row0B : row0A;
-    const int a0 = c.qt * BQ;
-    auto lrow = [&](int r) { return q_row0 + min(a0 + r, q_len - 1); };
-    dma_rows<DQK>(sQ[slot], [&](int r) { return qgb + ((int64_t)lrow(r) * P.hq + head) * (DQK * 2); }, tid, wave);
-    dma_rows<DV>(sO[slot], [&](int r) { return ogb + ((int64_t)lrow(r) * P.hq + head) * (DV * 2); }, tid, wave);
-    if (wave == 0)
-      dma4(P.lse2 + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sL[slot]));
-    else if (wave == 1)
-      dma4(P.delta + (int64_t)head * P.t_loc + lrow(lane), lds_addr(sD[slot]));
-    else if (wave == 2)
-      dma16(P.t.row_iv + (int64_t)lrow(lane) * 4, lds_addr(sIv[slot]));
-  };
-  // wait until tile m's batch has landed; the batches issued after it (tiles
-  // m+1 .. m+NS-2, those that exist) may stay in flight
-  auto wait_for = [&](int m) {
-    const int later = min(m + NS - 1, n_tiles) - (m + 1);
-    wait_vmem_le(later > 0 ? later * per_batch : 0);
-  };
-
-  QO qo;
-  OO oo;
-  qo.init(lane);
-  oo.init(lane);
-
-  f32x16_t dk[DQK / 32], dv[DV / 32];
-#pragma unroll
-  for (int d = 0; d < DQK / 32; ++d) dk[d] = zero16();
-#pragma unroll
-  for (int d = 0; d < DV / 32; ++d) dv[d] = zero16();
-  const float sl2 = P.scale_log2;
-
-  Cur cI = span_at(Cur{0, 0, 0, 0, 0, 0}, 0);  // next tile to issue
-  Cur cC = cI;                                  // tile being computed
-  for (int m = 0; m < NS - 1 && m < n_tiles; ++m) {
-    issue(cI, m);
-    cI = advance(cI);
-  }
-  wait_for(0);
-  __syncthreads();
-
-  for (int n = 0; n < n_tiles; ++n) {
-    if (n + NS - 1 < n_tiles) {
-      issue(cI, n + NS - 1);  // into the slot tile n-1 used
-      cI = advance(cI);
-    }
-    const int slot = n % NS;
-    const char* q_s = sQ[slot];
-    const char* o_s = sO[slot];
-    const bool isB = (cC.seg & 1) != 0;
-    const int q_rem = (isB ? qlenB : qlenA) - cC.qt * BQ;  // valid rows of this tile
-    const bool partial = cC.partial != 0;
-#pragma unroll
-    for (int qs = 0; qs < BQ / 32; ++qs) {
-      // S[q][key] and dP[q][key] for 32 queries x this wave's 32 keys
-      f32x16_t s = zero16(), dp = zero16();
-#pragma unroll
-      for (int st = 0; st < QS; ++st) s = E::mfma32(as_vec8<E>(qo.row(q_s, qs, st)), kf[st], s);
-#pragma unroll
-      for (int st = 0; st < VS; ++st) dp = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), vf[st], dp);
-      // lane holds query qs*32 + 8i + 4*half + j (r = 4i + j) for key kpos; the
-      // LSE (scaled by log2 e) and Delta of those queries are read per i
-      uint32_t pp[2][4], pd[2][4];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int i0 = r >> 2;
-        const f32x4_t lv = *(const f32x4_t*)(sL[slot] + qs * 32 + 8 * i0 + 4 * half);
-        const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * i0 + 4 * half);
-        float pv[2], dsv[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int j = (r + u) & 3;
-          float x = fmaf(s[r + u], sl2, -lv[j]);
-          if (partial) {
-            const int q = qs * 32 + 8 * i0 + 4 * half + j;
-            const int4 iv = *(const int4*)(sIv[slot] + 4 * q);
-            const bool vis = (q < q_rem) & (((kpos >= iv.x) & (kpos < iv.y)) | ((kpos >= iv.z) & (kpos < iv.w)));
-            x = vis ? x : -INFINITY;
-          }
-          const float p = __builtin_amdgcn_exp2f(x);
-          pv[u] = p;
-          dsv[u] = p * (dp[r + u] - dv4[j]);
-        }
-        pp[r >> 3][(r & 7) >> 1] = pack2<E>(pv[0], pv[1]);
-        pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
-      }
-      // dV^T[d][key] += sum_q dO^T[d][q] P[q][key];  dK^T += Q^T dS
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int rows0 = qs * 32 + st * 16;
-        const typename E::vec8 bp = as_vec8<E>(u32x4_t{pp[st][0], pp[st][1], pp[st][2], pp[st][3]});
-        const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
-#pragma unroll
-        for (int d = 0; d < DV / 32; ++d) {
-          const u32x2_t lo = oo.trans(o_s, rows0, 0, d);
-          const u32x2_t hi = oo.trans(o_s, rows0, 1, d);
-          dv[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bp, dv[d]);
-        }
-#pragma unroll
-        for (int d = 0; d < DQK / 32; ++d) {
-          const u32x2_t lo = qo.trans(q_s, rows0, 0, d);
-          const u32x2_t hi = qo.trans(q_s, rows0, 1, d);
-          dk[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, dk[d]);
-        }
-      }
-    }
-    cC = advance(cC);
-    if (n + 1 < n_tiles) wait_for(n + 1);
-    __syncthreads();
-  }
-  wait_vmem_all();
-
-  // ---- write this lane's key row: dK^T / dV^T lane holds d = 32*blk + 8i + 4*half + j ----
-  if (kvalid) {
-    uint16_t* dkr = (uint16_t*)P.dk + (grow * P.hkv + kvh) * DQK;
-    uint16_t* dvr = (uint16_t*)P.dv + (grow * P.hkv + kvh) * DV;
-    const float sc = P.scale;
-#pragma unroll
-    for (int d = 0; d < DQK / 32; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dd = d * 32 + 8 * i + 4 * half;
-        *(u32x2_t*)(dkr + dd) = u32x2_t{pack2<E>(dk[d][4 * i] * sc, dk[d][4 * i + 1] * sc),
-                                         pack2<E>(dk[d][4 * i + 2] * sc, dk[d][4 * i + 3] * sc)};
-      }
-#pragma unroll
-    for (int d = 0; d < DV / 32; ++d)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int dd = d * 32 + 8 * i + 4 * half;
-        *(u32x2_t*)(dvr + dd) = u32x2_t{pack2<E>(dv[d][4 * i], dv[d][4 * i + 1]),
-                                         pack2<E>(dv[d][4 * i + 2], dv[d][4 * i + 3])};
-      }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// dK / dV with paired waves (Q/K head dimension up to 128).  The same work item
-// and Q-tile stream as dkdv_kernel, run by 8 waves: waves w and w+4 (one SIMD)
-// own the same 32 keys.  Wave w (the P wave) computes S = Q K^T and
+// dK / dV, K/V-stationary, with paired waves.  A work-group owns 128 keys of one
+// K/V head and walks, for every query head of the group, the 64-row Q tiles of
+// both local chunks that see its keys (Q, dO, LSE, Delta and the row intervals
+// of those tiles stream through an NS-deep LDS ring, DMA issued NS-1 tiles
+// ahead).  8 waves: waves w and w+4 (one SIMD) own the same 32 keys, with that
+// key's K (or V) row in registers.  Wave w (the P wave) computes S = Q K^T and
 // P = exp2(S*scale*log2e - LSE*log2e), hands P to its partner through LDS and
 // accumulates dV^T += dO^T P; wave w+4 (the dS wave) computes dP = dO V^T,
 // dS = P (dP - Delta) and accumulates dK^T += Q^T dS.  Each tile runs in two
 // phases separated by a barrier -- (S, P | dP) then (dV | dS, dK) -- so that on
 // every SIMD one wave's vector work overlaps the other's MFMAs, and each wave
-// keeps one operand set and one accumulator set in registers.
+// keeps one operand set and one accumulator set in registers (up to 244 VGPRs
+// at Q/K head dim 192, so two waves per SIMD).  Each rank-major key row is
+// written once: no atomics, deterministic.
 // ---------------------------------------------------------------------------
+// Q/dO ring depth: 512-byte Q rows (Q/K head dim 192) leave LDS for 2 stages.
+template <int DQK>
+constexpr int kDkvPairStages = DQK > 128 ? 2 : 4;
+
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P) {
   constexpr int NT = 2 * kThreads;
   constexpr int BQ = 64;           // queries per Q tile
   constexpr int QS = DQK / 16;     // reduction steps over Dqk
   constexpr int VS = DV / 16;      // reduction steps over Dv
-  constexpr int NS = kDkvStages<DQK>;
+  constexpr int NS = kDkvPairStages<DQK>;
   using QO = TileOffsets<DQK>;
   using OO = TileOffsets<DV>;
   constexpr int QB = BQ * QO::RB, OB = BQ * OO::RB;
@@ -999,10 +752,7 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
   // last n_zero_ranges work-groups zero the dK/dV rows no local query sees
   launch(K_BWD_DQ, dq_kernel<E, DQK, DV>,
          (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups + (unsigned)p.n_zero_ranges);
-  if constexpr (DQK <= 128)
-    launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
-  else
-    launch(K_BWD_DKDV, dkdv_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv);
+  launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
   return e;
 }
 
