@@ -481,6 +481,13 @@ template <int DQK>
 constexpr int kDqStages = DQK > 128 ? 3 : 2;
 template <int DQK>
 constexpr int kDqBlocksPerCu = DQK > 128 ? 1 : 2;
+// With one wave per SIMD (Q/K head dim 192) nothing hides the LDS operand
+// reads, so the MFMA chains run as explicit software pipelines: each operand is
+// read kDqAhead MFMAs before its use.  (With two waves per SIMD this measured
+// the same as the compiler's schedule.)
+template <int DQK>
+constexpr bool kDqPipe = DQK > 128;
+constexpr int kDqAhead = 4;
 
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdParams P) {
@@ -682,11 +689,47 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
     for (int nb = 0; nb < BN / 32; ++nb) {
       // the S and dP chains alternate, so that consecutive MFMAs are independent
       f32x16_t s = zero16(), dp = zero16();
+      if constexpr (kDqPipe<DQK>) {
+        // the operand of MFMA i is read from LDS while MFMA i - AHEAD issues, in
+        // an order pinned by a scheduling barrier after every MFMA
+        constexpr int MN = QS < VS ? QS : VS, NM = QS + VS, AHEAD = kDqAhead;
+        // op i: S step or dP step (alternating while both chains have steps left)
+        auto is_s = [](int i) { return i < 2 * MN ? (i % 2 == 0) : QS > VS; };
+        auto step = [](int i) { return i < 2 * MN ? i / 2 : MN + (i - 2 * MN); };
+        auto read_op = [&](auto ic) -> u32x4_t {
+          constexpr int i = decltype(ic)::value;
+          if constexpr (is_s(i)) return ko.row(k_s, nb, step(i));
+          else return vo.row(v_s, nb, step(i));
+        };
+        u32x4_t op[AHEAD];
+        static_for<0, AHEAD>([&](auto ic) { op[decltype(ic)::value] = read_op(ic); });
+        static_for<0, NM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const u32x4_t a = op[i % AHEAD];
+          if constexpr (i + AHEAD < NM) op[i % AHEAD] = read_op(std::integral_constant<int, i + AHEAD>{});
+          if constexpr (is_s(i)) s = E::mfma32(as_vec8<E>(a), qf[step(i)], s);
+          else dp = E::mfma32(as_vec8<E>(a), of[step(i)], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
 #pragma unroll
-      for (int st = 0; st < (QS > VS ? QS : VS); ++st) {
-        if (st < QS) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
-        if (st < VS) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
+        for (int st = 0; st < (QS > VS ? QS : VS); ++st) {
+          if (st < QS) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
+          if (st < VS) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
+        }
       }
+      // dQ^T operands (transposing reads of K): the first AHEAD go out before the
+      // exponentials, which do not need them
+      constexpr int DM = 2 * (DQK / 32), DAHEAD = kDqAhead;
+      u32x4_t kt_op[DAHEAD];
+      if constexpr (kDqPipe<DQK>)
+        static_for<0, DAHEAD>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          const int rows0 = nb * 32 + (i / (DQK / 32)) * 16;
+          const u32x2_t lo = ko.trans(k_s, rows0, 0, i % (DQK / 32));
+          const u32x2_t hi = ko.trans(k_s, rows0, 1, i % (DQK / 32));
+          kt_op[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        });
       // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
       uint32_t pd[2][4];
 #pragma unroll
@@ -706,15 +749,33 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
         pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
       }
       // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
+      if constexpr (kDqPipe<DQK>) {
+        static_for<0, DM>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          constexpr int st = i / (DQK / 32), d = i % (DQK / 32);
+          const u32x4_t a = kt_op[i % DAHEAD];
+          if constexpr (i + DAHEAD < DM) {
+            constexpr int j = i + DAHEAD;
+            const int rows0 = nb * 32 + (j / (DQK / 32)) * 16;
+            const u32x2_t lo = ko.trans(k_s, rows0, 0, j % (DQK / 32));
+            const u32x2_t hi = ko.trans(k_s, rows0, 1, j % (DQK / 32));
+            kt_op[i % DAHEAD] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+          }
+          const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
+          acc[d] = E::mfma32(as_vec8<E>(a), bd, acc[d]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int rows0 = nb * 32 + st * 16;
-        const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
+        for (int st = 0; st < 2; ++st) {
+          const int rows0 = nb * 32 + st * 16;
+          const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
 #pragma unroll
-        for (int d = 0; d < DQK / 32; ++d) {
-          const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
-          const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
-          acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
+          for (int d = 0; d < DQK / 32; ++d) {
+            const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
+            const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
+            acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
+          }
         }
       }
     }
