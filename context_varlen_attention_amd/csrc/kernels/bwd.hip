@@ -16,7 +16,8 @@
 // row is written exactly once, so the result is deterministic (no atomics).
 //
 // Kernels, in launch order:
-//   dq_kernel         Q-stationary like the forward: S^T = K Q^T, dP^T = V dO^T,
+//   dq_kernel /       Q-stationary like the forward: S^T = K Q^T, dP^T = V dO^T,
+//   dq_pair_kernel    (the second with paired waves, for Q/K head dim 192)
 //                     dQ^T += K^T dS^T.  Its prologue also forms the backward
 //                     preprocess of its rows, Delta = rowsum(dO * O) and
 //                     LSE * log2(e), in fp32 for the dK/dV kernel, and its last
@@ -42,19 +43,19 @@ constexpr float kLog2e = 1.4426950408889634f;
 // zero dK / dV on rank-major rows outside every local prefix (one work-group
 // per range of at most 8 rows; run by the dQ kernel's last work-groups)
 // ---------------------------------------------------------------------------
-template <int DQK, int DV>
+template <int DQK, int DV, int NT = kThreads>
 __device__ __forceinline__ void zero_rows_block(const BwdParams& P, int range) {
   const int32_t r0 = P.t.zero_rows[2 * range], r1 = P.t.zero_rows[2 * range + 1];
   const u32x4_t z = {0u, 0u, 0u, 0u};
   {
     const int64_t n = (int64_t)(r1 - r0) * P.hkv * DQK / 8;
     u32x4_t* base = (u32x4_t*)((uint16_t*)P.dk + (int64_t)r0 * P.hkv * DQK);
-    for (int64_t i = threadIdx.x; i < n; i += kThreads) base[i] = z;
+    for (int64_t i = threadIdx.x; i < n; i += NT) base[i] = z;
   }
   {
     const int64_t n = (int64_t)(r1 - r0) * P.hkv * DV / 8;
     u32x4_t* base = (u32x4_t*)((uint16_t*)P.dv + (int64_t)r0 * P.hkv * DV);
-    for (int64_t i = threadIdx.x; i < n; i += kThreads) base[i] = z;
+    for (int64_t i = threadIdx.x; i < n; i += NT) base[i] = z;
   }
 }
 
@@ -137,6 +138,300 @@ __device__ __forceinline__ uint32_t key_bits(int lo, int hi) {
   if (hi <= lo) return 0u;
   const uint32_t upto = hi >= 32 ? ~0u : (1u << hi) - 1u;
   return upto & ~((1u << lo) - 1u);
+}
+
+// ---------------------------------------------------------------------------
+// dQ with paired waves (Q/K head dimension 192, where the single-wave form needs
+// more than 256 registers and so runs one wave per SIMD).  The same work item
+// as dq_kernel, run by 8 waves: waves w and w+4 (one SIMD) own the same 32
+// query rows of one head.  Wave w (the S wave) holds Q^T, forms S^T = K Q^T and
+// P = exp2(S * scale * log2 e - LSE * log2 e) (masked on partial tiles) and
+// hands P over in fp32 through LDS; wave w+4 (the dS wave) holds dO^T and the
+// dQ accumulators, forms dP^T = V dO^T and, after the mid-tile barrier,
+// dS = P (dP - Delta) and dQ^T += K^T dS^T.  The dS waves also form Delta and
+// LSE * log2 e of the rows (the backward preprocess) and stream the K/V tiles
+// through a 2-deep LDS ring, issuing tile n+1 at the start of tile n.  P is
+// never rounded, so the arithmetic is that of dq_kernel.
+// ---------------------------------------------------------------------------
+template <typename E, int DQK, int DV>
+__global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
+  constexpr int NT = 2 * kThreads;
+  const int n_dq_wg = P.n_dq_tiles * P.dq_head_groups;
+  if ((int)blockIdx.x >= n_dq_wg) {  // the grid's last work-groups do the zero fill
+    zero_rows_block<DQK, DV, NT>(P, (int)blockIdx.x - n_dq_wg);
+    return;
+  }
+  constexpr int BN = kDqTileKv;
+  constexpr int QS = DQK / 16, VS = DV / 16;
+  constexpr int NS = 2;
+  constexpr int NIR = 2 * NS;  // index ring slots
+  using KO = TileOffsets<DQK>;
+  using VO = TileOffsets<DV>;
+  constexpr int CHK = KO::RB / 16, CHV = VO::RB / 16;  // 16-byte chunks per LDS row
+  constexpr int NK = BN * CHK / kThreads, NV = BN * CHV / kThreads;  // per dS-wave thread
+  constexpr bool kSharedRows = CHK == CHV;
+  constexpr int NI = kSharedRows ? NK : NK + NV;
+  static_assert(BN == 64, "the index fetch covers 64 keys per tile");
+  __shared__ __attribute__((aligned(16))) char sK[NS][BN * KO::RB];
+  __shared__ __attribute__((aligned(16))) char sV[NS][BN * VO::RB];
+  __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][BN];
+  __shared__ __attribute__((aligned(16))) int32_t sSpan[kDqMaxSpans * 4];
+  __shared__ __attribute__((aligned(16))) f32x4_t sP[4][BN / 32][4][64];  // pair, key block, r/4, lane
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31, half = lane >> 5;
+  const bool dswave = wave >= 4;
+  const int pw = wave & 3;              // the pair (row block / head) of this wave
+  const int ltid = tid & (kThreads - 1);  // thread index inside its role
+
+  const int tile = blockIdx.x / P.dq_head_groups;
+  const int hg = blockIdx.x % P.dq_head_groups;
+  const int32_t* tr = P.t.dq_tiles + tile * 5;
+  const int seg = tr[0], q0 = tr[1], span0 = tr[3], nspan = tr[4];
+  const int32_t* sg = P.t.segs + seg * 8;
+  const int q_len = sg[2], kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
+  const int hpt = P.dq_heads_per_tile;
+  const int head = hg * hpt + (pw % hpt);
+  const int kvh = head / P.group;
+  const int a = q0 + (pw / hpt) * 32 + col;
+  const bool valid = a < q_len;
+  const int row = q_row0 + a;
+
+  const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
+  const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
+  const uint32_t kstride = (uint32_t)P.hkv * DQK * 2, vstride = (uint32_t)P.hkv * DV * 2;
+  const int32_t* __restrict__ kvi = P.t.kv_index + kv_off;
+
+  if (tid < 4 * nspan) sSpan[tid] = P.t.dq_spans[span0 * 4 + tid];
+  wait_vmem_all();
+  __syncthreads();
+  int n_tiles = 0;
+  for (int sp = 0; sp < nspan; ++sp) {
+    const int4 r = *(const int4*)(sSpan + 4 * sp);
+    n_tiles += __builtin_amdgcn_readfirstlane(r.y) - __builtin_amdgcn_readfirstlane(r.x);
+  }
+
+  struct Cur {
+    int sp, t, t_end, partial;
+  };
+  auto span_at = [&](int sp) {
+    const int4 r = *(const int4*)(sSpan + 4 * sp);
+    return Cur{sp, __builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+               __builtin_amdgcn_readfirstlane(r.z)};
+  };
+  auto advance = [&](Cur c) {
+    if (++c.t >= c.t_end && c.sp + 1 < nspan) c = span_at(c.sp + 1);
+    return c;
+  };
+
+  // ---- streaming by the dS waves.  batch(m): K and V of tile m into ring slot
+  // m % NS and, by wave 4, the prefix-index entries of tile m + NIR - 1 (clamped
+  // to a valid address when that tile does not exist: the slot is then never read).
+  Cur cF = nspan > 0 ? span_at(0) : Cur{0, 0, 0, 0};  // next tile whose indices get fetched
+  int next_f = 0;
+  auto fetch_idx = [&]() {
+    const int kb0 = next_f < n_tiles ? cF.t * BN : 0;
+    dma4(kvi + min(kb0 + lane, kv_len - 1), lds_addr(sIdx[next_f % NIR]));
+    if (next_f < n_tiles) cF = advance(cF);
+    ++next_f;
+  };
+  auto issue = [&](int m) {
+    const int32_t* si = sIdx[m % NIR];
+    int idx[NI];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) idx[i] = si[(i * kThreads + ltid) / CHK];
+    if constexpr (!kSharedRows) {
+#pragma unroll
+      for (int i = 0; i < NV; ++i) idx[NK + i] = si[(i * kThreads + ltid) / CHV];
+    }
+    const uint32_t kl = lds_addr(sK[m % NS]) + (uint32_t)pw * 64 * 16;
+    const uint32_t vl = lds_addr(sV[m % NS]) + (uint32_t)pw * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      const int s = i * kThreads + ltid;
+      int c = (s % CHK) ^ bwd_swz<KO::RB>(s / CHK);
+      if (c >= DQK / 8) c = 0;  // row padding: any in-bounds source
+      dma16(kg + ((uint64_t)(uint32_t)idx[i] * kstride + c * 16), kl + i * kThreads * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int s = i * kThreads + ltid;
+      int c = (s % CHV) ^ bwd_swz<VO::RB>(s / CHV);
+      if (c >= DV / 8) c = 0;
+      const int id = kSharedRows ? idx[i] : idx[NK + i];
+      dma16(vg + ((uint64_t)(uint32_t)id * vstride + c * 16), vl + i * kThreads * 16);
+    }
+    if (wave == 4) fetch_idx();
+  };
+
+  KO ko;
+  VO vo;
+  ko.init(lane);
+  vo.init(lane);
+  const float sl2 = P.scale_log2;
+
+  // The tile loop is instantiated once per role.
+  auto run = [&](auto role_c) {
+    constexpr bool DSW = decltype(role_c)::value;
+    // registers: Q^T (S wave) or dO^T (dS wave); lane holds row[16s + 8*half .. +7]
+    constexpr int FS = DSW ? VS : QS;
+    typename E::vec8 fr[FS];
+    {
+      const uint16_t* src = DSW ? (const uint16_t*)P.dout + ((int64_t)row * P.hq + head) * DV + 8 * half
+                                : (const uint16_t*)P.q + ((int64_t)row * P.hq + head) * DQK + 8 * half;
+#pragma unroll
+      for (int s = 0; s < FS; ++s) {
+        u32x4_t x = {0u, 0u, 0u, 0u};
+        if (valid) x = *(const u32x4_t*)(src + 16 * s);
+        fr[s] = as_vec8<E>(x);
+      }
+    }
+    float lse2 = INFINITY, delta = 0.f;
+    int lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
+    if constexpr (DSW) {
+      // the backward preprocess of this lane's (row, head): Delta = rowsum(dO * O)
+      // (each half-wave holds half of the row; the halves are summed across
+      // lanes l and l + 32) and LSE * log2(e), for the dK/dV kernel
+      u32x4_t ov[VS];
+      if (valid) {
+        const uint16_t* orow = (const uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV + 8 * half;
+#pragma unroll
+        for (int s = 0; s < VS; ++s) ov[s] = *(const u32x4_t*)(orow + 16 * s);
+        lse2 = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
+      }
+      wait_vmem_all();
+      float dsum = 0.f;
+      if (valid) {
+#pragma unroll
+        for (int s = 0; s < VS; ++s) {
+          const u32x4_t g = __builtin_bit_cast(u32x4_t, fr[s]);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            dsum = fmaf(E::to_float((uint16_t)(ov[s][w] & 0xFFFFu)), E::to_float((uint16_t)(g[w] & 0xFFFFu)), dsum);
+            dsum = fmaf(E::to_float((uint16_t)(ov[s][w] >> 16)), E::to_float((uint16_t)(g[w] >> 16)), dsum);
+          }
+        }
+      }
+      const auto ps = __builtin_amdgcn_permlane32_swap(__float_as_uint(dsum), __float_as_uint(dsum), false, false);
+      delta = __uint_as_float(ps[0]) + __uint_as_float(ps[1]);
+      if (valid && half == 0) {
+        P.delta[(int64_t)head * P.t_loc + row] = delta;
+        P.lse2[(int64_t)head * P.t_loc + row] = lse2;
+      }
+    } else {
+      if (valid) {
+        const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
+        lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
+        lse2 = P.lse[(int64_t)head * P.t_loc + row] * kLog2e;
+      }
+      wait_vmem_all();
+    }
+    // first batch: the indices of tiles 0 .. NIR-2, then tile 0
+    if (n_tiles > 0) {
+      if (wave == 4)
+        for (int m = 0; m < NIR - 1; ++m) fetch_idx();
+      if constexpr (DSW) wait_vmem_all();
+      __syncthreads();
+      if constexpr (DSW) {
+        issue(0);
+        wait_vmem_all();
+      }
+      __syncthreads();
+    }
+    f32x16_t acc[DSW ? DQK / 32 : 1];
+#pragma unroll
+    for (int d = 0; d < (DSW ? DQK / 32 : 1); ++d) acc[d] = zero16();
+    Cur cC = nspan > 0 ? span_at(0) : Cur{0, 0, 0, 0};  // tile being computed
+    for (int n = 0; n < n_tiles; ++n) {
+      const char* k_s = sK[n % NS];
+      const char* v_s = sV[n % NS];
+      const int kb0 = cC.t * BN;
+      const bool partial = cC.partial != 0;
+      if constexpr (!DSW) {
+        // ---- S wave: S^T and P of both 32-key blocks (phase 1) ----
+#pragma unroll
+        for (int nb = 0; nb < BN / 32; ++nb) {
+          f32x16_t sc = zero16();
+#pragma unroll
+          for (int st = 0; st < QS; ++st) sc = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), fr[st], sc);
+          // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f32x4_t pv;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int r = 4 * i + j;
+              float x = fmaf(sc[r], sl2, -lse2);
+              if (partial) {
+                const int b = kb0 + nb * 32 + 8 * i + 4 * half + j;
+                const bool vis = ((b >= lo1) & (b < hi1)) | ((b >= lo2) & (b < hi2));
+                x = vis ? x : -INFINITY;
+              }
+              pv[j] = __builtin_amdgcn_exp2f(x);
+            }
+            sP[pw][nb][i][lane] = pv;
+          }
+        }
+        __syncthreads();  // P is in LDS
+      } else {
+        // ---- dS wave: the next tile's loads and dP^T (phase 1); dS, dQ^T (phase 2) ----
+        if (n + NS - 1 < n_tiles) issue(n + NS - 1);  // into the slot tile n-1 used
+        f32x16_t dp[BN / 32];
+#pragma unroll
+        for (int nb = 0; nb < BN / 32; ++nb) dp[nb] = zero16();
+#pragma unroll
+        for (int st = 0; st < VS; ++st)
+#pragma unroll
+          for (int nb = 0; nb < BN / 32; ++nb) dp[nb] = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), fr[st], dp[nb]);
+        __syncthreads();  // P is in LDS
+#pragma unroll
+        for (int nb = 0; nb < BN / 32; ++nb) {
+          uint32_t pd[2][4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f32x4_t pv = sP[pw][nb][i][lane];
+            pd[i >> 1][2 * (i & 1)] = pack2<E>(pv[0] * (dp[nb][4 * i] - delta), pv[1] * (dp[nb][4 * i + 1] - delta));
+            pd[i >> 1][2 * (i & 1) + 1] =
+                pack2<E>(pv[2] * (dp[nb][4 * i + 2] - delta), pv[3] * (dp[nb][4 * i + 3] - delta));
+          }
+          // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int rows0 = nb * 32 + st * 16;
+            const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
+#pragma unroll
+            for (int d = 0; d < DQK / 32; ++d) {
+              const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
+              const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
+              acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
+            }
+          }
+        }
+        if (n + 1 < n_tiles) wait_vmem_all();  // tile n+1 has landed
+      }
+      cC = advance(cC);
+      __syncthreads();
+    }
+    wait_vmem_all();
+    if constexpr (DSW) {
+      if (valid) {
+        uint16_t* dqr = (uint16_t*)P.dq + ((int64_t)row * P.hq + head) * DQK;
+        const float sc = P.scale;
+#pragma unroll
+        for (int d = 0; d < DQK / 32; ++d)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dd = d * 32 + 8 * i + 4 * half;
+            *(u32x2_t*)(dqr + dd) = u32x2_t{pack2<E>(acc[d][4 * i] * sc, acc[d][4 * i + 1] * sc),
+                                             pack2<E>(acc[d][4 * i + 2] * sc, acc[d][4 * i + 3] * sc)};
+          }
+      }
+    }
+  };
+  if (dswave) run(std::true_type{});
+  else run(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -468,7 +763,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
 }
 
 // ---------------------------------------------------------------------------
-// dQ, Q-stationary.  A work-group holds 32 query rows of 4/heads_per_tile row
+// dQ, Q-stationary (Q/K head dim up to 128; 192 runs dq_pair_kernel below).
+// A work-group holds 32 query rows of 4/heads_per_tile row
 // blocks x heads_per_tile heads of one K/V group (one wave each; Q and dO of the
 // lane's query in registers) and walks the 64-key K/V tiles of its schedule.  K
 // and V stream through an NS-deep LDS ring by direct-to-LDS loads issued NS-1
@@ -478,16 +774,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
 // dS^T = P^T (dP^T - Delta),  dQ^T += K^T dS^T (A = transposing reads of K).
 // ---------------------------------------------------------------------------
 template <int DQK>
-constexpr int kDqStages = DQK > 128 ? 3 : 2;
+constexpr int kDqStages = 2;
 template <int DQK>
-constexpr int kDqBlocksPerCu = DQK > 128 ? 1 : 2;
-// With one wave per SIMD (Q/K head dim 192) nothing hides the LDS operand
-// reads, so the MFMA chains run as explicit software pipelines: each operand is
-// read kDqAhead MFMAs before its use.  (With two waves per SIMD this measured
-// the same as the compiler's schedule.)
-template <int DQK>
-constexpr bool kDqPipe = DQK > 128;
-constexpr int kDqAhead = 4;
+constexpr int kDqBlocksPerCu = 2;
 
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdParams P) {
@@ -689,47 +978,11 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
     for (int nb = 0; nb < BN / 32; ++nb) {
       // the S and dP chains alternate, so that consecutive MFMAs are independent
       f32x16_t s = zero16(), dp = zero16();
-      if constexpr (kDqPipe<DQK>) {
-        // the operand of MFMA i is read from LDS while MFMA i - AHEAD issues, in
-        // an order pinned by a scheduling barrier after every MFMA
-        constexpr int MN = QS < VS ? QS : VS, NM = QS + VS, AHEAD = kDqAhead;
-        // op i: S step or dP step (alternating while both chains have steps left)
-        auto is_s = [](int i) { return i < 2 * MN ? (i % 2 == 0) : QS > VS; };
-        auto step = [](int i) { return i < 2 * MN ? i / 2 : MN + (i - 2 * MN); };
-        auto read_op = [&](auto ic) -> u32x4_t {
-          constexpr int i = decltype(ic)::value;
-          if constexpr (is_s(i)) return ko.row(k_s, nb, step(i));
-          else return vo.row(v_s, nb, step(i));
-        };
-        u32x4_t op[AHEAD];
-        static_for<0, AHEAD>([&](auto ic) { op[decltype(ic)::value] = read_op(ic); });
-        static_for<0, NM>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          const u32x4_t a = op[i % AHEAD];
-          if constexpr (i + AHEAD < NM) op[i % AHEAD] = read_op(std::integral_constant<int, i + AHEAD>{});
-          if constexpr (is_s(i)) s = E::mfma32(as_vec8<E>(a), qf[step(i)], s);
-          else dp = E::mfma32(as_vec8<E>(a), of[step(i)], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      } else {
 #pragma unroll
-        for (int st = 0; st < (QS > VS ? QS : VS); ++st) {
-          if (st < QS) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
-          if (st < VS) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
-        }
+      for (int st = 0; st < (QS > VS ? QS : VS); ++st) {
+        if (st < QS) s = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), qf[st], s);
+        if (st < VS) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
       }
-      // dQ^T operands (transposing reads of K): the first AHEAD go out before the
-      // exponentials, which do not need them
-      constexpr int DM = 2 * (DQK / 32), DAHEAD = kDqAhead;
-      u32x4_t kt_op[DAHEAD];
-      if constexpr (kDqPipe<DQK>)
-        static_for<0, DAHEAD>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          const int rows0 = nb * 32 + (i / (DQK / 32)) * 16;
-          const u32x2_t lo = ko.trans(k_s, rows0, 0, i % (DQK / 32));
-          const u32x2_t hi = ko.trans(k_s, rows0, 1, i % (DQK / 32));
-          kt_op[i] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-        });
       // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
       uint32_t pd[2][4];
 #pragma unroll
@@ -749,33 +1002,15 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
         pd[r >> 3][(r & 7) >> 1] = pack2<E>(dsv[0], dsv[1]);
       }
       // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
-      if constexpr (kDqPipe<DQK>) {
-        static_for<0, DM>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          constexpr int st = i / (DQK / 32), d = i % (DQK / 32);
-          const u32x4_t a = kt_op[i % DAHEAD];
-          if constexpr (i + DAHEAD < DM) {
-            constexpr int j = i + DAHEAD;
-            const int rows0 = nb * 32 + (j / (DQK / 32)) * 16;
-            const u32x2_t lo = ko.trans(k_s, rows0, 0, j % (DQK / 32));
-            const u32x2_t hi = ko.trans(k_s, rows0, 1, j % (DQK / 32));
-            kt_op[i % DAHEAD] = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
-          }
-          const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
-          acc[d] = E::mfma32(as_vec8<E>(a), bd, acc[d]);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      } else {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int rows0 = nb * 32 + st * 16;
-          const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
+      for (int st = 0; st < 2; ++st) {
+        const int rows0 = nb * 32 + st * 16;
+        const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
 #pragma unroll
-          for (int d = 0; d < DQK / 32; ++d) {
-            const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
-            const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
-            acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
-          }
+        for (int d = 0; d < DQK / 32; ++d) {
+          const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
+          const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
+          acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
         }
       }
     }
@@ -811,8 +1046,11 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
   };
   // dQ first: it also forms Delta and LSE * log2(e), which dK/dV read, and its
   // last n_zero_ranges work-groups zero the dK/dV rows no local query sees
-  launch(K_BWD_DQ, dq_kernel<E, DQK, DV>,
-         (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups + (unsigned)p.n_zero_ranges);
+  const unsigned dq_grid = (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups + (unsigned)p.n_zero_ranges;
+  if constexpr (DQK > 128)
+    launch(K_BWD_DQ, dq_pair_kernel<E, DQK, DV>, dq_grid, 2 * kThreads);
+  else
+    launch(K_BWD_DQ, dq_kernel<E, DQK, DV>, dq_grid);
   launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
   return e;
 }

@@ -5,7 +5,6 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <type_traits>
 
 namespace cva {
 
@@ -153,16 +152,6 @@ __device__ __forceinline__ void wait_vmem_le(int n) {
     default:
       __builtin_amdgcn_s_waitcnt(0x0F70);
       break;
-  }
-}
-
-// Calls f(std::integral_constant<int, I>{}) for I = B .. E-1, in order, so that
-// every index is a compile-time constant inside f.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
   }
 }
 
