@@ -145,10 +145,12 @@ __device__ __forceinline__ uint32_t key_bits(int lo, int hi) {
 // more than 256 registers and so runs one wave per SIMD).  The same work item
 // as dq_kernel, run by 8 waves: waves w and w+4 (one SIMD) own the same 32
 // query rows of one head.  Wave w (the S wave) holds Q^T, forms S^T = K Q^T and
-// P = exp2(S * scale * log2 e - LSE * log2 e) (masked on partial tiles) and
-// hands P over in fp32 through LDS; wave w+4 (the dS wave) holds dO^T and the
-// dQ accumulators, forms dP^T = V dO^T and, after the mid-tile barrier,
-// dS = P (dP - Delta) and dQ^T += K^T dS^T.  The dS waves also form Delta and
+// P = exp2(S * scale * log2 e - LSE * log2 e) (masked on partial tiles) of both
+// 32-key blocks of a tile; wave w+4 (the dS wave) holds dO^T and forms
+// dP^T = V dO^T of both.  After the mid-tile barrier each forms dS = P (dP -
+// Delta) and dQ^T += K^T dS^T for one block (the dS wave block 0, with P handed
+// over in fp32 through LDS; the S wave block 1, with dP handed over likewise),
+// into partial sums added at the end.  The dS waves also form Delta and
 // LSE * log2 e of the rows (the backward preprocess) and stream the K/V tiles
 // through a 2-deep LDS ring, issuing tile n+1 at the start of tile n.  P is
 // never rounded, so the arithmetic is that of dq_kernel.
@@ -176,7 +178,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
   __shared__ __attribute__((aligned(16))) char sV[NS][BN * VO::RB];
   __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][BN];
   __shared__ __attribute__((aligned(16))) int32_t sSpan[kDqMaxSpans * 4];
-  __shared__ __attribute__((aligned(16))) f32x4_t sP[4][BN / 32][4][64];  // pair, key block, r/4, lane
+  __shared__ __attribute__((aligned(16))) f32x4_t sP[4][4][64];   // P of key block 0: pair, r/4, lane
+  __shared__ __attribute__((aligned(16))) f32x4_t sDP[4][4][64];  // dP of key block 1: pair, r/4, lane
+  __shared__ __attribute__((aligned(16))) float sDelta[4][64];    // Delta of the pair's rows, per lane
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -320,6 +324,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
         P.delta[(int64_t)head * P.t_loc + row] = delta;
         P.lse2[(int64_t)head * P.t_loc + row] = lse2;
       }
+      sDelta[pw][lane] = delta;  // for the S wave (read after the next barrier)
     } else {
       if (valid) {
         const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
@@ -340,9 +345,33 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
       }
       __syncthreads();
     }
-    f32x16_t acc[DSW ? DQK / 32 : 1];
+    // dQ^T partial sums: the dS wave over key block 0 of every tile, the S wave
+    // over key block 1 (added together at the end)
+    f32x16_t acc[DQK / 32];
 #pragma unroll
-    for (int d = 0; d < (DSW ? DQK / 32 : 1); ++d) acc[d] = zero16();
+    for (int d = 0; d < DQK / 32; ++d) acc[d] = zero16();
+    if constexpr (!DSW) delta = sDelta[pw][lane];
+    // dS^T of one key block from P and dP (lane layout of the S^T accumulators),
+    // packed for the dQ MFMA, then dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
+    auto ds_dq = [&](const char* k_s, int nb, const f32x4_t (&pv)[4], const f32x4_t (&dv)[4]) {
+      uint32_t pd[2][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pd[i >> 1][2 * (i & 1)] = pack2<E>(pv[i][0] * (dv[i][0] - delta), pv[i][1] * (dv[i][1] - delta));
+        pd[i >> 1][2 * (i & 1) + 1] = pack2<E>(pv[i][2] * (dv[i][2] - delta), pv[i][3] * (dv[i][3] - delta));
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int rows0 = nb * 32 + st * 16;
+        const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
+#pragma unroll
+        for (int d = 0; d < DQK / 32; ++d) {
+          const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
+          const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
+          acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
+        }
+      }
+    };
     Cur cC = nspan > 0 ? span_at(0) : Cur{0, 0, 0, 0};  // tile being computed
     for (int n = 0; n < n_tiles; ++n) {
       const char* k_s = sK[n % NS];
@@ -350,7 +379,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
       const int kb0 = cC.t * BN;
       const bool partial = cC.partial != 0;
       if constexpr (!DSW) {
-        // ---- S wave: S^T and P of both 32-key blocks (phase 1) ----
+        // ---- S wave: S^T and P of both 32-key blocks (phase 1); dS and dQ^T of
+        // key block 1 (phase 2) ----
+        f32x4_t p1[4];  // P of key block 1, kept in registers
 #pragma unroll
         for (int nb = 0; nb < BN / 32; ++nb) {
           f32x16_t sc = zero16();
@@ -371,12 +402,18 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
               }
               pv[j] = __builtin_amdgcn_exp2f(x);
             }
-            sP[pw][nb][i][lane] = pv;
+            if (nb == 0) sP[pw][i][lane] = pv;
+            else p1[i] = pv;
           }
         }
-        __syncthreads();  // P is in LDS
+        __syncthreads();  // P of block 0 and dP of block 1 are in LDS
+        f32x4_t dv1[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dv1[i] = sDP[pw][i][lane];
+        ds_dq(k_s, 1, p1, dv1);
       } else {
-        // ---- dS wave: the next tile's loads and dP^T (phase 1); dS, dQ^T (phase 2) ----
+        // ---- dS wave: the next tile's loads and dP^T of both key blocks (phase 1);
+        // dS and dQ^T of key block 0 (phase 2) ----
         if (n + NS - 1 < n_tiles) issue(n + NS - 1);  // into the slot tile n-1 used
         f32x16_t dp[BN / 32];
 #pragma unroll
@@ -385,36 +422,49 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
         for (int st = 0; st < VS; ++st)
 #pragma unroll
           for (int nb = 0; nb < BN / 32; ++nb) dp[nb] = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), fr[st], dp[nb]);
-        __syncthreads();  // P is in LDS
 #pragma unroll
-        for (int nb = 0; nb < BN / 32; ++nb) {
-          uint32_t pd[2][4];
+        for (int i = 0; i < 4; ++i)
+          sDP[pw][i][lane] = f32x4_t{dp[1][4 * i], dp[1][4 * i + 1], dp[1][4 * i + 2], dp[1][4 * i + 3]};
+        __syncthreads();  // P of block 0 and dP of block 1 are in LDS
+        f32x4_t p0[4], dv0[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const f32x4_t pv = sP[pw][nb][i][lane];
-            pd[i >> 1][2 * (i & 1)] = pack2<E>(pv[0] * (dp[nb][4 * i] - delta), pv[1] * (dp[nb][4 * i + 1] - delta));
-            pd[i >> 1][2 * (i & 1) + 1] =
-                pack2<E>(pv[2] * (dp[nb][4 * i + 2] - delta), pv[3] * (dp[nb][4 * i + 3] - delta));
-          }
-          // dQ^T[d][q] += sum_key K^T[d][key] dS^T[key][q]
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int rows0 = nb * 32 + st * 16;
-            const typename E::vec8 bd = as_vec8<E>(u32x4_t{pd[st][0], pd[st][1], pd[st][2], pd[st][3]});
-#pragma unroll
-            for (int d = 0; d < DQK / 32; ++d) {
-              const u32x2_t lo = ko.trans(k_s, rows0, 0, d);
-              const u32x2_t hi = ko.trans(k_s, rows0, 1, d);
-              acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bd, acc[d]);
-            }
-          }
+        for (int i = 0; i < 4; ++i) {
+          p0[i] = sP[pw][i][lane];
+          dv0[i] = f32x4_t{dp[0][4 * i], dp[0][4 * i + 1], dp[0][4 * i + 2], dp[0][4 * i + 3]};
         }
+        ds_dq(k_s, 0, p0, dv0);
         if (n + 1 < n_tiles) wait_vmem_all();  // tile n+1 has landed
       }
       cC = advance(cC);
       __syncthreads();
     }
     wait_vmem_all();
+    // the S wave's partial dQ^T joins the dS wave's through LDS, two 32-column
+    // blocks at a time (sDP and sP are free once the tiles are done)
+#pragma unroll
+    for (int d = 0; d < DQK / 32; d += 2) {
+      if constexpr (!DSW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sDP[pw][i][lane] = f32x4_t{acc[d][4 * i], acc[d][4 * i + 1], acc[d][4 * i + 2], acc[d][4 * i + 3]};
+          sP[pw][i][lane] =
+              f32x4_t{acc[d + 1][4 * i], acc[d + 1][4 * i + 1], acc[d + 1][4 * i + 2], acc[d + 1][4 * i + 3]};
+        }
+      }
+      __syncthreads();
+      if constexpr (DSW) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const f32x4_t x = sDP[pw][i][lane], y = sP[pw][i][lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[d][4 * i + j] += x[j];
+            acc[d + 1][4 * i + j] += y[j];
+          }
+        }
+      }
+      __syncthreads();
+    }
     if constexpr (DSW) {
       if (valid) {
         uint16_t* dqr = (uint16_t*)P.dq + ((int64_t)row * P.hq + head) * DQK;
