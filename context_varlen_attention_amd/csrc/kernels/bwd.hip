@@ -506,7 +506,6 @@ constexpr int kDkvPairStages = DQK > 128 ? 2 : 4;
 
 template <typename E, int DQK, int DV>
 __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P) {
-  constexpr int NT = 2 * kThreads;
   constexpr int BQ = 64;           // queries per Q tile
   constexpr int QS = DQK / 16;     // reduction steps over Dqk
   constexpr int VS = DV / 16;      // reduction steps over Dv

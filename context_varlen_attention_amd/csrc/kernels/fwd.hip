@@ -48,8 +48,9 @@ namespace {
 
 constexpr int kThreads = 512;              // 8 waves: two ping-pong groups of 4
 constexpr int kBN = 64;                    // keys per K/V tile
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: the base may lag the row max by 2^8
-constexpr float kRescaleLimit = 256.0f;    // 2^kRescaleThreshold
+// lazy rescaling: the exponent base may lag the row maximum by up to 8 (log2
+// units), i.e. a P value may reach 2^8 before the base moves
+constexpr float kRescaleLimit = 256.0f;
 constexpr int kReadAhead = 6;              // MFMAs between an LDS operand read and its use
 
 // LDS layouts (16-byte chunks, XOR-swizzled so that the MFMA operand reads are
@@ -352,7 +353,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   constexpr int NI = TL::NIDX;
   constexpr int NS = kStages<DQK>;
   constexpr int NIR = 2 * NS;       // index ring slots
-  constexpr int PER_BATCH = TL::KN + TL::VN + 1;  // loads per wave per full batch
   constexpr uint32_t KBUF = kBN * DQK * 2, VBUF = kBN * DV * 2;  // bytes per tile buffer
   __shared__ __attribute__((aligned(16))) uint16_t sK[NS][kBN * DQK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NS][kBN * DV];
