@@ -618,7 +618,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     {
       // operand reads run kReadAhead MFMAs ahead of their MFMA (the compiler
       // would otherwise issue each read just before its use and stall on it)
-      constexpr int PVM = 4 * DB, SM = 2 * KSTEPS, AHEAD = DQK > 128 ? 2 : kReadAhead;
+      constexpr int PVM = 4 * DB, SM = 2 * KSTEPS, AHEAD = DQK > 128 ? 3 : kReadAhead;
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
 #pragma unroll
       for (int i = 0; i < PVM; ++i) {
