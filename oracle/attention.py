@@ -145,7 +145,7 @@ def fwd_full_ref(w, q, k, v, scale=None):
     return o, lse
 
 
-def bwd_ref(w, q, k, v, do_local, scale=None, heads=None):
+def bwd_ref(w, q, k, v, do_local, scale=None, heads=None, rows=None, block=None):
     """Backward on rank (w.cp_size, w.rank)'s share.
 
     q, k, v: full unsplit tensors.  do_local: [T_loc, Hq, Dv] gradient of the
@@ -153,32 +153,42 @@ def bwd_ref(w, q, k, v, do_local, scale=None, heads=None):
     dk [T, Hkv, Dqk], dv [T, Hkv, Dv], all float64.  ``heads`` restricts the
     work to those query heads (their dQ, and their K/V groups' dK/dV -- complete
     only for groups whose every head is listed); other entries stay zero.
+
+    ``rows`` (local row ids) restricts the work to those query rows: their dQ
+    and their share of dK/dV.  dK and dV are sums over query rows of per-row
+    terms (the index_add_ of per-segment gradients in MindSpeed RFC section
+    3.1), so the shares of disjoint row sets add up to the full gradient.
+    ``block`` takes the rows of a sub-sequence that many at a time and adds the
+    blocks' shares (the same sum in another order; None: all rows at once).
     """
     scale = default_scale(w.d_qk) if scale is None else float(scale)
     G = w.hq // w.hkv
     cu = np.asarray(w.cu_seqlens, dtype=np.int64)
     T = int(cu[-1])
-    loc, groups = _local_rows_by_seq(w)
+    loc, groups = _local_rows_by_seq(w, rows)
     dq = np.zeros((len(loc), w.hq, w.d_qk))
     dk_seq = np.zeros((T, w.hkv, w.d_qk))   # packed (unsplit) order first
     dv_seq = np.zeros((T, w.hkv, w.d_v))
     dO = np.asarray(do_local, dtype=np.float64)
-    for i, (lrows, pos) in groups.items():
+    for i, (lrows_all, pos_all) in groups.items():
         s0, L = int(cu[i]), int(cu[i + 1] - cu[i])
-        lrows, pos = np.asarray(lrows), np.asarray(pos)
-        Qi = np.asarray(q[s0 + pos], dtype=np.float64)
+        lrows_all, pos_all = np.asarray(lrows_all), np.asarray(pos_all)
         Ki = np.asarray(k[s0: s0 + L], dtype=np.float64)
         Vi = np.asarray(v[s0: s0 + L], dtype=np.float64)
-        M = _mask_for(w, i, L, pos)
-        for h in (range(w.hq) if heads is None else heads):
-            g = h // G
-            P, _ = softmax_rows_ref(scale * (Qi[:, h] @ Ki[:, g].T), M)
-            dOh = dO[lrows, h, :]
-            dv_seq[s0: s0 + L, g] += P.T @ dOh
-            dP = dOh @ Vi[:, g].T
-            dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
-            dq[lrows, h] = scale * (dS @ Ki[:, g])
-            dk_seq[s0: s0 + L, g] += scale * (dS.T @ Qi[:, h])
+        step = len(lrows_all) if block is None else int(block)
+        for b in range(0, len(lrows_all), step):
+            lrows, pos = lrows_all[b: b + step], pos_all[b: b + step]
+            Qi = np.asarray(q[s0 + pos], dtype=np.float64)
+            M = _mask_for(w, i, L, pos)
+            for h in (range(w.hq) if heads is None else heads):
+                g = h // G
+                P, _ = softmax_rows_ref(scale * (Qi[:, h] @ Ki[:, g].T), M)
+                dOh = dO[lrows, h, :]
+                dv_seq[s0: s0 + L, g] += P.T @ dOh
+                dP = dOh @ Vi[:, g].T
+                dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
+                dq[lrows, h] = scale * (dS @ Ki[:, g])
+                dk_seq[s0: s0 + L, g] += scale * (dS.T @ Qi[:, h])
     row_of = rank_major_row_of_position(cu, w.cp_size)
     dk = np.zeros_like(dk_seq)
     dv = np.zeros_like(dv_seq)

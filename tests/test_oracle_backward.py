@@ -18,6 +18,25 @@ from oracle.split import rank_local_positions, rank_major_row_of_position
 from tests.test_oracle_attention import _wl
 
 
+def _torch_mask(mask, L, bounds):
+    """The test cases' masks written directly in torch (sink 2, window 5 for lambda)."""
+    qq = torch.arange(L)[:, None]
+    kk = torch.arange(L)[None, :]
+    if mask == "causal":
+        return kk <= qq
+    if mask == "lambda":
+        return (kk <= qq) & ((kk < 2) | (qq - kk < 5))
+    b = [int(x) for x in bounds]
+    M = torch.zeros(L, L, dtype=torch.bool)
+    M[:b[0], :b[0]] = torch.tril(torch.ones(b[0], b[0], dtype=torch.bool))
+    st = b[0]
+    for e in b[1:]:
+        M[st:e, :b[0]] = True
+        M[st:e, st:e] = torch.tril(torch.ones(e - st, e - st, dtype=torch.bool))
+        st = e
+    return M
+
+
 def _loss(w, q, k, v, do_loc, scale):
     o, _ = oracle.fwd_ref(w, q, k, v, scale)
     return float((o * do_loc).sum())
@@ -70,22 +89,7 @@ def test_torch_autograd(R, r, mask):
     outs = []
     for i in range(len(cu) - 1):
         s0, s1 = cu[i], cu[i + 1]
-        L = s1 - s0
-        qq = torch.arange(L)[:, None]
-        kk = torch.arange(L)[None, :]
-        if mask == "causal":
-            M = kk <= qq
-        elif mask == "lambda":
-            M = (kk <= qq) & ((kk < 2) | (qq - kk < 5))
-        else:
-            b = [int(x) for x in w.branch_bounds[i]]
-            M = torch.zeros(L, L, dtype=torch.bool)
-            M[:b[0], :b[0]] = torch.tril(torch.ones(b[0], b[0], dtype=torch.bool))
-            st = b[0]
-            for e in b[1:]:
-                M[st:e, :b[0]] = True
-                M[st:e, st:e] = torch.tril(torch.ones(e - st, e - st, dtype=torch.bool))
-                st = e
+        M = _torch_mask(mask, s1 - s0, None if w.branch_bounds is None else w.branch_bounds[i])
         Q = tq[s0:s1].permute(1, 0, 2)
         K = tk[s0:s1].permute(1, 0, 2).repeat_interleave(G, dim=0)
         V = tv[s0:s1].permute(1, 0, 2).repeat_interleave(G, dim=0)
@@ -123,3 +127,45 @@ def test_sum_over_ranks_equals_unsplit(R, mask):
     row_of = rank_major_row_of_position(cu, R)
     np.testing.assert_allclose(dk_sum[row_of], dk1, atol=1e-12)
     np.testing.assert_allclose(dv_sum[row_of], dv1, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask", ["causal", "lambda", "shared_prefix"])
+def test_row_subset_and_blocks_against_autograd(mask):
+    """bwd_ref(rows=S, block=b): dQ of the rows in S and their share of dK/dV,
+    which is what autograd gives when dO is zero outside S (dK and dV are sums
+    over query rows)."""
+    R, r = 2, 1
+    lens = [6 * R, 12 * R]
+    c = dict(lens=lens, R=R, r=r, hq=4, hkv=2, d=8, mask=mask, sink=2, window=5,
+             bounds=[[2 * R, 4 * R, 6 * R], [4 * R, 8 * R, 12 * R]])
+    w = _wl(c, dv=6)
+    q, k, v, do_full = synth.random_tensors(w, 35)
+    cu = [int(x) for x in w.cu_seqlens]
+    loc = rank_local_positions(cu, R, r)
+    sel = [1, 2, 3, 7, 8, 13, 17]  # local rows, spread over both sub-sequences
+    scale = 0.4
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    G = w.hq // w.hkv
+    outs = []
+    for i in range(len(cu) - 1):
+        s0, s1 = cu[i], cu[i + 1]
+        M = _torch_mask(mask, s1 - s0, None if w.branch_bounds is None else w.branch_bounds[i])
+        Q = tq[s0:s1].permute(1, 0, 2)
+        K = tk[s0:s1].permute(1, 0, 2).repeat_interleave(G, dim=0)
+        V = tv[s0:s1].permute(1, 0, 2).repeat_interleave(G, dim=0)
+        outs.append(torch.nn.functional.scaled_dot_product_attention(
+            Q, K, V, attn_mask=M, scale=scale).permute(1, 0, 2))
+    O = torch.cat(outs, 0)
+    dO_full = torch.zeros_like(O)
+    toks = [loc[n] for n in sel]
+    dO_full[toks] = torch.tensor(do_full[toks], dtype=torch.float64)
+    (O * dO_full).sum().backward()
+    do_loc = np.asarray(do_full[loc], dtype=np.float64)
+    for block in (None, 1, 2, 5):
+        dq, dk, dv = oracle.bwd_ref(w, q, k, v, do_loc, scale, rows=sel, block=block)
+        row_of = rank_major_row_of_position(cu, R)
+        np.testing.assert_allclose(dq[sel], tq.grad.numpy()[toks], atol=1e-11)
+        others = np.setdiff1d(np.arange(len(loc)), sel)
+        assert (dq[others] == 0).all()
+        np.testing.assert_allclose(dk[row_of], tk.grad.numpy(), atol=1e-11)
+        np.testing.assert_allclose(dv[row_of], tv.grad.numpy(), atol=1e-11)
