@@ -19,7 +19,10 @@ MI355X peak) is measured on its own stream during the timed steps while the
 other kernels run without instrumentation.  ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same workload on this host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gqa16k]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long128k]
+
+The default workload is the largest single-GPU one: one 131072-token sequence,
+CP rank 3 of 8, 32/8 heads, D=128, bf16, causal, forward + backward.
 """
 from __future__ import annotations
 
@@ -102,12 +105,63 @@ class LookAheadPlanner:
 
 
 def kernel_flops(w, pairs):
+    """Algorithmic flops per launch: the useful backward 2*N*Hq*(3*Dqk+2*Dv)
+    split over the two backward kernels without counting anything twice.  The
+    dK/dV kernel owns the score recompute (Dqk), dP (Dv), dV (Dv) and dK (Dqk);
+    the dQ kernel's own product is dQ (Dqk) -- its second score recompute and dP
+    are reported as issued work (kernel_flops_issued), not as useful work."""
     hq, dqk, dv = w.hq, w.d_qk, w.d_v
     return {
         "fwd": 2 * pairs * hq * (dqk + dv),
         "bwd_dkdv": 2 * pairs * hq * (2 * dqk + 2 * dv),
-        "bwd_dq": 2 * pairs * hq * (2 * dqk + dv),
+        "bwd_dq": 2 * pairs * hq * dqk,
     }
+
+
+def kernel_flops_issued(w, pairs):
+    """Flops a kernel executes on visible pairs, recompute included (where it
+    differs from the algorithmic count)."""
+    hq, dqk, dv = w.hq, w.d_qk, w.d_v
+    return {"bwd_dq": 2 * pairs * hq * (2 * dqk + dv)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def device_info(torch, dev):
+    """Name, architecture, compute units and peak engine clock of the GPU, and
+    the dense 16-bit MFMA peak they give (4096 flop per clock per CU)."""
+    import re
+    import subprocess
+    props = torch.cuda.get_device_properties(dev)
+    info = {"name": props.name, "arch": props.gcnArchName.split(":")[0],
+            "compute_units": int(props.multi_processor_count), "max_clock_mhz": None}
+    try:
+        out = subprocess.run(["rocminfo"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                             text=True, timeout=60).stdout
+        for agent in out.split("Agent ")[1:]:
+            if re.search(r"Name:\s+" + re.escape(info["arch"]) + r"\b", agent):
+                m = re.search(r"Max Clock Freq\. \(MHz\):\s+(\d+)", agent)
+                c = re.search(r"Compute Unit:\s+(\d+)", agent)
+                if m:
+                    info["max_clock_mhz"] = int(m.group(1))
+                if c:
+                    info["compute_units"] = int(c.group(1))
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if info["max_clock_mhz"]:
+        info["dense_16bit_peak_tflops"] = (info["compute_units"] * info["max_clock_mhz"] * 1e6
+                                           * 4096 / 1e12)
+    return info
 
 
 def kernel_bytes(w):
@@ -155,38 +209,67 @@ def measured_traffic(kernel, workload):
     return None
 
 
-def cpu_baseline(w, budget_s=12.0):
-    """fp64 oracle forward+backward on a bounded sample: whole K/V head groups."""
+def cpu_baseline(w, budget_s=12.0, block_rows=256):
+    """The fp64 oracle, forward then backward, on a bounded sample of the same
+    batch: blocks of ``block_rows`` local rows of one query head at a time
+    (the blocks walk through the rank's rows, the heads rotate), until
+    ``budget_s`` of CPU time is spent.  Useful flops are the sampled rows'
+    visible pairs times the same per-pair counts as the GPU's.
+
+    The oracle reads K/V over whole sub-sequences and Q/dO at the sampled rows,
+    so only K and V are drawn in full; Q and dO are drawn at the sampled rows
+    (the values do not change the work)."""
     import oracle
+    from oracle.masks import mask_rows_ref
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing: report the visible core count
         threads = os.cpu_count()
-    q, k, v, do = synth.make_tensors(w)
-    loc = oracle.rank_local_positions(w.cu_seqlens, w.cp_size, w.rank)
-    do_loc = do[loc]
-    G = w.hq // w.hkv
-    pairs = oracle.visible_pairs_ref(w)
-    done_heads, elapsed = 0, 0.0
-    for g in range(w.hkv):
-        heads = list(range(g * G, (g + 1) * G))
+    rng = np.random.default_rng([synth.CONFIG_IDS.get(w.name, 0), 7])
+    T = w.total_tokens
+    cu = np.asarray(w.cu_seqlens, dtype=np.int64)
+    loc = np.asarray(oracle.rank_local_positions(cu, w.cp_size, w.rank), dtype=np.int64)
+    T_loc = len(loc)
+    k = rng.standard_normal((T, w.hkv, w.d_qk), dtype=np.float32)
+    v = rng.standard_normal((T, w.hkv, w.d_v), dtype=np.float32)
+    q = np.zeros((T, w.hq, w.d_qk), dtype=np.float32)      # filled at the sampled rows
+    do_loc = np.zeros((T_loc, w.hq, w.d_v), dtype=np.float32)
+    n_blocks = max(1, T_loc // block_rows)
+    order = np.random.default_rng(5).permutation(n_blocks)
+    done_pairs, elapsed, n_rows, heads_used = 0, 0.0, 0, set()
+    for it, b in enumerate(order):
+        rows = np.arange(b * block_rows, min(T_loc, (b + 1) * block_rows))
+        h = int(it % w.hq)
+        q[loc[rows], h] = rng.standard_normal((len(rows), w.d_qk), dtype=np.float32)
+        do_loc[rows, h] = rng.standard_normal((len(rows), w.d_v), dtype=np.float32)
         t0 = time.perf_counter()
-        oracle.fwd_ref(w, q, k, v, heads=heads)
-        oracle.bwd_ref(w, q, k, v, do_loc, heads=heads)
+        oracle.fwd_ref(w, q, k, v, rows=rows, heads=[h])
+        oracle.bwd_ref(w, q, k, v, do_loc, heads=[h], rows=rows)
         elapsed += time.perf_counter() - t0
-        done_heads += G
+        toks = loc[rows]
+        seq = np.searchsorted(cu, toks, side="right") - 1
+        for i in np.unique(seq):
+            L = int(cu[i + 1] - cu[i])
+            pos = toks[seq == i] - cu[i]
+            bb = None if w.branch_bounds is None else w.branch_bounds[i]
+            done_pairs += int(mask_rows_ref(w.mask, L, pos, w.sink, w.window, bb,
+                                            getattr(w, "block", 0)).sum())
+        n_rows += len(rows)
+        heads_used.add(h)
         if elapsed >= budget_s:
             break
-    flops = 2 * pairs * done_heads * ((w.d_qk + w.d_v) + (3 * w.d_qk + 2 * w.d_v))
+    flops = 2 * done_pairs * ((w.d_qk + w.d_v) + (3 * w.d_qk + 2 * w.d_v))
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"fp64 numpy oracle fwd+bwd on {done_heads} of {w.hq} query heads "
-                  f"({done_heads // G} K/V groups), all local rows of the same batch; "
-                  f"{elapsed:.1f} s; useful flops counted as on the GPU",
+        "sample": f"fp64 numpy oracle fwd+bwd on {n_rows} of {T_loc} local rows x {len(heads_used)} "
+                  f"of {w.hq} query heads (blocks of {block_rows} rows, one head each) of the "
+                  f"same batch; {elapsed:.1f} s; useful flops of the sampled rows counted as on "
+                  f"the GPU",
+        "cpu_model": cpu_model(),
         "seconds": elapsed,
     }
 
@@ -216,7 +299,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gqa16k", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--workload", default="long128k", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix", "blockwise"])
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
     ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
@@ -319,6 +402,7 @@ def main():
     value = (fl_fwd + fl_bwd) / (ms_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     kfl = kernel_flops(w, pairs)
+    kfl_issued = kernel_flops_issued(w, pairs)
     kby = kernel_bytes(w)
     kernels = {}
     for name, (n, tot) in prof_times.items():
@@ -333,7 +417,9 @@ def main():
                "measured": "timed region" if steps_seen == args.steps and name == dom else "profile pass"}
         if name in kfl:
             rec.update(bound="mfma", achieved=kfl[name] / (avg * 1e-3) / 1e12, unit="TFLOP/s",
-                       peak=peak)
+                       peak=peak, flops_per_launch=kfl[name])
+            if name in kfl_issued:
+                rec["issued_tflops"] = kfl_issued[name] / (avg * 1e-3) / 1e12
         elif name in kby:
             rec.update(bound="hbm", achieved=kby[name] / (avg * 1e-3) / 1e9, unit="GB/s",
                        peak=PEAK_HBM_GBS)
@@ -373,12 +459,14 @@ def main():
         "plan_ms_host": 1e3 * float(np.mean(planner.build_s)) if planner.build_s else None,
         "roofline": roofline,
         "kernels": kernels,
+        "device": device_info(torch, dev),
     }
     del keep
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a bounded sample (cpu_baseline)")
         cb = cpu_baseline(w)
-        out["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample")}
+        out["cpu_baseline"] = {kk: cb[kk] for kk in ("value", "unit", "cores", "kind", "sample",
+                                                     "cpu_model")}
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

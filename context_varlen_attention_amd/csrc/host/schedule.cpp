@@ -582,7 +582,13 @@ void build_fwd_split(Plan& p) {
     }
     total += steps[t] * groups;
   }
-  const int64_t cap = std::max<int64_t>(kSplitMinSteps, (total + kSplitCUs - 1) / kSplitCUs);
+  int64_t cap = std::max<int64_t>(kSplitMinSteps, (total + kSplitCUs - 1) / kSplitCUs);
+  // CVA_FWD_SPLIT_CAP in the environment replaces the cut length (K/V tiles per
+  // piece, >= 1), e.g. to cut the long Q tiles of a batch the default leaves whole
+  if (const char* v = std::getenv("CVA_FWD_SPLIT_CAP")) {
+    const long c = std::strtol(v, nullptr, 10);
+    if (c >= 1) cap = c;
+  }
   p.fwd_split_cap = (int32_t)cap;
   struct Item { std::array<int32_t, QT_INTS> rec; std::vector<int32_t> spans; int32_t slot; int64_t cost; };
   std::vector<Item> items;

@@ -175,7 +175,9 @@ cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const 
  * with online softmax; a query block's K/V range is cut into pieces whose
  * partial outputs are merged through their log-sum-exp).  The plan cuts every
  * forward Q tile whose K/V walk is longer than the average work per compute
- * unit into up to 8 pieces; each piece writes an fp32 partial output and LSE
+ * unit (or, when the environment variable CVA_FWD_SPLIT_CAP holds an integer
+ * >= 1 at cva_plan_create, longer than that many 64-key K/V tiles) into up to 8
+ * pieces; each piece writes an fp32 partial output and LSE
  * to the workspace and a second kernel merges them into o and lse.  Same
  * arguments and results as cva_fwd, plus a caller-owned device workspace of at
  * least cva_fwd_workspace_bytes bytes (256-byte aligned) that must not be used

@@ -1,16 +1,19 @@
 """Backward parity: libcva dQ / rank-major dK / dV on the GPU against the fp64 oracle.
 
 Small shapes are compared element by element on every output (all masks, GQA,
-expanded-MLA head dims, several CP ranks); the 32k MLA-shape and 16k GQA
-workloads run at full size and are compared on a subset of heads (all rows of
-those heads).
+expanded-MLA head dims, several CP ranks).  The full-size workloads (16k GQA,
+128k single sequence, sparse masks, 32k MLA shape) run in the benchmark's
+launch configuration and are compared on whole K/V head groups: dQ of every
+local row of the group's query heads and the group's complete rank-major dK/dV
+(every dK/dV work item of that K/V head).
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import assert_close, device_inputs, plan_for
+from tests.gpu_helpers import (assert_close, bwd_ref_heads, device_inputs, plan_for,
+                               workload_tensors)
 
 pytestmark = pytest.mark.gpu
 
@@ -26,17 +29,21 @@ def _run(w, q, k, v, do, heads=None, scale=None):
     dq, dk, dv = cva.bwd(plan, tq, tk, tv, o, lse, tdo, softmax_scale=scale)
     torch.cuda.synchronize()
     loc = cva.local_token_ids(w.cu_seqlens, w.cp_size, w.rank)
-    rdq, rdk, rdv = oracle.bwd_ref(w, q, k, v, do[loc], scale=scale, heads=heads)
+    if heads is None:
+        rdq, rdk, rdv = oracle.bwd_ref(w, q, k, v, do[loc], scale=scale)
+    else:
+        rdq, rdk, rdv = bwd_ref_heads(w, q, k, v, do[loc], heads, scale=scale)
     dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
     if heads is not None:
         G = w.hq // w.hkv
         groups = sorted({h // G for h in heads})
         dq, rdq = dq[:, heads], rdq[:, heads]
         dk, rdk, dv, rdv = dk[:, groups], rdk[:, groups], dv[:, groups], rdv[:, groups]
-    e1 = assert_close(dq, rdq, w.dtype, "dQ")
-    e2 = assert_close(dk, rdk, w.dtype, "dK")
-    e3 = assert_close(dv, rdv, w.dtype, "dV")
-    print(f"[bwd]   max |err| dQ {e1:.2e} dK {e2:.2e} dV {e3:.2e}", flush=True)
+    e1, r1 = assert_close(dq, rdq, w.dtype, "dQ")
+    e2, r2 = assert_close(dk, rdk, w.dtype, "dK")
+    e3, r3 = assert_close(dv, rdv, w.dtype, "dV")
+    print(f"[bwd]   max |err| dQ {e1:.2e} dK {e2:.2e} dV {e3:.2e}; headroom ratio "
+          f"dQ {r1:.3f} dK {r2:.3f} dV {r3:.3f}", flush=True)
     return dq, dk, dv
 
 
@@ -76,20 +83,37 @@ def test_tiny_bf16_custom_scale():
     _run(w, q, k, v, do, scale=0.3)
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-def test_mla32k_three_heads(dtype):
-    w = synth.make_workload("mla32k", dtype=dtype)
-    q, k, v, do = synth.make_tensors(w)
-    _run(w, q, k, v, do, heads=[0, 7, 15])
+def test_mla32k_heads_0_15(dtype):
+    """Q/K head dim 192: every local row of heads 0 and 15 (each its own K/V head)."""
+    w, (q, k, v, do) = workload_tensors("mla32k", dtype=dtype)
+    _run(w, q, k, v, do, heads=[0, 15])
 
 
-def test_gqa16k_one_group():
+@pytest.mark.timeout(600)
+def test_gqa16k_first_and_last_group():
     """Full 16k GQA workload in the benchmark's launch configuration: all rows of
-    one K/V group's four query heads (dQ of each, and the group's complete
-    dK / dV)."""
-    w = synth.make_workload("gqa16k")
-    q, k, v, do = synth.make_tensors(w)
-    _run(w, q, k, v, do, heads=[4, 5, 6, 7])
+    the first and the last K/V group (dQ of their eight query heads, and the two
+    groups' complete dK / dV)."""
+    w, (q, k, v, do) = workload_tensors("gqa16k")
+    _run(w, q, k, v, do, heads=[0, 1, 2, 3, 28, 29, 30, 31])
+
+
+@pytest.mark.timeout(900)
+def test_long128k_last_group():
+    """The 131072-token sequence, rank 3 of 8: dQ of all 16384 local rows of
+    query heads 28..31 and K/V head 7's complete rank-major dK / dV."""
+    w, (q, k, v, do) = workload_tensors("long128k")
+    _run(w, q, k, v, do, heads=[28, 29, 30, 31])
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("mask", ["lambda", "shared_prefix", "blockwise"])
+def test_sparse8_one_head(mask):
+    """The 8-sequence sparse-mask batch (81408 rows): head 15's dQ, dK and dV."""
+    w, (q, k, v, do) = workload_tensors("sparse8", mask=mask)
+    _run(w, q, k, v, do, heads=[15])
 
 
 def test_uncovered_rows_are_zero_and_repeat_is_bitwise():

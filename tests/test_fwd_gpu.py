@@ -1,25 +1,29 @@
 """Forward parity: libcva on the GPU against the fp64 oracle.
 
-Small cases are compared element by element on every output; the full-size
+Small cases are compared element by element on every output.  The full-size
 workloads (16k GQA, 128k single sequence, sparse masks, MLA shape) run in the
-same launch configuration bench.py uses and are compared on sampled rows the
-oracle computes one by one.
+same launch configuration bench.py uses and are compared on every row of at
+least one whole K/V head group -- so every forward work item of that group,
+including the longest prefixes -- plus sampled rows of every head.
 """
+import functools
+
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import assert_close, device_inputs, plan_for
+from tests.gpu_helpers import (assert_close, device_inputs, fwd_ref_heads, plan_for,
+                               workload_tensors)
 
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, q, k, v, rows=None, scale=None, split=False):
+def _run(w, q, k, v, rows=None, scale=None, split=False, heads=None, ref=None):
     import torch
     import context_varlen_attention_amd as cva
     print(f"[fwd] {w.name} {w.dtype} mask={w.mask} R={w.cp_size} r={w.rank} T={w.total_tokens} "
-          f"H={w.hq}/{w.hkv} D={w.d_qk}/{w.d_v} split={split}", flush=True)
+          f"H={w.hq}/{w.hkv} D={w.d_qk}/{w.d_v} split={split} heads={heads}", flush=True)
     plan = plan_for(w)
     dq_, dk_, dv_ = device_inputs(w, q, k, v)
     if split:
@@ -28,12 +32,18 @@ def _run(w, q, k, v, rows=None, scale=None, split=False):
     torch.cuda.synchronize()
     o = o.float().cpu().numpy()
     lse = lse.cpu().numpy()
-    o_ref, lse_ref = oracle.fwd_ref(w, q, k, v, scale=scale, rows=rows)
+    if ref is None:
+        ref = (oracle.fwd_ref(w, q, k, v, scale=scale, rows=rows) if heads is None
+               else fwd_ref_heads(w, q, k, v, heads, rows=rows, scale=scale))
+    o_ref, lse_ref = ref
     if rows is not None:
         o, o_ref, lse, lse_ref = o[rows], o_ref[rows], lse[:, rows], lse_ref[:, rows]
-    eo = assert_close(o, o_ref, w.dtype, "O")
-    el = assert_close(lse, lse_ref, w.dtype, "LSE")
-    print(f"[fwd]   max |err| O {eo:.2e} LSE {el:.2e}", flush=True)
+    if heads is not None:
+        o, o_ref, lse, lse_ref = o[:, heads], o_ref[:, heads], lse[heads], lse_ref[heads]
+    eo, ro = assert_close(o, o_ref, w.dtype, "O")
+    el, rl = assert_close(lse, lse_ref, w.dtype, "LSE")
+    print(f"[fwd]   max |err| O {eo:.2e} LSE {el:.2e}; headroom ratio O {ro:.3f} LSE {rl:.3f}",
+          flush=True)
     return plan
 
 
@@ -115,23 +125,59 @@ def test_gqa16k_all_rows():
     _run(w, q, k, v)
 
 
+# the last K/V group of the 128k sequence: query heads 28..31, all 16384 local
+# rows (chunk 3 against a 32768-key prefix, chunk 12 against 106496 keys)
+LONG_GROUP = [28, 29, 30, 31]
+
+
+@functools.lru_cache(maxsize=1)
+def _long128k_group_ref():
+    w, (q, k, v, do) = workload_tensors("long128k")
+    return fwd_ref_heads(w, q, k, v, LONG_GROUP)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("split", [False, True])
+def test_long128k_group_all_rows(split, monkeypatch):
+    """cva_fwd, and cva_fwd_split with every Q tile longer than 256 K/V tiles cut
+    into pieces (the default cut leaves this batch whole: its longest Q tile
+    walks fewer K/V tiles than the average compute unit does)."""
+    if split:
+        monkeypatch.setenv("CVA_FWD_SPLIT_CAP", "256")
+    w, (q, k, v, do) = workload_tensors("long128k")
+    _run(w, q, k, v, heads=LONG_GROUP, split=split, ref=_long128k_group_ref())
+
+
 def test_long128k_sampled_rows():
-    w = synth.make_workload("long128k")
-    q, k, v = synth.make_tensors(w, with_dout=False)
+    w, (q, k, v, do) = workload_tensors("long128k")
     _run(w, q, k, v, rows=_sample_rows(w, 48, 2))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("mask", ["lambda", "shared_prefix", "blockwise"])
+def test_sparse8_head_all_rows(mask):
+    """Every row of query head 15 (its own K/V head): all 81408 rows of the batch."""
+    w, (q, k, v, do) = workload_tensors("sparse8", mask=mask)
+    _run(w, q, k, v, heads=[15])
 
 
 @pytest.mark.parametrize("mask", ["lambda", "shared_prefix", "blockwise"])
 def test_sparse8_sampled_rows(mask):
-    w = synth.make_workload("sparse8", mask=mask)
-    q, k, v = synth.make_tensors(w, with_dout=False)
+    w, (q, k, v, do) = workload_tensors("sparse8", mask=mask)
     _run(w, q, k, v, rows=_sample_rows(w, 64, 3))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_mla32k_heads_all_rows(dtype):
+    """Every row of query heads 0 and 15 (Q/K head dim 192, V head dim 128)."""
+    w, (q, k, v, do) = workload_tensors("mla32k", dtype=dtype)
+    _run(w, q, k, v, heads=[0, 15])
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 def test_mla32k_sampled_rows(dtype):
-    w = synth.make_workload("mla32k", dtype=dtype)
-    q, k, v = synth.make_tensors(w, with_dout=False)
+    w, (q, k, v, do) = workload_tensors("mla32k", dtype=dtype)
     _run(w, q, k, v, rows=_sample_rows(w, 64, 4))
 
 
