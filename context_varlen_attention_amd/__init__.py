@@ -92,7 +92,8 @@ EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_ge
            "cva_plan_device_bytes", "cva_plan_upload", "cva_fwd", "cva_fwd_workspace_bytes",
            "cva_fwd_split", "cva_bwd_workspace_bytes",
            "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read", "cva_timing_select",
-           "cva_placement_create", "cva_placement_get", "cva_placement_destroy"]
+           "cva_placement_create", "cva_placement_get", "cva_placement_destroy",
+           "cva_bwd_noalloc_max_bytes", "cva_bwd_noalloc"]
 
 # timing ids of cva_timing_read; ids 1 and 2 are reserved (formerly separate
 # Delta and zero-fill launches, now part of the dQ kernel)
@@ -140,6 +141,10 @@ def load_library():
     L.cva_bwd_workspace_bytes.argtypes = [vp]
     L.cva_bwd.restype = i32
     L.cva_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
+    L.cva_bwd_noalloc_max_bytes.restype = sz
+    L.cva_bwd_noalloc_max_bytes.argtypes = []
+    L.cva_bwd_noalloc.restype = i32
+    L.cva_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp]
     L.cva_plan_get_schedule.restype = i32
     L.cva_plan_get_schedule.argtypes = [vp, i32, ctypes.POINTER(_Schedule)]
     L.cva_timing_enable.restype = i32

@@ -313,11 +313,11 @@ size_t cva_bwd_workspace_bytes(const cva_plan* plan) {
   return 2 * (size_t)p->T_loc * p->hq * sizeof(float);  // Delta, LSE * log2(e)
 }
 
-cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
-                   const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
-                   void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
-                   void* stream) {
-  const Plan* p = reinterpret_cast<const Plan*>(plan);
+namespace {
+
+cva_status check_bwd_args(const Plan* p, const void* q, const void* k_rm, const void* v_rm,
+                          const void* o, const float* lse, const void* dout, void* dq,
+                          void* dk_rm, void* dv_rm, float softmax_scale) {
   cva_status st = check_ready(p);
   if (st != CVA_OK) return st;
   if (q == nullptr || k_rm == nullptr || v_rm == nullptr || o == nullptr || lse == nullptr ||
@@ -325,12 +325,13 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
     return fail(CVA_E_ARG, "a tensor pointer is NULL");
   if ((st = check_scale(softmax_scale)) != CVA_OK) return st;
   if (p->dtype == CVA_FP32) return fail(CVA_E_UNSUPPORTED, "backward is implemented for bf16 and fp16");
-  const size_t need = cva_bwd_workspace_bytes(plan);
-  if (workspace == nullptr || ws_bytes < need) {
-    std::ostringstream os;
-    os << "workspace needs " << need << " bytes";
-    return fail(CVA_E_WORKSPACE, os.str());
-  }
+  return CVA_OK;
+}
+
+// Launches the backward with Delta / LSE*log2(e) in `stats` (2 * T_loc * Hq floats).
+cva_status run_bwd(const Plan* p, const void* q, const void* k_rm, const void* v_rm,
+                   const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
+                   void* dv_rm, float* stats, float softmax_scale, void* stream) {
   cva::BwdParams bp;
   bp.q = q;
   bp.k = k_rm;
@@ -341,8 +342,8 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   bp.dq = dq;
   bp.dk = dk_rm;
   bp.dv = dv_rm;
-  bp.delta = (float*)workspace;
-  bp.lse2 = bp.delta + (size_t)p->T_loc * p->hq;
+  bp.delta = stats;
+  bp.lse2 = stats + (size_t)p->T_loc * p->hq;
   bp.t = tables(*p);
   bp.n_dq_tiles = p->dq.n_tiles();
   bp.n_kv_tiles = p->dkdv.n_tiles();
@@ -359,6 +360,46 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
   hipError_t e = cva::launch_bwd(p->dtype, p->d_qk, p->d_v, bp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return CVA_OK;
+}
+
+}  // namespace
+
+cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                   const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
+                   void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
+                   void* stream) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  cva_status st = check_bwd_args(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, softmax_scale);
+  if (st != CVA_OK) return st;
+  const size_t need = cva_bwd_workspace_bytes(plan);
+  if (workspace == nullptr || ws_bytes < need) {
+    std::ostringstream os;
+    os << "workspace needs " << need << " bytes";
+    return fail(CVA_E_WORKSPACE, os.str());
+  }
+  return run_bwd(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, (float*)workspace,
+                 softmax_scale, stream);
+}
+
+size_t cva_bwd_noalloc_max_bytes(void) { return cva::kBwdNoAllocScratchBytes; }
+
+cva_status cva_bwd_noalloc(const cva_plan* plan, const void* q, const void* k_rm,
+                           const void* v_rm, const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk_rm, void* dv_rm, float softmax_scale, void* stream) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  cva_status st = check_bwd_args(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, softmax_scale);
+  if (st != CVA_OK) return st;
+  const size_t need = cva_bwd_workspace_bytes(plan);
+  if (need > cva::kBwdNoAllocScratchBytes) {
+    std::ostringstream os;
+    os << "cva_bwd_noalloc holds at most " << cva::kBwdNoAllocScratchBytes
+       << " bytes of row statistics; this plan needs " << need << " (use cva_bwd with a workspace)";
+    return fail(CVA_E_WORKSPACE, os.str());
+  }
+  float* stats = nullptr;
+  hipError_t e = cva::bwd_noalloc_scratch((hipStream_t)stream, &stats);
+  if (e != hipSuccess) return hip_fail(e, "library device array (hipGetSymbolAddress)");
+  return run_bwd(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, stats, softmax_scale, stream);
 }
 
 cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out) {

@@ -26,6 +26,7 @@
 //   dkdv_pair_kernel  K/V-stationary: a work-group owns 128 keys of one K/V
 //                     head and walks the 64-row Q tiles that see them; paired
 //                     waves per 32 keys, see below.
+#include <mutex>
 #include <type_traits>
 
 #include "../host/plan.hpp"
@@ -1105,6 +1106,41 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
 }
 
 }  // namespace
+
+// Device memory of the allocation-free backward (cva_bwd_noalloc): the per-row
+// statistics Delta and LSE*log2(e) that the dQ kernel writes and the dK/dV
+// kernel reads, held by the library for the life of the process on every GPU
+// it runs on.  Host code never names this array in a kernel argument or copy:
+// it uses the per-device address hipGetSymbolAddress returns.
+static __device__ __align__(256) float scratch[kBwdNoAllocScratchBytes / sizeof(float)];
+
+hipError_t bwd_noalloc_scratch(hipStream_t stream, float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // first use on this device: look the array up with the device current
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (a == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = (float*)addr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t s,
                       LaunchHook* h) {

@@ -1,6 +1,7 @@
 // Kernel parameter blocks and launchers shared by the C ABI and the HIP kernels.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 
 #include <hip/hip_runtime_api.h>
@@ -83,5 +84,11 @@ hipError_t launch_fwd(int dtype, int d_qk, int d_v, const FwdParams& p, hipStrea
                       LaunchHook* hook);
 hipError_t launch_bwd(int dtype, int d_qk, int d_v, const BwdParams& p, hipStream_t stream,
                       LaunchHook* hook);
+
+// Allocation-free backward: bytes of the library-held device array that takes
+// the place of the caller's workspace, and its address on the device of
+// `stream` (looked up once per device; no allocation).
+constexpr size_t kBwdNoAllocScratchBytes = size_t(16) << 20;
+hipError_t bwd_noalloc_scratch(hipStream_t stream, float** ptr);
 
 }  // namespace cva

@@ -205,6 +205,25 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
                     void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
                     void* stream);
 
+/* Allocation-free backward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results as cva_bwd without the
+ * workspace: the row statistics (Delta and LSE*log2(e), cva_bwd_workspace_bytes
+ * bytes) go to a device array the library holds on every GPU it runs on until
+ * the process ends, of cva_bwd_noalloc_max_bytes() bytes (16 MiB: Hq * T_loc up
+ * to 2^21, e.g. 32 heads x 65536 local rows).  The call allocates nothing (no
+ * hipMalloc/hipFree); its first call on a GPU looks up that GPU's copy of the
+ * array.  Every call on one GPU shares the array, whose contents are left from
+ * the last call (everything it reads is written earlier in the same call):
+ * calls that may run at the same time on one GPU (unordered streams) race and
+ * must not be made.  Errors: CVA_E_WORKSPACE if the plan needs more than the
+ * array holds, CVA_E_HIP if the array cannot be looked up, otherwise as
+ * cva_bwd. */
+size_t cva_bwd_noalloc_max_bytes(void);
+cva_status cva_bwd_noalloc(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                           const void* o, const float* lse, const void* dout, void* dq,
+                           void* dk_rm, void* dv_rm, float softmax_scale, void* stream);
+
 /* Schedule introspection for tests and tools.  which: 0 forward, 1 backward dQ,
  * 2 backward dK/dV, 3 forward with split K/V ranges (the items of
  * cva_fwd_split, same record layout as 0; pieces of one Q tile share its
