@@ -101,3 +101,51 @@ def volumes_ref(data_dev, comp_dev, sizes, n_devices):
                     recv[dev] += size
     return {"tokens": tokens, "pairs": pairs, "block_volume": int(block_volume),
             "connectivity": int(connectivity), "send": send, "recv": recv}
+
+
+def share_fwd_ref(w, q, k, v, B, comp_dev, device, scale=None):
+    """Forward of one device's share of a placement, from the definition.
+
+    DCP paper, section 4.1: a computation block (sequence i, Q block qb, K/V
+    block kb) is the attention of the query rows of block qb against the keys
+    of block kb; a device computes the blocks assigned to it, and the partial
+    results of the blocks that feed one output block are reduced (Fig. 9(b)).
+    A device's share for Q block (i, qb) is therefore masked softmax attention
+    of those rows over the keys of every K/V block kb with (i, qb, kb) on that
+    device: S = scale * Q K^T, S[~(M and key in the device's blocks)] = -inf,
+    softmax, O = P V, LSE = log sum exp.  Merging all devices' shares of an
+    output block by log-sum-exp gives unsplit attention.
+
+    ``w``: the batch (cu_seqlens, heads, mask; unsplit); q, k, v the packed
+    tensors [T, H, D]; ``comp_dev``: {(seq, qb, kb): device}.  Returns o
+    [T, Hq, Dv] and lse [Hq, T] (float64), NaN at rows of Q blocks the device
+    has no computation block for.
+    """
+    from .attention import default_scale, softmax_rows_ref
+    scale = default_scale(w.d_qk) if scale is None else float(scale)
+    G = w.hq // w.hkv
+    cu = [int(x) for x in w.cu_seqlens]
+    T = cu[-1]
+    o = np.full((T, w.hq, w.d_v), np.nan)
+    lse = np.full((w.hq, T), np.nan)
+    mine = {}
+    for (i, qb, kb), dev in comp_dev.items():
+        if dev == device:
+            mine.setdefault((i, qb), []).append(kb)
+    for (i, qb), kbs in sorted(mine.items()):
+        s0, L = cu[i], cu[i + 1] - cu[i]
+        rows = np.arange(qb * B, min(L, (qb + 1) * B))
+        bounds = None if w.branch_bounds is None else w.branch_bounds[i]
+        M = mask_ref(w.mask, L, w.sink, w.window, bounds, getattr(w, "block", 0))[rows]
+        keys = np.zeros(L, dtype=bool)
+        for kb in kbs:
+            keys[kb * B: (kb + 1) * B] = True
+        M = M & keys[None, :]
+        Q = np.asarray(q[s0 + rows], dtype=np.float64)
+        K = np.asarray(k[s0: s0 + L], dtype=np.float64)
+        V = np.asarray(v[s0: s0 + L], dtype=np.float64)
+        for h in range(w.hq):
+            P, l = softmax_rows_ref(scale * (Q[:, h] @ K[:, h // G].T), M)
+            o[s0 + rows, h] = P @ V[:, h // G]
+            lse[h, s0 + rows] = l
+    return o, lse

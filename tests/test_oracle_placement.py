@@ -122,3 +122,80 @@ def test_send_equals_receive_in_total():
     v = volumes_ref(d, c, (2, 3, 5), 4)
     assert v["send"].sum() == v["recv"].sum() == v["connectivity"]
     assert v["connectivity"] <= v["block_volume"]
+
+
+# ---- one device's share of a placement: forward from the definition ----
+
+import math  # noqa: E402
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+from oracle.placement import share_fwd_ref  # noqa: E402
+
+
+def _share_case(mask, dtype="fp32"):
+    lens = [10, 7, 13]
+    bb = None
+    if mask == "shared_prefix":
+        bb = [[3, 6, 8, 10], [2, 4, 6, 7], [4, 7, 10, 13]]
+    w = synth.custom_workload(lens, 1, 0, 4, 2, 8, 6, dtype, mask=mask, sink=2, window=4,
+                              branch_bounds=bb)
+    return w, synth.random_tensors(w, 71, with_dout=False)
+
+
+@pytest.mark.parametrize("mask", ["causal", "lambda", "shared_prefix"])
+def test_share_with_every_block_on_one_device_is_full_attention(mask):
+    w, (q, k, v) = _share_case(mask)
+    B = 3
+    _, comp = blocks_ref(w.cu_seqlens, B, mask, sink=2, window=4,
+                         bounds=None if w.branch_bounds is None else w.branch_bounds)
+    o, lse = share_fwd_ref(w, q, k, v, B, {c: 0 for c in comp}, 0, scale=0.5)
+    ro, rl = oracle.fwd_full_ref(w, q, k, v, scale=0.5)
+    np.testing.assert_allclose(o, ro, atol=1e-13)
+    np.testing.assert_allclose(lse, rl, atol=1e-13)
+    o1, _ = share_fwd_ref(w, q, k, v, B, {c: 0 for c in comp}, 1, scale=0.5)
+    assert np.isnan(o1).all()  # device 1 computes nothing
+
+
+@pytest.mark.parametrize("mask", ["causal", "lambda", "shared_prefix"])
+def test_lse_merge_of_all_shares_is_full_attention(mask):
+    """Fig. 9(b): the partial outputs of the computation blocks of one output block,
+    spread over devices, reduce to the unsplit result."""
+    w, (q, k, v) = _share_case(mask)
+    B, R = 2, 3
+    _, comp = blocks_ref(w.cu_seqlens, B, mask, sink=2, window=4,
+                         bounds=None if w.branch_bounds is None else w.branch_bounds)
+    rng = np.random.default_rng(4)
+    comp_dev = {c: int(rng.integers(0, R)) for c in comp}
+    shares = [share_fwd_ref(w, q, k, v, B, comp_dev, d, scale=0.7) for d in range(R)]
+    ro, rl = oracle.fwd_full_ref(w, q, k, v, scale=0.7)
+    T = w.total_tokens
+    for h in range(w.hq):
+        for t in range(T):
+            parts = [(o[t, h], l[h, t]) for o, l in shares if not np.isnan(l[h, t])]
+            assert parts, (h, t)  # every row has a visible key on some device
+            ls = np.array([l for _, l in parts])
+            m = ls[np.isfinite(ls)].max()
+            wts = np.exp(ls - m)
+            merged = sum(wt * o for wt, (o, _) in zip(wts, parts)) / wts.sum()
+            np.testing.assert_allclose(merged, ro[t, h], atol=1e-12)
+            assert abs(m + math.log(wts.sum()) - rl[h, t]) < 1e-12
+
+
+def test_share_of_one_block_by_brute_force():
+    """Q block 2 of a 10-token causal sequence (block 3) against K/V block 1 only:
+    rows 6..8 over keys 3..5, written as plain loops."""
+    w = synth.custom_workload([10], 1, 0, 2, 1, 3, 2, "fp32")
+    q, k, v = synth.random_tensors(w, 72, with_dout=False)
+    o, lse = share_fwd_ref(w, q, k, v, 3, {(0, 2, 1): 5, (0, 2, 2): 4}, 5, scale=0.9)
+    for h in range(2):
+        for t in (6, 7, 8):
+            s = [0.9 * sum(float(q[t, h, d]) * float(k[j, 0, d]) for d in range(3)) for j in (3, 4, 5)]
+            mx = max(s)
+            e = [math.exp(x - mx) for x in s]
+            den = sum(e)
+            for d in range(2):
+                want = sum(e[n] * float(v[j, 0, d]) for n, j in enumerate((3, 4, 5))) / den
+                assert abs(o[t, h, d] - want) < 1e-12
+            assert abs(lse[h, t] - (mx + math.log(den))) < 1e-12
+    assert np.isnan(o[:6]).all() and np.isnan(o[9:]).all()
