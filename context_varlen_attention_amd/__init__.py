@@ -24,7 +24,7 @@ import os
 
 import numpy as np
 
-__all__ = ["Plan", "Placement", "fwd", "bwd", "CvaError", "local_token_ids",
+__all__ = ["Plan", "Placement", "PlacedPlan", "fwd", "bwd", "bwd_noalloc", "CvaError", "local_token_ids",
            "rank_major_token_ids", "library_path", "load_library", "timing_enable", "timing_read",
            "timing_select"]
 
@@ -78,6 +78,15 @@ class _Schedule(ctypes.Structure):
                 ("tiles", _P32), ("spans", _P32)]
 
 
+class _Tables(ctypes.Structure):
+    _fields_ = [("n_segs", ctypes.c_int32), ("segs", _P32), ("kv_index_len", ctypes.c_int64),
+                ("kv_index", _P32), ("n_rows", ctypes.c_int64), ("row_iv", _P32),
+                ("n_zero_ranges", ctypes.c_int32), ("zero_rows", _P32),
+                ("n_split_items", ctypes.c_int32), ("split_slot", _P32),
+                ("n_combine", ctypes.c_int32), ("split_combine", _P32),
+                ("n_split_slots", ctypes.c_int32)]
+
+
 class _PlacementInfo(ctypes.Structure):
     _fields_ = [("n_devices", ctypes.c_int32), ("block", ctypes.c_int32),
                 ("n_data_blocks", ctypes.c_int32), ("n_comp_blocks", ctypes.c_int32),
@@ -93,7 +102,8 @@ EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_ge
            "cva_fwd_split", "cva_bwd_workspace_bytes",
            "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read", "cva_timing_select",
            "cva_placement_create", "cva_placement_get", "cva_placement_destroy",
-           "cva_bwd_noalloc_max_bytes", "cva_bwd_noalloc"]
+           "cva_bwd_noalloc_max_bytes", "cva_bwd_noalloc", "cva_placement_plan_create",
+           "cva_plan_get_tables"]
 
 # timing ids of cva_timing_read; ids 1 and 2 are reserved (formerly separate
 # Delta and zero-fill launches, now part of the dQ kernel)
@@ -145,6 +155,8 @@ def load_library():
     L.cva_bwd_noalloc_max_bytes.argtypes = []
     L.cva_bwd_noalloc.restype = i32
     L.cva_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, f32, vp]
+    L.cva_plan_get_tables.restype = i32
+    L.cva_plan_get_tables.argtypes = [vp, ctypes.POINTER(_Tables)]
     L.cva_plan_get_schedule.restype = i32
     L.cva_plan_get_schedule.argtypes = [vp, i32, ctypes.POINTER(_Schedule)]
     L.cva_timing_enable.restype = i32
@@ -158,6 +170,8 @@ def load_library():
                                        i32, i32, i32, ctypes.c_double, ctypes.POINTER(vp)]
     L.cva_placement_get.restype = i32
     L.cva_placement_get.argtypes = [vp, ctypes.POINTER(_PlacementInfo)]
+    L.cva_placement_plan_create.restype = i32
+    L.cva_placement_plan_create.argtypes = [vp, i32, ctypes.POINTER(vp)]
     L.cva_placement_destroy.restype = None
     L.cva_placement_destroy.argtypes = [vp]
     _lib = L
@@ -176,7 +190,72 @@ def _arr(ptr, n, dtype):
     return np.ctypeslib.as_array(ptr, shape=(n,)).astype(dtype, copy=True)
 
 
-class Plan:
+class _PlanBase:
+    """A libcva plan handle: schedules, device copy (shared by Plan and PlacedPlan)."""
+
+    _h = None
+    _dev = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.cva_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def schedule(self, which):
+        """(tile_q, tile_kv, tiles [n,5], spans [m,4]) of schedule 0 fwd, 1 dQ, 2 dK/dV,
+        3 forward with split K/V ranges."""
+        s = _Schedule()
+        _check(load_library().cva_plan_get_schedule(self._h, int(which), ctypes.byref(s)))
+        tiles = _arr(s.tiles, s.n_tiles * 5, np.int64).reshape(-1, 5)
+        spans = _arr(s.spans, s.n_spans * 4, np.int64).reshape(-1, 4)
+        return s.tile_q, s.tile_kv, tiles, spans
+
+    def tables(self):
+        """``cva_plan_get_tables``: the plan's other device tables as numpy arrays."""
+        t = _Tables()
+        _check(load_library().cva_plan_get_tables(self._h, ctypes.byref(t)))
+        return {
+            "segs": _arr(t.segs, t.n_segs * 8, np.int64).reshape(-1, 8),
+            "kv_index": _arr(t.kv_index, t.kv_index_len, np.int64),
+            "row_iv": _arr(t.row_iv, t.n_rows * 4, np.int64).reshape(-1, 4),
+            "zero_rows": _arr(t.zero_rows, t.n_zero_ranges * 2, np.int64).reshape(-1, 2),
+            "split_slot": _arr(t.split_slot, t.n_split_items, np.int64),
+            "split_combine": _arr(t.split_combine, t.n_combine * 5, np.int64).reshape(-1, 5),
+            "n_split_slots": int(t.n_split_slots),
+        }
+
+    def fwd_workspace_bytes(self):
+        """Bytes of the workspace ``cva_fwd_split`` needs (0: the plan splits nothing)."""
+        return int(load_library().cva_fwd_workspace_bytes(self._h))
+
+    def device_bytes(self):
+        return int(load_library().cva_plan_device_bytes(self._h))
+
+    def upload(self, device=None, stream=None):
+        """Copy the plan tables into a torch uint8 buffer on ``device`` and bind them."""
+        import torch
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        nbytes = self.device_bytes()
+        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        off = (-buf.data_ptr()) % 256
+        view = buf[off: off + nbytes]
+        s = _stream_ptr(stream, dev)
+        _check(load_library().cva_plan_upload(self._h, ctypes.c_void_p(view.data_ptr()),
+                                              nbytes, s))
+        self._dev = buf  # keep alive while the plan is used
+        return self
+
+    @property
+    def uploaded(self):
+        return self._dev is not None
+
+
+class Plan(_PlanBase):
     """Host plan of one rank: metadata + tile schedules (``cva_plan_create``).
 
     ``branch_bounds``: shared-prefix layout, int [n_seqs][n_branches+1] of
@@ -237,53 +316,9 @@ class Plan:
             "visible_pairs_per_rank": _arr(m.visible_pairs_per_rank, m.cp_size, np.int64),
         }
 
-    def __del__(self):
-        h = getattr(self, "_h", None)
-        if h is not None and _lib is not None:
-            _lib.cva_plan_destroy(h)
-            self._h = None
-
-    @property
-    def handle(self):
-        return self._h
-
     @property
     def cu_seqlens(self):
         return self._cu.astype(np.int64)
-
-    def schedule(self, which):
-        """(tile_q, tile_kv, tiles [n,5], spans [m,4]) of schedule 0 fwd, 1 dQ, 2 dK/dV,
-        3 forward with split K/V ranges."""
-        s = _Schedule()
-        _check(load_library().cva_plan_get_schedule(self._h, int(which), ctypes.byref(s)))
-        tiles = _arr(s.tiles, s.n_tiles * 5, np.int64).reshape(-1, 5)
-        spans = _arr(s.spans, s.n_spans * 4, np.int64).reshape(-1, 4)
-        return s.tile_q, s.tile_kv, tiles, spans
-
-    def fwd_workspace_bytes(self):
-        """Bytes of the workspace ``cva_fwd_split`` needs (0: the plan splits nothing)."""
-        return int(load_library().cva_fwd_workspace_bytes(self._h))
-
-    def device_bytes(self):
-        return int(load_library().cva_plan_device_bytes(self._h))
-
-    def upload(self, device=None, stream=None):
-        """Copy the plan tables into a torch uint8 buffer on ``device`` and bind them."""
-        import torch
-        dev = torch.device("cuda") if device is None else torch.device(device)
-        nbytes = self.device_bytes()
-        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
-        off = (-buf.data_ptr()) % 256
-        view = buf[off: off + nbytes]
-        s = _stream_ptr(stream, dev)
-        _check(load_library().cva_plan_upload(self._h, ctypes.c_void_p(view.data_ptr()),
-                                              nbytes, s))
-        self._dev = buf  # keep alive while the plan is used
-        return self
-
-    @property
-    def uploaded(self):
-        return self._dev is not None
 
     def visible_pairs(self):
         return self.metadata["visible_pairs"]
@@ -337,24 +372,61 @@ class Placement:
                                       int(hkv), int(d_qk), int(d_v), DTYPES[dtype],
                                       float(epsilon), ctypes.byref(handle)))
         del bb
-        try:
-            info = _PlacementInfo()
-            _check(L.cva_placement_get(handle, ctypes.byref(info)))
-            r = info.n_devices
-            self.n_devices, self.block = int(info.n_devices), int(info.block)
-            self.data_blocks = _arr(info.data_blocks, info.n_data_blocks * 4, np.int64).reshape(-1, 4)
-            self.comp_blocks = _arr(info.comp_blocks, info.n_comp_blocks * 4, np.int64).reshape(-1, 4)
-            self.comp_pairs = _arr(info.comp_pairs, info.n_comp_blocks, np.int64)
-            self.device_tokens = _arr(info.device_tokens, r, np.int64)
-            self.device_pairs = _arr(info.device_pairs, r, np.int64)
-            self.device_send_bytes = _arr(info.device_send_bytes, r, np.int64)
-            self.device_recv_bytes = _arr(info.device_recv_bytes, r, np.int64)
-            self.total_comm_bytes = int(info.total_comm_bytes)
-            self.block_comm_bytes = int(info.block_comm_bytes)
-            self.zigzag_pairs = _arr(info.zigzag_pairs, r, np.int64) if info.zigzag_valid else None
-            self.zigzag_comm_bytes = int(info.zigzag_comm_bytes)
-        finally:
-            L.cva_placement_destroy(handle)
+        self._h = handle
+        self.hq, self.hkv, self.d_qk, self.d_v, self.dtype = int(hq), int(hkv), int(d_qk), int(d_v), dtype
+        self.total_tokens = int(cu32[-1]) if cu32.size else 0
+        info = _PlacementInfo()
+        _check(L.cva_placement_get(handle, ctypes.byref(info)))
+        r = info.n_devices
+        self.n_devices, self.block = int(info.n_devices), int(info.block)
+        self.data_blocks = _arr(info.data_blocks, info.n_data_blocks * 4, np.int64).reshape(-1, 4)
+        self.comp_blocks = _arr(info.comp_blocks, info.n_comp_blocks * 4, np.int64).reshape(-1, 4)
+        self.comp_pairs = _arr(info.comp_pairs, info.n_comp_blocks, np.int64)
+        self.device_tokens = _arr(info.device_tokens, r, np.int64)
+        self.device_pairs = _arr(info.device_pairs, r, np.int64)
+        self.device_send_bytes = _arr(info.device_send_bytes, r, np.int64)
+        self.device_recv_bytes = _arr(info.device_recv_bytes, r, np.int64)
+        self.total_comm_bytes = int(info.total_comm_bytes)
+        self.block_comm_bytes = int(info.block_comm_bytes)
+        self.zigzag_pairs = _arr(info.zigzag_pairs, r, np.int64) if info.zigzag_valid else None
+        self.zigzag_comm_bytes = int(info.zigzag_comm_bytes)
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and _lib is not None:
+            _lib.cva_placement_destroy(h)
+            self._h = None
+
+    def device_plan(self, device):
+        """``cva_placement_plan_create``: device ``device``'s computation blocks as a
+        plan run by :func:`fwd` with ``workspace=True`` on the packed tensors."""
+        return PlacedPlan(self, device)
+
+
+class PlacedPlan(_PlanBase):
+    """One device's share of a :class:`Placement` (``cva_placement_plan_create``).
+
+    Runs through ``fwd(plan, q, k, v, workspace=True)`` (``cva_fwd_split``) on the
+    packed, unsplit tensors q [T, Hq, Dqk], k/v [T, Hkv, D]; writes o [T, Hq, Dv] and
+    lse [Hq, T] at the rows of the O blocks the device contributes to (its partial
+    result over its own computation blocks) and leaves the other rows untouched.
+    ``blocks`` lists the device's computation blocks (rows of
+    ``placement.comp_blocks``).
+    """
+
+    def __init__(self, placement, device):
+        L = load_library()
+        handle = ctypes.c_void_p()
+        self._h = None
+        self._dev = None
+        _check(L.cva_placement_plan_create(placement._h, int(device), ctypes.byref(handle)))
+        self._h = handle
+        self.device = int(device)
+        self.cp_size, self.rank = 1, 0
+        self.hq, self.hkv = placement.hq, placement.hkv
+        self.d_qk, self.d_v, self.dtype = placement.d_qk, placement.d_v, placement.dtype
+        self.global_tokens = self.local_tokens = placement.total_tokens
+        self.blocks = placement.comp_blocks[placement.comp_blocks[:, 3] == self.device]
 
 
 def _stream_ptr(stream, device):
@@ -460,6 +532,28 @@ def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk
                      vp(dk_rm.data_ptr()), vp(dv_rm.data_ptr()), vp(workspace.data_ptr()),
                      workspace.numel() * workspace.element_size(), _scale(plan, softmax_scale),
                      _stream_ptr(stream, dev)))
+    return dq, dk_rm, dv_rm
+
+
+def bwd_noalloc(plan: Plan, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, softmax_scale=None,
+                stream=None):
+    """``cva_bwd_noalloc``: ``bwd`` into caller-given dq / dk_rm / dv_rm with no
+    device allocation (the row statistics live in the library's own array)."""
+    dev = q.device
+    dt = _TORCH_DT[plan.dtype]
+    T, Tl = plan.global_tokens, plan.local_tokens
+    for t, name, shape in ((q, "q", (Tl, plan.hq, plan.d_qk)), (k_rm, "k_rm", (T, plan.hkv, plan.d_qk)),
+                           (v_rm, "v_rm", (T, plan.hkv, plan.d_v)), (o, "o", (Tl, plan.hq, plan.d_v)),
+                           (dout, "dout", (Tl, plan.hq, plan.d_v)), (dq, "dq", (Tl, plan.hq, plan.d_qk)),
+                           (dk_rm, "dk_rm", (T, plan.hkv, plan.d_qk)),
+                           (dv_rm, "dv_rm", (T, plan.hkv, plan.d_v))):
+        _expect(t, name, shape, dt, dev)
+    _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
+    vp = ctypes.c_void_p
+    _check(load_library().cva_bwd_noalloc(
+        plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()), vp(o.data_ptr()),
+        vp(lse.data_ptr()), vp(dout.data_ptr()), vp(dq.data_ptr()), vp(dk_rm.data_ptr()),
+        vp(dv_rm.data_ptr()), _scale(plan, softmax_scale), _stream_ptr(stream, dev)))
     return dq, dk_rm, dv_rm
 
 

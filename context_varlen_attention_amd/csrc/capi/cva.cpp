@@ -173,6 +173,7 @@ void cva_plan_destroy(cva_plan* plan) { delete reinterpret_cast<Plan*>(plan); }
 cva_status cva_plan_get_metadata(const cva_plan* plan, cva_metadata* out) {
   const Plan* p = reinterpret_cast<const Plan*>(plan);
   if (p == nullptr || out == nullptr) return fail(CVA_E_ARG, "plan or out is NULL");
+  if (p->placed) return fail(CVA_E_UNSUPPORTED, "a placement share has no context-parallel metadata");
   out->local_tokens = p->T_loc;
   out->global_tokens = p->T;
   out->n_seqs = p->n_seqs;
@@ -238,6 +239,8 @@ cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v
   if (q == nullptr || k_rm == nullptr || v_rm == nullptr || o == nullptr || lse == nullptr)
     return fail(CVA_E_ARG, "a tensor pointer is NULL");
   if ((st = check_scale(softmax_scale)) != CVA_OK) return st;
+  if (p->placed && !split)
+    return fail(CVA_E_UNSUPPORTED, "a placement share runs through cva_fwd_split (its blocks merge by LSE)");
   split = split && splits(*p);
   if (split) {
     const size_t need = split_bytes(*p);
@@ -325,6 +328,7 @@ cva_status check_bwd_args(const Plan* p, const void* q, const void* k_rm, const 
     return fail(CVA_E_ARG, "a tensor pointer is NULL");
   if ((st = check_scale(softmax_scale)) != CVA_OK) return st;
   if (p->dtype == CVA_FP32) return fail(CVA_E_UNSUPPORTED, "backward is implemented for bf16 and fp16");
+  if (p->placed) return fail(CVA_E_UNSUPPORTED, "the backward of a placement share is not implemented");
   return CVA_OK;
 }
 
@@ -420,6 +424,25 @@ cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedu
   return CVA_OK;
 }
 
+cva_status cva_plan_get_tables(const cva_plan* plan, cva_plan_tables* out) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  if (p == nullptr || out == nullptr) return fail(CVA_E_ARG, "plan or out is NULL");
+  out->n_segs = (int32_t)(p->segs.size() / cva::SEG_INTS);
+  out->segs = p->segs.data();
+  out->kv_index_len = (int64_t)p->kv_index.size();
+  out->kv_index = p->kv_index.data();
+  out->n_rows = (int64_t)(p->row_iv.size() / 4);
+  out->row_iv = p->row_iv.data();
+  out->n_zero_ranges = (int32_t)(p->zero_rows.size() / 2);
+  out->zero_rows = p->zero_rows.data();
+  out->n_split_items = (int32_t)p->fwds_slot.size();
+  out->split_slot = p->fwds_slot.data();
+  out->n_combine = (int32_t)(p->fwds_combine.size() / cva::CB_INTS);
+  out->split_combine = p->fwds_combine.data();
+  out->n_split_slots = p->n_split_slots;
+  return CVA_OK;
+}
+
 cva_status cva_placement_create(const int32_t* cu_seqlens, int32_t n_seqs, const cva_mask_desc* mask,
                                 int32_t n_devices, int32_t block, int32_t hq, int32_t hkv,
                                 int32_t d_qk, int32_t d_v, int32_t dtype, double epsilon,
@@ -493,6 +516,29 @@ cva_status cva_placement_get(const cva_placement* placement, cva_placement_info*
   out->zigzag_valid = pl->zigzag_ok ? 1 : 0;
   out->zigzag_pairs = pl->zigzag_pairs.data();
   out->zigzag_comm_bytes = pl->zigzag_comm_bytes;
+  return CVA_OK;
+}
+
+cva_status cva_placement_plan_create(const cva_placement* placement, int32_t device,
+                                     cva_plan** out) {
+  cva::set_error("");
+  if (out == nullptr) return fail(CVA_E_ARG, "out is NULL");
+  *out = nullptr;
+  const auto* pl = reinterpret_cast<const cva::Placement*>(placement);
+  if (pl == nullptr) return fail(CVA_E_ARG, "placement is NULL");
+  Plan* p = new (std::nothrow) Plan();
+  if (p == nullptr) return fail(CVA_E_ARG, "out of host memory");
+  cva_status st;
+  try {
+    st = cva::build_placed_plan(*pl, device, *p);
+  } catch (const std::bad_alloc&) {
+    st = fail(CVA_E_ARG, "out of host memory while building the plan");
+  }
+  if (st != CVA_OK) {
+    delete p;
+    return st;
+  }
+  *out = reinterpret_cast<cva_plan*>(p);
   return CVA_OK;
 }
 

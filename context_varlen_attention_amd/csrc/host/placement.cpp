@@ -265,3 +265,94 @@ cva_status build_placement(Placement& pl) {
 }
 
 }  // namespace cva
+
+namespace cva {
+
+// One device's share of a placement as a plan.  The packed batch is addressed
+// as it is (row = packed token), so every device reads its local and fetched
+// blocks in place: segments are the Q blocks the device computes on (all of
+// their sequence's keys addressable, in-sequence positions), and each
+// computation block becomes forward items restricted to its K/V block's keys
+// (DCP paper, section 4.1: a computation block pairs one Q block with one K/V
+// block; Fig. 9(b): blocks that feed the same output block are reduced).
+cva_status build_placed_plan(const Placement& pl, int32_t device, Plan& p) {
+  const Plan& m = pl.mask;
+  if (device < 0 || device >= pl.n_devices) {
+    set_error("device must be in [0, n_devices)");
+    return CVA_E_RANK;
+  }
+  if (pl.dtype != CVA_BF16 && pl.dtype != CVA_FP16) {
+    set_error("a placement share runs on the bf16/fp16 kernels");
+    return CVA_E_UNSUPPORTED;
+  }
+  if (pl.hq % pl.hkv != 0) {
+    set_error("query heads must be a multiple of K/V heads");
+    return CVA_E_HEADS;
+  }
+  if (!head_dims_supported(pl.dtype, pl.d_qk, pl.d_v)) {
+    set_error("no kernel for these head dims; supported: (64,64), (128,128), (192,128)");
+    return CVA_E_HEADDIM;
+  }
+  if (pl.block % kFwdTileKv != 0) {
+    set_error("running a placement share needs a block size that is a multiple of 64 (the K/V tile)");
+    return CVA_E_UNSUPPORTED;
+  }
+  const int32_t B = pl.block;
+  p.n_seqs = m.n_seqs;
+  p.cp_size = 1;
+  p.rank = 0;
+  p.hq = pl.hq;
+  p.hkv = pl.hkv;
+  p.d_qk = pl.d_qk;
+  p.d_v = pl.d_v;
+  p.dtype = pl.dtype;
+  p.mask_type = m.mask_type;
+  p.sink = m.sink;
+  p.window = m.window;
+  p.n_branches = m.n_branches;
+  p.block = m.block;
+  p.cu = m.cu;
+  p.branch_bounds = m.branch_bounds;
+  p.placed = true;
+  p.placed_device = device;
+  p.T = p.T_loc = m.cu[m.n_seqs];
+  p.kv_index.resize((size_t)p.T);
+  std::iota(p.kv_index.begin(), p.kv_index.end(), 0);  // one run per sequence, from its first token
+  p.row_iv.assign((size_t)p.T * 4, 0);
+  for (int32_t i = 0; i < m.n_seqs; ++i)
+    for (int32_t q = 0; q < m.cu[i + 1] - m.cu[i]; ++q)
+      position_intervals(p, i, q, &p.row_iv[((size_t)m.cu[i] + q) * 4]);
+  // the device's computation blocks in (sequence, Q block, K/V block) order
+  std::vector<int32_t> mine;
+  for (int32_t c = 0; c < (int32_t)pl.comp_pairs.size(); ++c)
+    if (pl.comp[(size_t)c * 4 + 3] == device) mine.push_back(c);
+  std::sort(mine.begin(), mine.end(), [&](int32_t a, int32_t b) {
+    for (int f = 0; f < 3; ++f)
+      if (pl.comp[(size_t)a * 4 + f] != pl.comp[(size_t)b * 4 + f])
+        return pl.comp[(size_t)a * 4 + f] < pl.comp[(size_t)b * 4 + f];
+    return false;
+  });
+  std::vector<PlacedBlock> blocks;
+  p.segs.clear();
+  p.visible_pairs = 0;
+  int32_t last_seq = -1, last_qb = -1;
+  for (int32_t c : mine) {
+    const int32_t seq = pl.comp[(size_t)c * 4], qb = pl.comp[(size_t)c * 4 + 1], kb = pl.comp[(size_t)c * 4 + 2];
+    const int32_t L = m.cu[seq + 1] - m.cu[seq];
+    if (seq != last_seq || qb != last_qb) {
+      p.segs.insert(p.segs.end(), {seq, qb, std::min(B, L - qb * B), L, m.cu[seq] + qb * B, m.cu[seq],
+                                   qb * B, L});
+      last_seq = seq;
+      last_qb = qb;
+    }
+    blocks.push_back({(int32_t)(p.segs.size() / SEG_INTS) - 1, kb * B, std::min(L, (kb + 1) * B)});
+    p.visible_pairs += pl.comp_pairs[c];
+  }
+  p.visible_pairs_per_rank.assign(1, p.visible_pairs);
+  cva_status st = build_placed_schedule(p, blocks);
+  if (st != CVA_OK) return st;
+  build_blob(p);
+  return CVA_OK;
+}
+
+}  // namespace cva

@@ -87,6 +87,12 @@ struct Plan {
   int32_t fwd_split_cap = 0;
   std::vector<int32_t> zero_rows;  // [m][2] rank-major row ranges no local query sees (<= 8 rows each)
 
+  // one device's share of a block placement (build_placed_plan): segments are
+  // the Q blocks the device computes on, the only schedule is fwds (one item per
+  // computation block and Q tile, each with its own partial slot)
+  bool placed = false;
+  int32_t placed_device = -1;
+
   // device copy
   std::vector<int32_t> blob;
   BlobLayout layout;
@@ -112,6 +118,16 @@ struct Placement {
 };
 cva_status build_placement(Placement& pl);
 
+// A computation block of a placed plan: Q block segment `seg` against the keys
+// [k0, k1) of its sequence (in-sequence positions).
+struct PlacedBlock {
+  int32_t seg, k0, k1;
+};
+// Device `device`'s computation blocks of a placement as a plan (placement.cpp).
+cva_status build_placed_plan(const Placement& pl, int32_t device, Plan& p);
+// Its forward items, partial slots and merge records (schedule.cpp).
+cva_status build_placed_schedule(Plan& p, const std::vector<PlacedBlock>& blocks);
+
 // Thread-local error message used by the C ABI.
 void set_error(const std::string& msg);
 const char* last_error();
@@ -123,6 +139,9 @@ cva_status validate_request(const int32_t* cu_seqlens, int32_t n_seqs, int32_t c
 
 // Mask descriptor checks (also used by the block placement); cu is validated.
 cva_status validate_mask(const cva_mask_desc* mask, const int32_t* cu, int32_t n_seqs);
+
+// Supported kernel head shapes (validate.cpp).
+bool head_dims_supported(int32_t dtype, int32_t d_qk, int32_t d_v);
 
 // metadata.cpp
 cva_status build_metadata(Plan& p);
@@ -158,6 +177,6 @@ constexpr int32_t kDkvTileKv = 128;   // dK/dV kernel: keys per work-group (4 wa
 constexpr int32_t kZeroRowsPerBlock = 8;  // rank-major rows per zero-fill work-group
 constexpr int32_t kSplitCUs = 256;        // compute units the split balances over (MI355X)
 constexpr int32_t kSplitMinSteps = 8;     // never cut a piece shorter than this many K/V tiles
-constexpr int32_t kSplitMaxPieces = 8;    // pieces per Q tile (merge keeps their weights in registers)
+constexpr int32_t kSplitMaxPieces = 8;    // pieces the split forward cuts a Q tile into, at most
 
 }  // namespace cva

@@ -640,3 +640,80 @@ void build_fwd_split(Plan& p) {
 }
 
 }  // namespace cva
+
+namespace cva {
+
+// Forward items of a placed plan: for every Q tile of every segment (Q block)
+// and every computation block of that segment, the K/V tiles of the block's
+// key range that the tile's rows see, as one item with a partial slot of its
+// own; one merge record per Q tile lists its consecutive slots (possibly none:
+// the merge then gives its rows O = 0 and LSE = -inf, no visible key).
+cva_status build_placed_schedule(Plan& p, const std::vector<PlacedBlock>& blocks) {
+  const FwdShape fs = forward_shape(p);
+  p.fwd_heads_per_tile = fs.heads_per_tile;
+  p.fwd = p.dq = p.dkdv = Schedule{};
+  p.fwd.tile_q = p.dq.tile_q = fs.tile_q;
+  p.fwd.tile_kv = p.dq.tile_kv = fs.tile_kv;
+  p.dkdv.tile_q = kDkvTileQ;
+  p.dkdv.tile_kv = kDkvTileKv;
+  p.fwds = Schedule{};
+  p.fwds.tile_q = fs.tile_q;
+  p.fwds.tile_kv = fs.tile_kv;
+  p.fwds_slot.clear();
+  p.fwds_combine.clear();
+  p.zero_rows.clear();
+  p.n_split_slots = 0;
+  p.fwd_split_cap = 0;
+  struct Item { std::array<int32_t, QT_INTS> rec; std::vector<SpanOut> spans; int32_t slot; int64_t cost; };
+  std::vector<Item> items;
+  Scratch w;
+  IvList U0, F0;
+  const int32_t nseg = (int32_t)(p.segs.size() / SEG_INTS);
+  size_t b0 = 0;
+  for (int32_t sg = 0; sg < nseg; ++sg) {
+    size_t b1 = b0;
+    while (b1 < blocks.size() && blocks[b1].seg == sg) ++b1;
+    const int32_t q_len = p.segs[(size_t)sg * SEG_INTS + SEG_QLEN];
+    for (int32_t a0 = 0; a0 < q_len; a0 += fs.tile_q) {
+      const int32_t a1 = std::min(q_len, a0 + fs.tile_q);
+      tile_sets(p, sg, a0, a1, w);
+      U0 = w.U;
+      F0 = w.F;
+      const int32_t slot0 = p.n_split_slots;
+      for (size_t b = b0; b < b1; ++b) {
+        const int32_t k0 = blocks[b].k0, k1 = blocks[b].k1;
+        auto clip = [&](const IvList& in, IvList& out) {
+          out.clear();
+          for (const Iv& x : in) {
+            const int32_t lo = std::max(x.first, k0), hi = std::min(x.second, k1);
+            if (hi > lo) out.push_back({lo, hi});
+          }
+        };
+        clip(U0, w.U);
+        clip(F0, w.F);
+        tile_spans(w, fs.tile_kv);
+        if (w.spans.empty()) continue;  // no row of this tile sees a key of the block
+        if ((int32_t)w.spans.size() > kFwdMaxSpans) {
+          set_error("a computation block gives a query tile more K/V spans than the forward kernel supports");
+          return CVA_E_UNSUPPORTED;
+        }
+        Item it{{sg, a0, a1 - a0, 0, (int32_t)w.spans.size()}, w.spans, p.n_split_slots++, 0};
+        for (const SpanOut& x : w.spans) it.cost += x.t1 - x.t0;
+        items.push_back(std::move(it));
+      }
+      p.fwds_combine.insert(p.fwds_combine.end(), {sg, a0, a1 - a0, slot0, p.n_split_slots - slot0});
+    }
+    b0 = b1;
+  }
+  std::stable_sort(items.begin(), items.end(), [](const Item& a, const Item& b) { return a.cost > b.cost; });
+  for (Item& it : items) {
+    it.rec[QT_SPAN0] = p.fwds.n_spans();
+    p.fwds.tiles.insert(p.fwds.tiles.end(), it.rec.begin(), it.rec.end());
+    for (const SpanOut& x : it.spans) p.fwds.spans.insert(p.fwds.spans.end(), {x.t0, x.t1, x.partial, 0});
+    p.fwds_slot.push_back(it.slot);
+    p.fwds.tile_pairs += it.cost;
+  }
+  return CVA_OK;
+}
+
+}  // namespace cva

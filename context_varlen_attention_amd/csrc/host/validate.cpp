@@ -25,7 +25,7 @@ static cva_status fail(cva_status s, const std::string& msg) {
   return s;
 }
 
-static bool head_dims_supported(int32_t /*dtype*/, int32_t d_qk, int32_t d_v) {
+bool head_dims_supported(int32_t /*dtype*/, int32_t d_qk, int32_t d_v) {
   return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
 }
 

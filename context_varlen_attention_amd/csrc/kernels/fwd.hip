@@ -694,7 +694,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
 // Merge of the pieces of split K/V ranges: for every (query row, head) of a split
 // Q tile, O = sum_p w_p O_p / sum_p w_p and LSE = m + ln(sum_p w_p) with
 // w_p = exp(LSE_p - m), m = max_p LSE_p (the log-sum-exp combination of
-// partial softmax results).  One thread per (row, head); HBM-bound and small.
+// partial softmax results); any number of pieces, none included (O = 0,
+// LSE = -inf: no visible key).  One thread per (row, head); HBM-bound and small.
 template <typename E, int DV>
 __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams P) {
   const int item = blockIdx.x / P.n_head_groups;
@@ -713,36 +714,24 @@ __global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams P) {
     auto srow = [&](int pc) {
       return ((int64_t)((slot0 + pc) * P.n_head_groups + hg) * hpt + hh) * P.tile_q + r;
     };
-    float lp[kSplitMaxPieces];
     float m = -INFINITY;
-#pragma unroll
-    for (int pc = 0; pc < kSplitMaxPieces; ++pc) {
-      lp[pc] = pc < npiece ? P.ws_lse[srow(pc)] : -INFINITY;
-      m = fmaxf(m, lp[pc]);
-    }
+    for (int pc = 0; pc < npiece; ++pc) m = fmaxf(m, P.ws_lse[srow(pc)]);
     uint16_t* orow = (uint16_t*)P.o + (row * P.hq + head) * DV;
     if (m == -INFINITY) {  // no visible key in any piece
       for (int d = 0; d < DV; d += 8) *(u32x4_t*)(orow + d) = u32x4_t{0u, 0u, 0u, 0u};
       P.lse[(int64_t)head * P.t_loc + row] = -INFINITY;
       continue;
     }
-    float w[kSplitMaxPieces];
     float wsum = 0.f;
-#pragma unroll
-    for (int pc = 0; pc < kSplitMaxPieces; ++pc) {
-      w[pc] = pc < npiece ? expf(lp[pc] - m) : 0.f;
-      wsum += w[pc];
-    }
+    for (int pc = 0; pc < npiece; ++pc) wsum += expf(P.ws_lse[srow(pc)] - m);
     const float inv = 1.f / wsum;
     for (int d = 0; d < DV; d += 8) {
       f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int pc = 0; pc < kSplitMaxPieces; ++pc) {
-        if (pc < npiece) {
-          const float* src = P.ws_o + srow(pc) * DV + d;
-          lo += w[pc] * *(const f32x4_t*)src;
-          hi += w[pc] * *(const f32x4_t*)(src + 4);
-        }
+      for (int pc = 0; pc < npiece; ++pc) {
+        const float w = expf(P.ws_lse[srow(pc)] - m);
+        const float* src = P.ws_o + srow(pc) * DV + d;
+        lo += w * *(const f32x4_t*)src;
+        hi += w * *(const f32x4_t*)(src + 4);
       }
       *(u32x4_t*)(orow + d) = u32x4_t{pack2<E>(lo[0] * inv, lo[1] * inv), pack2<E>(lo[2] * inv, lo[3] * inv),
                                       pack2<E>(hi[0] * inv, hi[1] * inv), pack2<E>(hi[2] * inv, hi[3] * inv)};

@@ -246,6 +246,37 @@ typedef struct {
 
 cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out);
 
+/* The plan's remaining device tables, as cva_plan_upload copies them (host
+ * views owned by the plan), for tests and tools that check every index a
+ * kernel dereferences (MindSpeed RFC section 3.4: reliability).
+ *   segs          [n_segs][8] {sequence, chunk (placement share: Q block), queries,
+ *                 K/V prefix length, first local row, offset in kv_index, in-sequence
+ *                 position of the first query, sequence length}
+ *   kv_index      [kv_index_len] rank-major row of every prefix position
+ *   row_iv        [n_rows][4] visible keys of every local row, [a0, a1) u [b0, b1),
+ *                 in positions of its segment's prefix
+ *   zero_rows     [n_zero_ranges][2] rank-major row ranges the backward zero-fills
+ *   split_slot    [n_split_items] partial slot of every item of schedule 3, or -1
+ *   split_combine [n_combine][5] {segment, first query, rows, first slot, pieces}
+ *   n_split_slots partial slots of schedule 3 */
+typedef struct {
+  int32_t n_segs;
+  const int32_t* segs;
+  int64_t kv_index_len;
+  const int32_t* kv_index;
+  int64_t n_rows;
+  const int32_t* row_iv;
+  int32_t n_zero_ranges;
+  const int32_t* zero_rows;
+  int32_t n_split_items;
+  const int32_t* split_slot;
+  int32_t n_combine;
+  const int32_t* split_combine;
+  int32_t n_split_slots;
+} cva_plan_tables;
+
+cva_status cva_plan_get_tables(const cva_plan* plan, cva_plan_tables* out);
+
 /* Block placement over n_devices (DCP paper, section 4.1 and its placement
  * model): data blocks are the Q, K/V and O rows (all heads) of `block`
  * consecutive tokens of one sequence, kept on one device; computation blocks
@@ -297,6 +328,28 @@ cva_status cva_placement_create(const int32_t* cu_seqlens, int32_t n_seqs, const
                                 int32_t d_qk, int32_t d_v, int32_t dtype, double epsilon,
                                 cva_placement** out);
 cva_status cva_placement_get(const cva_placement* placement, cva_placement_info* out);
+
+/* One device's share of a placement as a plan (DCP paper, section 4.1: every
+ * computation block pairs a Q block with a K/V block; Fig. 9(b): when several
+ * computation blocks feed one output block their partial results are reduced).
+ * The plan computes every computation block the placement gives `device`: the
+ * block's query rows against its K/V block's keys under the placement's mask,
+ * one fp32 partial output and LSE per block (per 64..256-row query tile), and
+ * merges the partials of blocks that feed the same O block by log-sum-exp.  Run
+ * it with cva_fwd_split (cva_fwd, cva_bwd and cva_plan_get_metadata return
+ * CVA_E_UNSUPPORTED) on the packed, unsplit tensors, every block in place:
+ * q [T, Hq, Dqk], k_rm [T, Hkv, Dqk], v_rm [T, Hkv, Dv], o [T, Hq, Dv],
+ * lse [Hq, T] with T = cu_seqlens[n].  It writes the rows of the O blocks the
+ * device contributes to -- the device's partial result over its own
+ * computation blocks, normalised, with its LSE (what it would send to the O
+ * block's owner; the owner merges the devices' results the same way) -- and
+ * leaves every other row untouched.  Needs bf16/fp16, a supported head shape
+ * and a block size that is a multiple of 64.  The plan is independent of the
+ * placement object afterwards (release with cva_plan_destroy).  Errors:
+ * CVA_E_RANK (device out of range), CVA_E_UNSUPPORTED, CVA_E_HEADS,
+ * CVA_E_HEADDIM. */
+cva_status cva_placement_plan_create(const cva_placement* placement, int32_t device,
+                                     cva_plan** out);
 void cva_placement_destroy(cva_placement* placement);
 
 /* Per-kernel timing, for benchmarks.  While enabled, cva_fwd and cva_bwd

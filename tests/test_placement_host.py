@@ -172,3 +172,58 @@ def test_invalid_placements_rejected(kw, status):
         cva.Placement(a["cu"], a["R"], a["B"], hq=a["hq"], mask=a["mask"], sink=a["sink"],
                       window=a["window"], mask_block=a["mask_block"], epsilon=a["eps"])
     assert ei.value.status_name == status, str(ei.value)
+
+
+# ---- one device's share as a plan: its forward items cover exactly its blocks ----
+
+from oracle.masks import mask_ref as _mask_ref_oracle  # noqa: E402
+
+
+@pytest.mark.parametrize("mask", ["causal", "lambda", "shared_prefix", "blockwise"])
+def test_placed_plan_items_cover_exactly_the_device_blocks(mask):
+    """Every visible (query, key) pair of a device's computation blocks is in exactly
+    one forward item of its plan and no other pair is; a span marked full has every
+    valid row seeing every key of its tiles; items of one Q tile merge together."""
+    lens = [640, 384, 1000]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    bb = None
+    if mask == "shared_prefix":
+        bb = np.array([synth.shared_prefix_bounds(L, prefix=128) for L in lens])
+    kw = dict(sink=32, window=200) if mask == "lambda" else dict(sink=1, window=2, mask_block=64)
+    pl = cva.Placement(cu, 3, 128, hq=4, hkv=2, d_qk=128, mask=mask, branch_bounds=bb, **kw)
+    masks = [_mask_ref_oracle(mask, L, kw.get("sink", 0), kw.get("window", 0),
+                              None if bb is None else bb[i], kw.get("mask_block", 0))
+             for i, L in enumerate(lens)]
+    B = 128
+    multi = 0
+    for d in range(3):
+        pp = pl.device_plan(d)
+        t = pp.tables()
+        segs = t["segs"]
+        tile_q, tile_kv, tiles, spans = pp.schedule(3)
+        cnt = [np.zeros((L, L), np.int64) for L in lens]
+        for (sg, q0, rows, s0, ns) in tiles:
+            i, qb, qlen = segs[sg, 0], segs[sg, 1], segs[sg, 2]
+            assert segs[sg, 4] == cu[i] + qb * B and qlen == min(B, lens[i] - qb * B)
+            qrows = np.arange(qb * B + q0, qb * B + q0 + rows)
+            for (t0, t1, partial, _) in spans[s0: s0 + ns]:
+                keys = np.arange(t0 * tile_kv, min(t1 * tile_kv, lens[i]))
+                vis = masks[i][np.ix_(qrows, keys)]
+                cnt[i][np.ix_(qrows, keys)] += vis
+                if not partial:
+                    assert vis.all(), "a span marked full has a masked element"
+        want = [np.zeros((L, L), np.int64) for L in lens]
+        for (i, qb, kb, dev) in pl.comp_blocks:
+            if dev == d:
+                want[i][qb * B:(qb + 1) * B, kb * B:(kb + 1) * B] = masks[i][qb * B:(qb + 1) * B,
+                                                                               kb * B:(kb + 1) * B]
+        for i in range(len(lens)):
+            assert np.array_equal(cnt[i], want[i]), (d, i)
+        # merge records: one per Q tile of every segment, over the slots of its items
+        comb = t["split_combine"]
+        slot_of_item = t["split_slot"]
+        for (sg, q0, rows, slot0, npiece) in comb:
+            items = [n for n in range(len(tiles)) if tiles[n, 0] == sg and tiles[n, 1] == q0]
+            assert sorted(slot_of_item[items]) == list(range(slot0, slot0 + npiece))
+            multi = max(multi, npiece)
+    assert multi >= 2  # some output tile is fed by several computation blocks
