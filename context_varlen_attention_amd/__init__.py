@@ -29,7 +29,9 @@ __all__ = ["Plan", "Placement", "PlacedPlan", "fwd", "bwd", "bwd_noalloc", "CvaE
            "timing_select"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libcva.so")
+# CVA_LIBRARY selects another build of the same library (e.g. the host-sanitized
+# one the CPU tests use); by default the in-tree libcva.so next to this file.
+_LIB_PATH = os.environ.get("CVA_LIBRARY") or os.path.join(_HERE, "libcva.so")
 _lib = None
 
 DTYPES = {"bf16": 0, "fp16": 1, "fp32": 2}

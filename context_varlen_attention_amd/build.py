@@ -32,6 +32,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__"]
+# Host-only checking build (build_host_sanitized): AddressSanitizer and
+# UndefinedBehaviorSanitizer on the host C++ (g++ only; the HIP kernels are
+# built exactly as in the product library and are not instrumented).
+SANITIZE_HOST_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                       "-fno-sanitize-recover=all"]
 
 
 def _run(cmd):
@@ -70,6 +75,35 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
     return LIB
+
+
+def build_host_sanitized(out_path: str, jobs: int = 8) -> str:
+    """libcva with its host C++ (validation, metadata, schedules, placement, C
+    ABI) compiled with ASan + UBSan, for CPU test runs with the sanitizer
+    runtime preloaded (the binding loads it when CVA_LIBRARY names it)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = tempfile.mkdtemp(prefix="cva_san_")
+    try:
+        inc = ["-I", INCLUDE, "-I", CSRC, "-I", os.path.join(ROCM, "include")]
+        cmds, objs = [], []
+        for src in HIP_SOURCES:
+            obj = os.path.join(objdir, os.path.basename(src) + ".o")
+            cmds.append([HIPCC, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+        host_flags = [f for f in HOST_FLAGS if f != "-O2"] + SANITIZE_HOST_FLAGS
+        for src in HOST_SOURCES:
+            obj = os.path.join(objdir, os.path.basename(src) + ".san.o")
+            cmds.append(["g++", *host_flags, *inc, "-c", os.path.join(CSRC, src), "-o", obj])
+            objs.append(obj)
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            list(ex.map(_run, cmds))
+        rocm_lib = os.path.join(ROCM, "lib")
+        _run(["g++", "-shared", "-fPIC", *SANITIZE_HOST_FLAGS, *objs, "-o", out_path,
+              "-L", rocm_lib, "-Wl,-rpath," + rocm_lib, "-lamdhip64"])
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
+    return out_path
 
 
 if __name__ == "__main__":
