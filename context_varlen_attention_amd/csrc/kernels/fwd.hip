@@ -52,6 +52,7 @@ constexpr int kBN = 64;                    // keys per K/V tile
 // units), i.e. a P value may reach 2^8 before the base moves
 constexpr float kRescaleLimit = 256.0f;
 constexpr int kReadAhead = 6;              // MFMAs between an LDS operand read and its use
+constexpr int kXReadAhead = 3;             // MFMA pairs between an operand read and its use (Dqk == Dv)
 
 // LDS layouts (16-byte chunks, XOR-swizzled so that the MFMA operand reads are
 // bank-conflict free on gfx950's 64 x 4-byte-bank LDS, as measured with the
@@ -533,6 +534,44 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   auto scores = [&](int n) {  // S(n) - base from K ring slot n % NS
     tile_scores<E, DQK, kFromBase>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, nbase);
   };
+  // X(n) when Dqk == Dv (as many score as PV MFMAs): the score MFMAs of tile n+1
+  // and the PV MFMAs of tile n alternate, every LDS operand read issued AH MFMA
+  // pairs ahead of its use and the order pinned pair by pair, so that the reads
+  // are spread over the step and none is waited for right after its issue
+  auto x_step_interleaved = [&](int n) {
+    constexpr int KO = kKoff<DQK>;
+    constexpr int NP = 2 * KSTEPS;  // == 4 * DB
+    constexpr int AH = kXReadAhead;
+    const uint16_t* sv = (const uint16_t*)((const char*)sV + (n % NS) * VBUF);
+    const uint16_t* skk = (const uint16_t*)((const char*)sK + ((n + 1) % NS) * KBUF);
+    auto readk = [&](int i) {
+      const int kt = i >> 1, nb = i & 1;
+      return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
+    };
+    auto readv = [&](int i, u32x2_t& lo, u32x2_t& hi) {  // PV operand i: (nb, ks, d) = (i / 2DB, i / DB % 2, i % DB)
+      const int key0 = (i / (2 * DB)) * 32 + ((i / DB) & 1) * 16, d = i % DB;
+      lo = lds_read_tr(sv + key0 * DV, voff[d]);
+      hi = lds_read_tr(sv + (key0 + 8) * DV, voff[d]);
+    };
+    u32x4_t kr[AH];
+    u32x2_t vl[AH], vh[AH];
+#pragma unroll
+    for (int j = 0; j < AH; ++j) {
+      kr[j] = readk(j);
+      readv(j, vl[j], vh[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int kt = i >> 1, nb = i & 1;
+      s[nb] = E::mfma32(as_vec8<E>(kr[i % AH]), qf[kt], (kFromBase && kt == 0) ? nbase : s[nb]);
+      if (i + AH < NP) kr[i % AH] = readk(i + AH);
+      const int pnbks = i / DB, d = i % DB;
+      st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{vl[i % AH][0], vl[i % AH][1], vh[i % AH][0], vh[i % AH][1]}),
+                            as_vec8<E>(pk[pnbks >> 1][pnbks & 1]), st.acc[d]);
+      if (i + AH < NP) readv(i + AH, vl[i % AH], vh[i % AH]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   auto init_scores = [&]() {
     if constexpr (!kFromBase) {
 #pragma unroll
@@ -613,6 +652,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       if constexpr (kSplitIssue) issue_k_part(n);
       else issue_batch(n);
     }
+    if constexpr (DQK == DV) {
+      x_step_interleaved(n);
+    } else {
     pv(n);
     scores(n + 1);
     {
@@ -632,6 +674,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         if (PVM + i + AHEAD < PVM + SM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+    }
     }
     __syncthreads();
     softmax(cY);
