@@ -87,7 +87,7 @@ class LookAheadPlanner:
                     t0 = time.perf_counter()
                     p = make_plan(self.cva, self.w)
                     self.build_s.append(time.perf_counter() - t0)
-                    p.upload(stream=self.stream)  # returns after the copy has landed
+                    p.upload(stream=self.stream)  # async; launches on the main stream wait for it
                     self.q.put(p)
         except BaseException as e:  # surfaced to the consumer
             self.err = e

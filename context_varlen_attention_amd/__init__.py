@@ -239,18 +239,30 @@ class _PlanBase:
         return int(load_library().cva_plan_device_bytes(self._h))
 
     def upload(self, device=None, stream=None):
-        """Copy the plan tables into a torch uint8 buffer on ``device`` and bind them."""
+        """Copy the plan tables into a torch uint8 buffer on ``device`` and bind them
+        (asynchronously, on ``stream``; launches on other streams wait for the copy)."""
         import torch
         dev = torch.device("cuda") if device is None else torch.device(device)
+        s = torch.cuda.current_stream(dev) if stream is None else stream
         nbytes = self.device_bytes()
-        buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(s):
+            buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
         off = (-buf.data_ptr()) % 256
         view = buf[off: off + nbytes]
-        s = _stream_ptr(stream, dev)
         _check(load_library().cva_plan_upload(self._h, ctypes.c_void_p(view.data_ptr()),
-                                              nbytes, s))
+                                              nbytes, ctypes.c_void_p(s.cuda_stream)))
+        ready = torch.cuda.Event()
+        ready.record(s)
         self._dev = buf  # keep alive while the plan is used
+        self._dev_stream, self._dev_ready = s, ready
         return self
+
+    def _bind_stream(self, s):
+        """Order a launch on stream ``s`` after the upload, and keep the table buffer
+        from being reused while ``s`` may still read it."""
+        if s != self._dev_stream:
+            s.wait_event(self._dev_ready)
+            self._dev.record_stream(s)
 
     @property
     def uploaded(self):
@@ -431,11 +443,20 @@ class PlacedPlan(_PlanBase):
         self.blocks = placement.comp_blocks[placement.comp_blocks[:, 3] == self.device]
 
 
-def _stream_ptr(stream, device):
+def _launch_stream(plan, stream, device, tensors):
+    """The stream a call runs on.  Caller tensors allocated on another stream are
+    marked as used by it (record_stream), so that the caching allocator does not
+    hand their memory out again while the call may still run; the plan's tables
+    are ordered after their upload."""
     import torch
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return ctypes.c_void_p(stream.cuda_stream)
+    cur = torch.cuda.current_stream(device)
+    s = cur if stream is None else stream
+    if s != cur:
+        for t in tensors:
+            if t is not None:
+                t.record_stream(s)
+    plan._bind_stream(s)
+    return s
 
 
 _TORCH_DT = {"bf16": "bfloat16", "fp16": "float16", "fp32": "float32"}
@@ -478,25 +499,30 @@ def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, strea
     _expect(q, "q", (Tl, plan.hq, plan.d_qk), dt, dev)
     _expect(k_rm, "k_rm", (T, plan.hkv, plan.d_qk), dt, dev)
     _expect(v_rm, "v_rm", (T, plan.hkv, plan.d_v), dt, dev)
-    if out is None:
-        out = torch.empty((Tl, plan.hq, plan.d_v), dtype=q.dtype, device=dev)
+    s = _launch_stream(plan, stream, dev, (q, k_rm, v_rm, out, lse))
+    with torch.cuda.stream(s):  # outputs made here belong to the launch stream
+        if out is None:
+            out = torch.empty((Tl, plan.hq, plan.d_v), dtype=q.dtype, device=dev)
+        if lse is None:
+            lse = torch.empty((plan.hq, Tl), dtype=torch.float32, device=dev)
     _expect(out, "out", (Tl, plan.hq, plan.d_v), dt, dev)
-    if lse is None:
-        lse = torch.empty((plan.hq, Tl), dtype=torch.float32, device=dev)
     _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
     vp = ctypes.c_void_p
     L = load_library()
     if workspace is None:
         _check(L.cva_fwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
                          vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
-                         _stream_ptr(stream, dev)))
+                         vp(s.cuda_stream)))
         return out, lse
     if workspace is True:
-        workspace = torch.empty(max(plan.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(plan.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    elif s != torch.cuda.current_stream(dev):
+        workspace.record_stream(s)
     _check(L.cva_fwd_split(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
                            vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
                            vp(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
-                           _stream_ptr(stream, dev)))
+                           vp(s.cuda_stream)))
     return out, lse
 
 
@@ -515,25 +541,27 @@ def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk
     _expect(o, "o", (Tl, plan.hq, plan.d_v), dt, dev)
     _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
     _expect(dout, "dout", (Tl, plan.hq, plan.d_v), dt, dev)
-    if dq is None:
-        dq = torch.empty_like(q)
-    if dk_rm is None:
-        dk_rm = torch.empty_like(k_rm)
-    if dv_rm is None:
-        dv_rm = torch.empty_like(v_rm)
+    s = _launch_stream(plan, stream, dev, (q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, workspace))
+    L = load_library()
+    ws_bytes = int(L.cva_bwd_workspace_bytes(plan.handle))
+    with torch.cuda.stream(s):  # outputs and workspace made here belong to the launch stream
+        if dq is None:
+            dq = torch.empty_like(q)
+        if dk_rm is None:
+            dk_rm = torch.empty_like(k_rm)
+        if dv_rm is None:
+            dv_rm = torch.empty_like(v_rm)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=dev)
     _expect(dq, "dq", (Tl, plan.hq, plan.d_qk), dt, dev)
     _expect(dk_rm, "dk_rm", (T, plan.hkv, plan.d_qk), dt, dev)
     _expect(dv_rm, "dv_rm", (T, plan.hkv, plan.d_v), dt, dev)
-    L = load_library()
-    ws_bytes = int(L.cva_bwd_workspace_bytes(plan.handle))
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 4), dtype=torch.uint8, device=dev)
     vp = ctypes.c_void_p
     _check(L.cva_bwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
                      vp(o.data_ptr()), vp(lse.data_ptr()), vp(dout.data_ptr()), vp(dq.data_ptr()),
                      vp(dk_rm.data_ptr()), vp(dv_rm.data_ptr()), vp(workspace.data_ptr()),
                      workspace.numel() * workspace.element_size(), _scale(plan, softmax_scale),
-                     _stream_ptr(stream, dev)))
+                     vp(s.cuda_stream)))
     return dq, dk_rm, dv_rm
 
 
@@ -551,11 +579,12 @@ def bwd_noalloc(plan: Plan, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, softm
                            (dv_rm, "dv_rm", (T, plan.hkv, plan.d_v))):
         _expect(t, name, shape, dt, dev)
     _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
+    s = _launch_stream(plan, stream, dev, (q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm))
     vp = ctypes.c_void_p
     _check(load_library().cva_bwd_noalloc(
         plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()), vp(o.data_ptr()),
         vp(lse.data_ptr()), vp(dout.data_ptr()), vp(dq.data_ptr()), vp(dk_rm.data_ptr()),
-        vp(dv_rm.data_ptr()), _scale(plan, softmax_scale), _stream_ptr(stream, dev)))
+        vp(dv_rm.data_ptr()), _scale(plan, softmax_scale), vp(s.cuda_stream)))
     return dq, dk_rm, dv_rm
 
 

@@ -6,9 +6,11 @@
 // stream, all arguments checked on the host first so that a failing call
 // enqueues nothing (MindSpeed RFC section 3.4: validate before any operator
 // call).
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <sstream>
 #include <vector>
@@ -58,9 +60,13 @@ cva_status check_scale(float s) {
 }
 
 // Event-pair timing around kernel launches (cva_timing_enable / cva_timing_read).
+// One process-wide timer; its state is guarded by a mutex so that launches from
+// several host threads record their events without corrupting it (each
+// before/after pair is taken under one lock held across the launch).
 struct Timer final : cva::LaunchHook {
+  std::mutex mu;
   struct Rec { int kernel; hipEvent_t a, b; };
-  bool on = false;
+  std::atomic<bool> on{false};
   std::vector<Rec> pending;
   std::vector<hipEvent_t> pool;
   int64_t launches[CVA_N_KERNELS] = {};
@@ -74,6 +80,7 @@ struct Timer final : cva::LaunchHook {
   uint32_t mask = ~0u;  // kernels to time
   bool skip = false;    // the launch in flight is not timed
   void before(int kernel, hipStream_t s) override {
+    mu.lock();  // released in after(): the launch between them is recorded as one pair
     skip = ((mask >> kernel) & 1u) == 0;
     if (skip) return;
     Rec r{kernel, get(), get()};
@@ -81,8 +88,8 @@ struct Timer final : cva::LaunchHook {
     pending.push_back(r);
   }
   void after(int, hipStream_t s) override {
-    if (skip) return;
-    if (!pending.empty() && pending.back().b) (void)hipEventRecord(pending.back().b, s);
+    if (!skip && !pending.empty() && pending.back().b) (void)hipEventRecord(pending.back().b, s);
+    mu.unlock();
   }
   hipError_t drain() {
     hipError_t err = hipSuccess;
@@ -168,7 +175,15 @@ cva_status cva_plan_create(const int32_t* cu_seqlens, int32_t n_seqs, int32_t cp
   return CVA_OK;
 }
 
-void cva_plan_destroy(cva_plan* plan) { delete reinterpret_cast<Plan*>(plan); }
+void cva_plan_destroy(cva_plan* plan) {
+  Plan* p = reinterpret_cast<Plan*>(plan);
+  if (p != nullptr && p->upload_done != nullptr) {
+    // an upload may still be reading the host tables: let it finish first
+    (void)hipEventSynchronize((hipEvent_t)p->upload_done);
+    (void)hipEventDestroy((hipEvent_t)p->upload_done);
+  }
+  delete p;
+}
 
 cva_status cva_plan_get_metadata(const cva_plan* plan, cva_metadata* out) {
   const Plan* p = reinterpret_cast<const Plan*>(plan);
@@ -208,13 +223,19 @@ cva_status cva_plan_upload(cva_plan* plan, void* dev_buf, size_t bytes, void* st
     return fail(CVA_E_ARG, os.str());
   }
   if (((uintptr_t)dev_buf) % 256 != 0) return fail(CVA_E_ARG, "device buffer must be 256-byte aligned");
+  if (p->upload_done == nullptr) {
+    hipEvent_t ev = nullptr;
+    hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags(plan upload)");
+    p->upload_done = ev;
+  }
+  // the copy reads the plan's own host tables, which stay alive until it has
+  // completed (cva_plan_destroy waits for the event): no host synchronisation
   hipError_t e = hipMemcpyAsync(dev_buf, p->blob.data(), need, hipMemcpyHostToDevice,
                                 (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(plan)");
-  // the copy reads the host blob, which the plan keeps alive; make it complete
-  // before returning so the caller may reuse pageable memory freely
-  e = hipStreamSynchronize((hipStream_t)stream);
-  if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize(plan upload)");
+  e = hipEventRecord((hipEvent_t)p->upload_done, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord(plan upload)");
   p->dev = dev_buf;
   p->dev_bytes = bytes;
   return CVA_OK;
@@ -547,6 +568,7 @@ void cva_placement_destroy(cva_placement* placement) {
 }
 
 cva_status cva_timing_enable(int32_t on) {
+  std::lock_guard<std::mutex> lock(g_timer.mu);
   if (on) {
     hipError_t e = g_timer.drain();
     g_timer.reset();
@@ -559,12 +581,14 @@ cva_status cva_timing_enable(int32_t on) {
 }
 
 cva_status cva_timing_select(uint32_t kernel_mask) {
+  std::lock_guard<std::mutex> lock(g_timer.mu);
   g_timer.mask = kernel_mask;
   return CVA_OK;
 }
 
 cva_status cva_timing_read(cva_kernel_times* out) {
   if (out == nullptr) return fail(CVA_E_ARG, "out is NULL");
+  std::lock_guard<std::mutex> lock(g_timer.mu);
   hipError_t e = g_timer.drain();
   for (int k = 0; k < CVA_N_KERNELS; ++k) {
     out->launches[k] = g_timer.launches[k];

@@ -33,23 +33,6 @@ namespace cva {
 
 namespace {
 
-struct RowSetP {
-  int n = 0;
-  std::pair<int32_t, int32_t> v[2];
-};
-
-RowSetP row_set_p(const int32_t* iv) {
-  RowSetP r;
-  std::pair<int32_t, int32_t> a{iv[0], iv[1]}, b{iv[2], iv[3]};
-  if (a.second <= a.first) std::swap(a, b);
-  if (a.second <= a.first) return r;
-  if (b.second <= b.first) { r.n = 1; r.v[0] = a; return r; }
-  if (b.first < a.first) std::swap(a, b);
-  if (b.first <= a.second) { r.n = 1; r.v[0] = {a.first, std::max(a.second, b.second)}; return r; }
-  r.n = 2; r.v[0] = a; r.v[1] = b;
-  return r;
-}
-
 struct Sizes {
   int64_t q_row, kv_row, o_row;
 };
@@ -133,7 +116,7 @@ cva_status build_placement(Placement& pl) {
       for (int32_t q = qb * B; q < std::min(L, (qb + 1) * B); ++q) {
         int32_t iv[4];
         position_intervals(m, i, q, iv);
-        const RowSetP rs = row_set_p(iv);
+        const KeySet rs = key_set(iv);
         for (int k = 0; k < rs.n; ++k) {
           int32_t a = rs.v[k].first;
           const int32_t e = rs.v[k].second;
@@ -254,7 +237,7 @@ cva_status build_placement(Placement& pl) {
           for (int32_t q = j * c; q < (j + 1) * c; ++q) {
             int32_t iv[4];
             position_intervals(m, i, q, iv);
-            const RowSetP rs = row_set_p(iv);
+            const KeySet rs = key_set(iv);
             for (int k = 0; k < rs.n; ++k) pl.zigzag_pairs[s] += rs.v[k].second - rs.v[k].first;
           }
     }

@@ -4,6 +4,7 @@
 
 #include <cstdint>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "cva.h"
@@ -98,7 +99,36 @@ struct Plan {
   BlobLayout layout;
   void* dev = nullptr;
   size_t dev_bytes = 0;
+  void* upload_done = nullptr;  // hipEvent_t recorded after the last upload's copy (C ABI layer)
 };
+
+// The visible keys of a row, [iv0, iv1) u [iv2, iv3), as at most two disjoint,
+// sorted intervals (overlapping or touching intervals merged).
+struct KeySet {
+  int n = 0;
+  std::pair<int32_t, int32_t> v[2];
+};
+inline KeySet key_set(const int32_t* iv) {
+  KeySet r;
+  std::pair<int32_t, int32_t> a{iv[0], iv[1]}, b{iv[2], iv[3]};
+  if (a.second <= a.first) std::swap(a, b);
+  if (a.second <= a.first) return r;  // both empty
+  if (b.second <= b.first) {
+    r.n = 1;
+    r.v[0] = a;
+    return r;
+  }
+  if (b.first < a.first) std::swap(a, b);
+  if (b.first <= a.second) {
+    r.n = 1;
+    r.v[0] = {a.first, a.second > b.second ? a.second : b.second};
+  } else {
+    r.n = 2;
+    r.v[0] = a;
+    r.v[1] = b;
+  }
+  return r;
+}
 
 // Placement of data and computation blocks over devices (placement.cpp).
 struct Placement {

@@ -37,28 +37,8 @@ using Iv = std::pair<int32_t, int32_t>;  // [first, end)
 using IvList = std::vector<Iv>;
 
 // A row's visible set: at most two disjoint, sorted intervals.
-struct RowSet {
-  int n = 0;
-  Iv v[2];
-};
-
-RowSet row_set(const int32_t* iv) {
-  RowSet r;
-  Iv a{iv[0], iv[1]}, b{iv[2], iv[3]};
-  if (a.second <= a.first) std::swap(a, b);
-  if (a.second <= a.first) return r;                 // both empty
-  if (b.second <= b.first) { r.n = 1; r.v[0] = a; return r; }
-  if (b.first < a.first) std::swap(a, b);
-  if (b.first <= a.second) {                          // overlap or touch: merge
-    r.n = 1;
-    r.v[0] = {a.first, std::max(a.second, b.second)};
-  } else {
-    r.n = 2;
-    r.v[0] = a;
-    r.v[1] = b;
-  }
-  return r;
-}
+using RowSet = KeySet;
+inline RowSet row_set(const int32_t* iv) { return key_set(iv); }
 
 // Intersection of a sorted disjoint list with a row set, in place.
 void intersect_into(IvList& F, const RowSet& s, IvList& tmp) {

@@ -160,7 +160,11 @@ size_t cva_plan_device_bytes(const cva_plan* plan);
 
 /* Copy the plan's tables to caller-owned device memory dev_buf (at least
  * cva_plan_device_bytes bytes, 256-byte aligned) on `stream`, and bind the plan
- * to that buffer for later cva_fwd / cva_bwd calls.  The buffer must stay
+ * to that buffer for later cva_fwd / cva_bwd calls.  The copy is asynchronous:
+ * the call returns once it is enqueued (the plan keeps its host tables alive
+ * until the copy has completed; cva_plan_destroy waits for it).  Calls that use
+ * the plan on `stream` are ordered after the copy; on another stream the caller
+ * orders them (e.g. with an event recorded on `stream`).  The buffer must stay
  * alive and untouched while those calls may run. */
 cva_status cva_plan_upload(cva_plan* plan, void* dev_buf, size_t bytes, void* stream);
 
@@ -360,7 +364,8 @@ void cva_placement_destroy(cva_placement* placement);
  *   0 forward, 3 backward dK/dV, 4 backward dQ (which also forms Delta and
  *   zero-fills the uncovered dK/dV rows), 5 forward merge of split pieces;
  *   ids 1 and 2 are reserved (no kernel of their own any more).
- * Process-wide state; use from one thread at a time. */
+ * Process-wide state, safe to use from several host threads (a mutex guards it;
+ * launches are timed while they are being enqueued, one at a time). */
 #define CVA_N_KERNELS 6
 typedef struct {
   int64_t launches[CVA_N_KERNELS];
