@@ -188,11 +188,16 @@ def kernel_source_hash(kernel):
     return h.hexdigest()[:16]
 
 
+def traffic_key(w):
+    """How counter summaries name a workload: name/mask/dtype."""
+    return f"{w.name}/{w.mask}/{w.dtype}"
+
+
 def measured_traffic(kernel, workload):
     """HBM bytes per launch from a committed counter summary under profiles/.
 
     Summaries carry lines ``<!-- traffic kernel=K workload=W sha=S bytes=B -->``
-    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the factor a plain
+    (W as ``traffic_key`` forms it; FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the factor a plain
     copy of known size gives).  Returns None when no summary matches the
     kernel's current sources.
     """
@@ -430,7 +435,7 @@ def main():
     d = kernels[dom]
     roofline = {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"),
                 "peak": d.get("peak"), "unit": d.get("unit"), "frac": d.get("frac"),
-                "traffic": measured_traffic(dom, w.name),
+                "traffic": measured_traffic(dom, traffic_key(w)),
                 "per_launch": (f"{kfl[dom]:.4e} flop" if dom in kfl else f"{kby.get(dom, 0)} B")}
     fwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("fwd")) or None
     bwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("bwd"))
