@@ -738,49 +738,59 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
 // Q tile, O = sum_p w_p O_p / sum_p w_p and LSE = m + ln(sum_p w_p) with
 // w_p = exp(LSE_p - m), m = max_p LSE_p (the log-sum-exp combination of
 // partial softmax results); any number of pieces, none included (O = 0,
-// LSE = -inf: no visible key).  One thread per (row, head); HBM-bound and small.
+// LSE = -inf: no visible key).  HBM-bound and small: DV/8 threads per (row,
+// head), 8 columns each, so that a wave reads whole partial rows; a work-group
+// takes kMergeThreads / (DV/8) (row, head) pairs of one Q tile and head group.
+constexpr int kMergeThreads = 256;
+template <int DV>
+constexpr int kMergePairs = kMergeThreads / (DV / 8);
+
 template <typename E, int DV>
-__global__ __launch_bounds__(256) void fwd_merge_kernel(FwdParams P) {
-  const int item = blockIdx.x / P.n_head_groups;
-  const int hg = blockIdx.x % P.n_head_groups;
+__global__ __launch_bounds__(kMergeThreads) void fwd_merge_kernel(FwdParams P) {
+  constexpr int TPR = DV / 8;
+  constexpr int RPB = kMergePairs<DV>;
+  const int hpt = P.heads_per_tile;
+  const int nsub = (hpt * P.tile_q + RPB - 1) / RPB;
+  const int sub = blockIdx.x % nsub;
+  const int item = blockIdx.x / nsub / P.n_head_groups;
+  const int hg = blockIdx.x / nsub % P.n_head_groups;
+  const int x = sub * RPB + (int)threadIdx.x / TPR;  // (head, row) pair inside the tile
+  const int d = 8 * ((int)threadIdx.x % TPR);
+  if (x >= hpt * P.tile_q) return;
   const int32_t* cb = P.combine + item * 5;
   const int seg = cb[0], q0 = cb[1], slot0 = cb[3], npiece = cb[4];
   const int32_t* sg = P.t.segs + seg * 8;
   const int q_len = sg[2], q_row0 = sg[4];
-  const int hpt = P.heads_per_tile;
-  for (int x = threadIdx.x; x < hpt * P.tile_q; x += blockDim.x) {
-    const int hh = x / P.tile_q, r = x % P.tile_q;
-    const int a = q0 + r;
-    if (a >= q_len) continue;
-    const int head = hg * hpt + hh;
-    const int64_t row = q_row0 + a;
-    auto srow = [&](int pc) {
-      return ((int64_t)((slot0 + pc) * P.n_head_groups + hg) * hpt + hh) * P.tile_q + r;
-    };
-    float m = -INFINITY;
-    for (int pc = 0; pc < npiece; ++pc) m = fmaxf(m, P.ws_lse[srow(pc)]);
-    uint16_t* orow = (uint16_t*)P.o + (row * P.hq + head) * DV;
-    if (m == -INFINITY) {  // no visible key in any piece
-      for (int d = 0; d < DV; d += 8) *(u32x4_t*)(orow + d) = u32x4_t{0u, 0u, 0u, 0u};
-      P.lse[(int64_t)head * P.t_loc + row] = -INFINITY;
-      continue;
-    }
-    float wsum = 0.f;
-    for (int pc = 0; pc < npiece; ++pc) wsum += expf(P.ws_lse[srow(pc)] - m);
-    const float inv = 1.f / wsum;
-    for (int d = 0; d < DV; d += 8) {
-      f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
-      for (int pc = 0; pc < npiece; ++pc) {
-        const float w = expf(P.ws_lse[srow(pc)] - m);
-        const float* src = P.ws_o + srow(pc) * DV + d;
-        lo += w * *(const f32x4_t*)src;
-        hi += w * *(const f32x4_t*)(src + 4);
-      }
-      *(u32x4_t*)(orow + d) = u32x4_t{pack2<E>(lo[0] * inv, lo[1] * inv), pack2<E>(lo[2] * inv, lo[3] * inv),
-                                      pack2<E>(hi[0] * inv, hi[1] * inv), pack2<E>(hi[2] * inv, hi[3] * inv)};
-    }
-    P.lse[(int64_t)head * P.t_loc + row] = m + logf(wsum);
+  const int hh = x / P.tile_q, r = x % P.tile_q;
+  const int a = q0 + r;
+  if (a >= q_len) return;
+  const int head = hg * hpt + hh;
+  const int64_t row = q_row0 + a;
+  auto srow = [&](int pc) {
+    return ((int64_t)((slot0 + pc) * P.n_head_groups + hg) * hpt + hh) * P.tile_q + r;
+  };
+  float m = -INFINITY;
+  for (int pc = 0; pc < npiece; ++pc) m = fmaxf(m, P.ws_lse[srow(pc)]);
+  uint16_t* orow = (uint16_t*)P.o + (row * P.hq + head) * DV + d;
+  float* lrow = P.lse + (int64_t)head * P.t_loc + row;
+  if (m == -INFINITY) {  // no visible key in any piece
+    *(u32x4_t*)orow = u32x4_t{0u, 0u, 0u, 0u};
+    if (d == 0) *lrow = -INFINITY;
+    return;
   }
+  float wsum = 0.f;
+  f32x4_t lo = {0.f, 0.f, 0.f, 0.f}, hi = {0.f, 0.f, 0.f, 0.f};
+  for (int pc = 0; pc < npiece; ++pc) {
+    const float w = expf(P.ws_lse[srow(pc)] - m);
+    const float* src = P.ws_o + srow(pc) * DV + d;
+    wsum += w;
+    lo += w * *(const f32x4_t*)src;
+    hi += w * *(const f32x4_t*)(src + 4);
+  }
+  const float inv = 1.f / wsum;
+  *(u32x4_t*)orow = u32x4_t{pack2<E>(lo[0] * inv, lo[1] * inv), pack2<E>(lo[2] * inv, lo[3] * inv),
+                            pack2<E>(hi[0] * inv, hi[1] * inv), pack2<E>(hi[2] * inv, hi[3] * inv)};
+  if (d == 0) *lrow = m + logf(wsum);
 }
 
 // fp32 correctness kernel: one thread per (query row, head), keys one at a time,
@@ -845,8 +855,9 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_combine == 0) return e;
   if (hook) hook->before(K_FWD_MERGE, s);
-  hipLaunchKernelGGL((fwd_merge_kernel<E, DV>), dim3((unsigned)p.n_combine * (unsigned)p.n_head_groups),
-                     dim3(256), 0, s, p);
+  const unsigned nsub = ((unsigned)(p.heads_per_tile * p.tile_q) + kMergePairs<DV> - 1) / kMergePairs<DV>;
+  hipLaunchKernelGGL((fwd_merge_kernel<E, DV>), dim3((unsigned)p.n_combine * (unsigned)p.n_head_groups * nsub),
+                     dim3(kMergeThreads), 0, s, p);
   if (hook) hook->after(K_FWD_MERGE, s);
   return hipGetLastError();
 }
