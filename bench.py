@@ -20,6 +20,11 @@ other kernels run without instrumentation.  ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long128k]
+                       [--mask M] [--dtype D] [--no-split]
+
+The forward is cva_fwd_split whenever the plan cuts a Q tile's K/V range (a
+tile walking more than 4/3 of the average work per compute unit), else
+cva_fwd; ``--no-split`` forces cva_fwd.
 
 The default workload is the largest single-GPU one: one 131072-token sequence,
 CP rank 3 of 8, 32/8 heads, D=128, bf16, causal, forward + backward.
@@ -164,9 +169,19 @@ def device_info(torch, dev):
     return info
 
 
-def kernel_bytes(w):
-    """HBM-bound kernels: algorithmic bytes per launch (none left on the step's path)."""
-    return {}
+def kernel_bytes(w, split_plan=None):
+    """HBM-bound kernels: algorithmic bytes per launch.  The split forward's merge
+    reads, per (row, head) of a cut Q tile, every piece's fp32 partial row and
+    LSE, and writes the row of O (input dtype) and its LSE."""
+    if split_plan is None:
+        return {}
+    comb = split_plan.tables()["split_combine"]
+    if len(comb) == 0:
+        return {}
+    esz = {"bf16": 2, "fp16": 2, "fp32": 4}[w.dtype]
+    rows, npiece = comb[:, 2].astype(np.int64), comb[:, 4].astype(np.int64)
+    per_row = npiece * (w.d_v + 1) * 4 + w.d_v * esz + 4
+    return {"fwd_merge": int((rows * w.hq * per_row).sum())}
 
 
 KERNEL_SOURCES = {
@@ -308,8 +323,9 @@ def main():
     ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix", "blockwise"])
     ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
     ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
-    ap.add_argument("--split", action="store_true",
-                    help="forward with split K/V ranges (cva_fwd_split) instead of cva_fwd")
+    ap.add_argument("--no-split", action="store_true",
+                    help="always cva_fwd (by default the forward is cva_fwd_split whenever the "
+                         "plan cuts a Q tile's K/V range, i.e. needs a forward workspace)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -351,7 +367,7 @@ def main():
     ws = torch.empty(max(int(cva.load_library().cva_bwd_workspace_bytes(ref_plan.handle)), 4),
                      dtype=torch.uint8, device=dev)
     fwd_ws = None
-    if args.split and ref_plan.fwd_workspace_bytes() > 0:
+    if not args.no_split and ref_plan.fwd_workspace_bytes() > 0:
         fwd_ws = torch.empty(ref_plan.fwd_workspace_bytes(), dtype=torch.uint8, device=dev)
     fwd_only = args.fwd_only or w.dtype == "fp32"
     log(f"workload {w.name}: T={T} T_loc={T_loc} seqs={len(w.lengths)} pairs/head={pairs} "
@@ -408,7 +424,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     kfl = kernel_flops(w, pairs)
     kfl_issued = kernel_flops_issued(w, pairs)
-    kby = kernel_bytes(w)
+    kby = kernel_bytes(w, ref_plan if fwd_ws is not None else None)
     kernels = {}
     for name, (n, tot) in prof_times.items():
         if n == 0:

@@ -177,11 +177,13 @@ cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const 
 
 /* Forward with split K/V ranges (DCP paper, background: block-wise attention
  * with online softmax; a query block's K/V range is cut into pieces whose
- * partial outputs are merged through their log-sum-exp).  The plan cuts every
- * forward Q tile whose K/V walk is longer than the average work per compute
- * unit (or, when the environment variable CVA_FWD_SPLIT_CAP holds an integer
- * >= 1 at cva_plan_create, longer than that many 64-key K/V tiles) into up to 8
- * pieces; each piece writes an fp32 partial output and LSE
+ * partial outputs are merged through their log-sum-exp).  With A the average
+ * work per compute unit in 64-key K/V tiles (at least 8), the plan cuts every
+ * forward Q tile whose K/V walk is longer than 4/3 A (longer than 8 when A is
+ * 8) into up to 8 pieces of at most A tiles; when the environment variable
+ * CVA_FWD_SPLIT_CAP holds an integer c >= 1 at cva_plan_create, every tile
+ * longer than c is cut into pieces of at most c.  Each piece writes an fp32
+ * partial output and LSE
  * to the workspace and a second kernel merges them into o and lse.  Same
  * arguments and results as cva_fwd, plus a caller-owned device workspace of at
  * least cva_fwd_workspace_bytes bytes (256-byte aligned) that must not be used
