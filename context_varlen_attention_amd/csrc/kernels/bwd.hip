@@ -194,14 +194,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
   const int tile = blockIdx.x / P.dq_head_groups;
   const int hg = blockIdx.x % P.dq_head_groups;
   const int32_t* tr = P.t.dq_tiles + tile * 5;
-  const int seg = tr[0], q0 = tr[1], span0 = tr[3], nspan = tr[4];
+  const int seg = tr[0], q0 = tr[1], rows = tr[2], span0 = tr[3], nspan = tr[4];
   const int32_t* sg = P.t.segs + seg * 8;
-  const int q_len = sg[2], kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
+  const int kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
   const int hpt = P.dq_heads_per_tile;
   const int head = hg * hpt + (pw % hpt);
   const int kvh = head / P.group;
   const int a = q0 + (pw / hpt) * 32 + col;
-  const bool valid = a < q_len;
+  const bool valid = a < q0 + rows;  // the tile's own rows (a tile may end inside its segment)
   const int row = q_row0 + a;
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
@@ -861,14 +861,14 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
   const int tile = blockIdx.x / P.dq_head_groups;
   const int hg = blockIdx.x % P.dq_head_groups;
   const int32_t* tr = P.t.dq_tiles + tile * 5;
-  const int seg = tr[0], q0 = tr[1], span0 = tr[3], nspan = tr[4];
+  const int seg = tr[0], q0 = tr[1], rows = tr[2], span0 = tr[3], nspan = tr[4];
   const int32_t* sg = P.t.segs + seg * 8;
-  const int q_len = sg[2], kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
+  const int kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
   const int hpt = P.dq_heads_per_tile;
   const int head = hg * hpt + (wave % hpt);
   const int kvh = head / P.group;
   const int a = q0 + (wave / hpt) * 32 + col;
-  const bool valid = a < q_len;
+  const bool valid = a < q0 + rows;  // the tile's own rows (a tile may end inside its segment)
   const int row = q_row0 + a;
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;

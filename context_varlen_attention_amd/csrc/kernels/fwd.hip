@@ -370,16 +370,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   const int tile = blockIdx.x / P.n_head_groups;
   const int hg = blockIdx.x % P.n_head_groups;
   const int32_t* tr = P.t.fwd_tiles + tile * 5;
-  const int seg = tr[0], q0 = tr[1], span0 = tr[3], nspan = tr[4];
+  const int seg = tr[0], q0 = tr[1], rows = tr[2], span0 = tr[3], nspan = tr[4];
   const int32_t* sg = P.t.segs + seg * 8;
-  const int q_len = sg[2], kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
+  const int kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
   const int hpt = P.heads_per_tile;
   const int head = hg * hpt + (w4 % hpt);
   const int kvh = head / P.group;
   const int rowblk = w4 / hpt + grp * (4 / hpt);
   const int a = q0 + rowblk * 32 + col;  // segment-relative query index of this lane
   const int split_slot = P.slot != nullptr ? P.slot[tile] : -1;  // piece of a split K/V range
-  const bool valid = a < q_len;
+  const bool valid = a < q0 + rows;       // the tile's own rows (a tile may end inside its segment)
   const int row = q_row0 + a;             // local row
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
@@ -758,12 +758,12 @@ __global__ __launch_bounds__(kMergeThreads) void fwd_merge_kernel(FwdParams P) {
   const int d = 8 * ((int)threadIdx.x % TPR);
   if (x >= hpt * P.tile_q) return;
   const int32_t* cb = P.combine + item * 5;
-  const int seg = cb[0], q0 = cb[1], slot0 = cb[3], npiece = cb[4];
+  const int seg = cb[0], q0 = cb[1], rows = cb[2], slot0 = cb[3], npiece = cb[4];
   const int32_t* sg = P.t.segs + seg * 8;
-  const int q_len = sg[2], q_row0 = sg[4];
+  const int q_row0 = sg[4];
   const int hh = x / P.tile_q, r = x % P.tile_q;
+  if (r >= rows) return;
   const int a = q0 + r;
-  if (a >= q_len) return;
   const int head = hg * hpt + hh;
   const int64_t row = q_row0 + a;
   auto srow = [&](int pc) {
@@ -800,13 +800,13 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdParams P) {
   const int tile = blockIdx.x / P.n_head_groups;
   const int hg = blockIdx.x % P.n_head_groups;
   const int32_t* tr = P.t.fwd_tiles + tile * 5;
-  const int seg = tr[0], q0 = tr[1], span0 = tr[3], nspan = tr[4];
+  const int seg = tr[0], q0 = tr[1], rows = tr[2], span0 = tr[3], nspan = tr[4];
   const int32_t* sg = P.t.segs + seg * 8;
-  const int q_len = sg[2], kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
+  const int kv_len = sg[3], q_row0 = sg[4], kv_off = sg[5];
   const int hpt = P.heads_per_tile;
   const int head = hg * hpt + (threadIdx.x % hpt);
   const int a = q0 + threadIdx.x / hpt;
-  if (a >= q_len || a >= q0 + P.tile_q) return;
+  if ((int)threadIdx.x / hpt >= rows) return;
   const int kvh = head / P.group;
   const int row = q_row0 + a;
   const float* qrow = (const float*)P.q + ((int64_t)row * P.hq + head) * DQK;

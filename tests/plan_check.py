@@ -4,9 +4,10 @@ Walks every table the kernels read -- segments, the prefix index, per-row
 visible intervals, the forward / dQ / dK-dV / split schedules and their spans,
 the zero-fill ranges, the split slots and merge records -- and asserts that
 every index a kernel dereferences through them lies inside the buffer it
-addresses: the tile records' segment ids, every row a tile covers, every
+addresses (the tile records' segment ids, every row a tile covers, every
 prefix-index entry a K/V tile loads (rank-major row < T), the rows of each
-zero-fill range, every partial slot.  It reads the tables through the C ABI
+zero-fill range, every partial slot), and that the forward and dQ tiles
+partition every segment's rows.  It reads the tables through the C ABI
 (cva_plan_get_tables / cva_plan_get_schedule) and shares no code with the
 library that builds them.
 """
@@ -53,7 +54,14 @@ def check_plan_tables(plan, n_seqs, T, T_loc):
         sg, q0, rows, s0, ns = tiles.T
         _req(((sg >= 0) & (sg < n_segs)).all(), f"schedule {which}: segment id out of range")
         _req(((q0 >= 0) & (q0 < q_len[sg])).all(), f"schedule {which}: first query outside its segment")
-        _req((rows == np.minimum(tile_q, q_len[sg] - q0)).all(), f"schedule {which}: row count")
+        _req(((rows >= 1) & (rows <= np.minimum(tile_q, q_len[sg] - q0))).all(),
+             f"schedule {which}: row count")
+        if which in (0, 1):  # each row of every segment in exactly one tile (the split repeats tiles)
+            cover = np.zeros(int(q_len.sum()), np.int32)
+            seg0 = np.concatenate([[0], np.cumsum(q_len)[:-1]])
+            for g, a0, n in zip(sg, q0, rows):
+                cover[seg0[g] + a0: seg0[g] + a0 + n] += 1
+            _req((cover == 1).all(), f"schedule {which}: tiles do not partition the segments' rows")
         _req(((ns >= 0) & (ns <= MAX_SPANS[which]) & (s0 >= 0) & (s0 + ns <= len(spans))).all(),
              f"schedule {which}: span range")
         if which == 3:

@@ -112,6 +112,24 @@ def _mask_rows(w, i, pos):
     return oracle.masks.mask_rows_ref(w.mask, L, pos, w.sink, w.window, b, w.block)
 
 
+def _q_cuts(w, pos, tq):
+    """Row ranges of a segment's Q tiles: every tq rows from the segment's start,
+    except under the causal blockwise mask, where the cuts fall on in-sequence
+    positions that are multiples of tq (the first cut rounded down to a multiple
+    of 32 rows; none if that leaves it at 0 or past the end)."""
+    n = len(pos)
+    first = tq
+    if w.mask == "blockwise":
+        f = ((-int(pos[0])) % tq) // 32 * 32
+        if 0 < f < n:
+            first = f
+    cuts, x = [0], min(first, n)
+    while cuts[-1] < n:
+        cuts.append(x)
+        x = min(n, x + tq)
+    return list(zip(cuts[:-1], cuts[1:]))
+
+
 @pytest.mark.parametrize("ci", range(len(MASK_CASES)))
 @pytest.mark.parametrize("which", [0, 1, 3])
 def test_q_schedule_covers_exactly_nonempty_tiles(ci, which):
@@ -120,9 +138,10 @@ def test_q_schedule_covers_exactly_nonempty_tiles(ci, which):
     plan = _plan(w)
     tq, tk, tiles, spans = plan.schedule(which)
     segs = _oracle_segments(w)
+    cuts = {seg: _q_cuts(w, pos, tq) for seg, (i, pos, kv_len) in enumerate(segs)}
     got = {}
     for seg, q0, rows, s0, ns in tiles:
-        assert rows == min(tq, len(segs[seg][1]) - q0)
+        assert (q0, q0 + rows) in cuts[seg]
         for a, b, partial, _ in spans[s0: s0 + ns]:
             for t in range(a, b):
                 assert (seg, q0, t) not in got
@@ -130,8 +149,8 @@ def test_q_schedule_covers_exactly_nonempty_tiles(ci, which):
     exp = {}
     for seg, (i, pos, kv_len) in enumerate(segs):
         M = _mask_rows(w, i, pos)
-        for q0 in range(0, len(pos), tq):
-            blk = M[q0: q0 + tq, :kv_len]
+        for q0, q1 in cuts[seg]:
+            blk = M[q0: q1, :kv_len]
             for t in range((kv_len + tk - 1) // tk):
                 sub = blk[:, t * tk: (t + 1) * tk]
                 if sub.any():
