@@ -321,7 +321,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long128k", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--mask", default=None, choices=[None, "causal", "lambda", "shared_prefix", "blockwise"])
-    ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16"])
+    ap.add_argument("--dtype", default=None, choices=[None, "bf16", "fp16", "fp32"])
     ap.add_argument("--fwd-only", action="store_true", help="time forward only (profiling aid)")
     ap.add_argument("--no-split", action="store_true",
                     help="always cva_fwd (by default the forward is cva_fwd_split whenever the "
