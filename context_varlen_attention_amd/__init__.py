@@ -86,7 +86,11 @@ class _Tables(ctypes.Structure):
                 ("n_zero_ranges", ctypes.c_int32), ("zero_rows", _P32),
                 ("n_split_items", ctypes.c_int32), ("split_slot", _P32),
                 ("n_combine", ctypes.c_int32), ("split_combine", _P32),
-                ("n_split_slots", ctypes.c_int32)]
+                ("n_split_slots", ctypes.c_int32),
+                ("fwd_deal_wgs", ctypes.c_int32), ("fwd_deal_start", _P32),
+                ("fwd_deal_items", _P32), ("n_fwd_deal_items", ctypes.c_int32),
+                ("split_deal_wgs", ctypes.c_int32), ("split_deal_start", _P32),
+                ("split_deal_items", _P32), ("n_split_deal_items", ctypes.c_int32)]
 
 
 class _PlacementInfo(ctypes.Structure):
@@ -229,6 +233,12 @@ class _PlanBase:
             "split_slot": _arr(t.split_slot, t.n_split_items, np.int64),
             "split_combine": _arr(t.split_combine, t.n_combine * 5, np.int64).reshape(-1, 5),
             "n_split_slots": int(t.n_split_slots),
+            "fwd_deal": (int(t.fwd_deal_wgs),
+                         _arr(t.fwd_deal_start, t.fwd_deal_wgs + 1 if t.fwd_deal_wgs else 0, np.int64),
+                         _arr(t.fwd_deal_items, t.n_fwd_deal_items, np.int64)),
+            "split_deal": (int(t.split_deal_wgs),
+                           _arr(t.split_deal_start, t.split_deal_wgs + 1 if t.split_deal_wgs else 0, np.int64),
+                           _arr(t.split_deal_items, t.n_split_deal_items, np.int64)),
         }
 
     def fwd_workspace_bytes(self):

@@ -6,9 +6,11 @@
 // stream, all arguments checked on the host first so that a failing call
 // enqueues nothing (MindSpeed RFC section 3.4: validate before any operator
 // call).
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <new>
@@ -51,6 +53,8 @@ cva::PlanTables tables(const Plan& p) {
   t.zero_rows = b + L.zero_rows;
   t.fwds_slot = b + L.fwds_slot;
   t.fwds_combine = b + L.fwds_combine;
+  t.deal_start = b + L.fwd_deal_start;
+  t.deal_items = b + L.fwd_deal_items;
   return t;
 }
 
@@ -252,6 +256,20 @@ size_t split_bytes(const Plan& p) {
   return o_bytes + rows * sizeof(float);
 }
 
+// Work-groups per head group of the streamed forward for the schedule being
+// launched (its deal), or 0 for one work-group per item.  Measured on MI355X,
+// the streamed form wins at Q/K head dim 192 (the 32k expanded-MLA batch:
+// forward 571 -> 506 us) and loses at 128 (4-26 % on the other batches), so it
+// is the default for head dims above 128 only; CVA_FWD_STREAM=1 / =0 in the
+// environment selects it / one work-group per item for every plan.
+int32_t stream_wgs(const Plan& p, const cva::StreamDeal& d) {
+  if (const char* v = std::getenv("CVA_FWD_STREAM")) {
+    if (v[0] == '0' && v[1] == 0) return 0;
+    if (v[0] == '1' && v[1] == 0) return d.wgs;
+  }
+  return p.d_qk > 128 ? d.wgs : 0;
+}
+
 cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v_rm, void* o,
                    float* lse, float softmax_scale, void* workspace, size_t ws_bytes,
                    bool split, void* stream) {
@@ -298,6 +316,8 @@ cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v
     const int32_t* b = (const int32_t*)p->dev;
     fp.t.fwd_tiles = b + p->layout.fwds_tiles;
     fp.t.fwd_spans = b + p->layout.fwds_spans;
+    fp.t.deal_start = b + p->layout.fwds_deal_start;
+    fp.t.deal_items = b + p->layout.fwds_deal_items;
     fp.n_tiles = p->fwds.n_tiles();
     fp.slot = fp.t.fwds_slot;
     fp.combine = fp.t.fwds_combine;
@@ -306,6 +326,7 @@ cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v
     fp.ws_o = (float*)workspace;
     fp.ws_lse = (float*)((char*)workspace + (rows * p->d_v * sizeof(float) + 255) / 256 * 256);
   }
+  fp.stream_wgs = stream_wgs(*p, split ? p->fwds_deal : p->fwd_deal);
   hipError_t e = cva::launch_fwd(p->dtype, p->d_qk, p->d_v, fp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return CVA_OK;
@@ -461,6 +482,14 @@ cva_status cva_plan_get_tables(const cva_plan* plan, cva_plan_tables* out) {
   out->n_combine = (int32_t)(p->fwds_combine.size() / cva::CB_INTS);
   out->split_combine = p->fwds_combine.data();
   out->n_split_slots = p->n_split_slots;
+  out->fwd_deal_wgs = p->fwd_deal.wgs;
+  out->fwd_deal_start = p->fwd_deal.start.data();
+  out->fwd_deal_items = p->fwd_deal.items.data();
+  out->n_fwd_deal_items = (int32_t)p->fwd_deal.items.size();
+  out->split_deal_wgs = p->fwds_deal.wgs;
+  out->split_deal_start = p->fwds_deal.start.data();
+  out->split_deal_items = p->fwds_deal.items.data();
+  out->n_split_deal_items = (int32_t)p->fwds_deal.items.size();
   return CVA_OK;
 }
 

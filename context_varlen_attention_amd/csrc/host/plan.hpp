@@ -51,7 +51,20 @@ struct BlobLayout {
   int64_t kv_tiles = 0, kv_spans = 0;
   int64_t zero_rows = 0;
   int64_t fwds_tiles = 0, fwds_spans = 0, fwds_slot = 0, fwds_combine = 0;
+  int64_t fwd_deal_start = 0, fwd_deal_items = 0, fwds_deal_start = 0, fwds_deal_items = 0;
   int64_t total = 0;
+};
+
+// Streamed forward (one work-group per CU walking a list of work items as one
+// stream of K/V tiles): the items of a forward schedule dealt to `wgs`
+// work-groups per head group (every head group gets the same deal), each
+// work-group's items in work-group order.  wgs == 0: one work-group per item.
+constexpr int32_t kFwdStreamMaxItems = 48;  // items one work-group holds in LDS
+constexpr int32_t kStreamItemSteps = 1;     // an item boundary's cost, in K/V tile steps
+struct StreamDeal {
+  int32_t wgs = 0;
+  std::vector<int32_t> start;  // [wgs + 1] into items
+  std::vector<int32_t> items;  // schedule item indices
 };
 
 // Combine record of a Q tile whose K/V range was split over several forward
@@ -86,6 +99,7 @@ struct Plan {
   std::vector<int32_t> fwds_combine;  // [m][CB_INTS]
   int32_t n_split_slots = 0;
   int32_t fwd_split_cap = 0;
+  StreamDeal fwd_deal, fwds_deal;  // streamed forward deals of fwd and fwds
   std::vector<int32_t> zero_rows;  // [m][2] rank-major row ranges no local query sees (<= 8 rows each)
 
   // one device's share of a block placement (build_placed_plan): segments are
@@ -183,6 +197,13 @@ void position_intervals(const Plan& p, int32_t seq, int32_t q, int32_t iv[4]);
 cva_status build_schedules(Plan& p);
 void build_blob(Plan& p);
 void build_fwd_split(Plan& p);
+// Deal of schedule s's items to the streamed forward's work-groups
+// (kSplitCUs / head groups of them, at most one per item), round by round:
+// every work-group takes one item per round, the round's items (longest first)
+// going to the least loaded work-groups (load: K/V tile steps +
+// kStreamItemSteps per item); no deal (wgs = 0) for fp32 or when a work-group
+// would get more than kFwdStreamMaxItems items.
+void build_stream_deal(const Plan& p, const Schedule& s, StreamDeal& d);
 
 // Tile shape of the forward kernel for a plan's head shape.
 struct FwdShape {

@@ -26,6 +26,7 @@
 #include <new>
 #include <numeric>
 #include <thread>
+#include <utility>
 
 #include "plan.hpp"
 
@@ -507,6 +508,8 @@ cva_status build_schedules(Plan& p) {
   }
 
   build_fwd_split(p);
+  build_stream_deal(p, p.fwd, p.fwd_deal);
+  build_stream_deal(p, p.fwds, p.fwds_deal);
 
   // rank-major rows outside every prefix are zero in dK/dV
   std::vector<char> covered((size_t)p.T, 0);
@@ -532,10 +535,12 @@ void build_blob(Plan& p) {
   const std::vector<int32_t>* parts[] = {&p.segs, &p.kv_index, &p.row_iv, &p.fwd.tiles, &p.fwd.spans,
                                          &p.dq.tiles, &p.dq.spans, &p.dkdv.tiles, &p.dkdv.spans,
                                          &p.zero_rows, &p.fwds.tiles, &p.fwds.spans, &p.fwds_slot,
-                                         &p.fwds_combine};
+                                         &p.fwds_combine, &p.fwd_deal.start, &p.fwd_deal.items,
+                                         &p.fwds_deal.start, &p.fwds_deal.items};
   int64_t* offs[] = {&L.segs, &L.kv_index, &L.row_iv, &L.fwd_tiles, &L.fwd_spans,
                      &L.dq_tiles, &L.dq_spans, &L.kv_tiles, &L.kv_spans, &L.zero_rows,
-                     &L.fwds_tiles, &L.fwds_spans, &L.fwds_slot, &L.fwds_combine};
+                     &L.fwds_tiles, &L.fwds_spans, &L.fwds_slot, &L.fwds_combine,
+                     &L.fwd_deal_start, &L.fwd_deal_items, &L.fwds_deal_start, &L.fwds_deal_items};
   constexpr int kParts = (int)(sizeof(parts) / sizeof(parts[0]));
   int64_t total = 0;
   for (int k = 0; k < kParts; ++k) {
@@ -644,6 +649,50 @@ void build_fwd_split(Plan& p) {
   }
 }
 
+void build_stream_deal(const Plan& p, const Schedule& s, StreamDeal& d) {
+  d = StreamDeal{};
+  const int32_t n = s.n_tiles();
+  if (n == 0 || p.dtype == CVA_FP32) return;
+  const int32_t groups = p.hq / p.fwd_heads_per_tile;
+  int32_t wgs = std::min<int32_t>(n, std::max<int32_t>(1, kSplitCUs / groups));
+  // CVA_FWD_STREAM_WGS in the environment caps the work-groups per head group
+  // (>= 1), e.g. to give every work-group of a small batch several items
+  if (const char* v = std::getenv("CVA_FWD_STREAM_WGS")) {
+    const long c = std::strtol(v, nullptr, 10);
+    if (c >= 1) wgs = std::min<int32_t>(wgs, (int32_t)c);
+  }
+  if ((n + wgs - 1) / wgs > kFwdStreamMaxItems) return;  // more rounds than the LDS table holds
+  // Round by round (each work-group one item per round, so that the work-groups
+  // of an XCD start their items together and walk the same K/V tiles at about
+  // the same time), the round's items in schedule order (longest first) to the
+  // work-groups in order of their load so far (least loaded first).
+  std::vector<std::vector<int32_t>> lists((size_t)wgs);
+  std::vector<int64_t> load((size_t)wgs, 0);
+  std::vector<int32_t> order((size_t)wgs);
+  for (int32_t r0 = 0; r0 < n; r0 += wgs) {
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return load[(size_t)a] < load[(size_t)b]; });
+    for (int32_t k = 0; k < wgs && r0 + k < n; ++k) {
+      const int32_t t = r0 + k;
+      const int32_t* tr = &s.tiles[(size_t)t * QT_INTS];
+      int64_t steps = kStreamItemSteps;
+      for (int32_t j = 0; j < tr[QT_NSPAN]; ++j) {
+        const int32_t* sp = &s.spans[(size_t)(tr[QT_SPAN0] + j) * SPAN_INTS];
+        steps += sp[1] - sp[0];
+      }
+      const int32_t w = order[(size_t)k];
+      lists[(size_t)w].push_back(t);
+      load[(size_t)w] += steps;
+    }
+  }
+  d.wgs = wgs;
+  d.start.assign(1, 0);
+  for (const auto& li : lists) {
+    d.items.insert(d.items.end(), li.begin(), li.end());
+    d.start.push_back((int32_t)d.items.size());
+  }
+}
+
 }  // namespace cva
 
 namespace cva {
@@ -718,6 +767,8 @@ cva_status build_placed_schedule(Plan& p, const std::vector<PlacedBlock>& blocks
     p.fwds_slot.push_back(it.slot);
     p.fwds.tile_pairs += it.cost;
   }
+  p.fwd_deal = StreamDeal{};
+  build_stream_deal(p, p.fwds, p.fwds_deal);
   return CVA_OK;
 }
 

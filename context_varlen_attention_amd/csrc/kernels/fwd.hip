@@ -734,6 +734,539 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Streamed (persistent) forward: one work-group per CU walks a fixed list of
+// items (Q tile x head group) as one stream of K/V tiles, so that the next
+// item's prefix indices and K/V tiles are fetched while the current item's last
+// tiles run, instead of every work-group starting cold (tile record, segment,
+// indices, Q and the first K tile one after another: several microseconds per
+// item on short walks).
+//
+// Work-group w of head group hg walks the items the plan dealt to w (the same
+// deal for every head group: each item, longest first, to the least loaded
+// work-group), so that every work-group stays on one head group, i.e. on the
+// XCD whose L2 holds that K/V head.  The items' records and spans are copied
+// into LDS at the start.
+//
+// At an item boundary (tile L the last of item k, tile L+1 the first of item
+// k+1) the steps differ from the single-item kernel only here:
+//   Y(L):   before the softmax of tile L each wave loads item k+1's Q row
+//           (into its Q registers: item k's last scores ran in X(L-1)) and
+//           visible intervals, waits for them and pre-scales Q; after the
+//           softmax the next scores start from 0 (item k+1 has no exponent
+//           base yet).  The wait follows the loads at once: a load pending
+//           where two paths join would make the compiler wait for all loads
+//           (those of the tile stream included) before every later use of Q.
+//   X(L):   unchanged: PV(L) of item k, S(L+1) of item k+1.
+//   Y(L+1): item k's epilogue (normalise, write O and LSE or its partial),
+//           then the softmax state is reset and item k+1's softmax runs.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxItems = kFwdStreamMaxItems;  // items per work-group (the plan's deal keeps to it)
+constexpr int kItemInts = 12;
+enum { IT_Q0 = 0, IT_ROWS, IT_KVLEN, IT_QROW0, IT_KVOFF, IT_NSPAN, IT_SLOT, IT_FIRST, IT_NTILES };
+
+// Cursor over the stream of K/V tiles of a work-group's items; it carries its
+// item's span count, prefix offset and length (read from LDS only when it
+// enters a span, so that advancing by a tile and fetching the tile's indices
+// stay on scalar registers).
+struct StreamCursor {
+  int item, sp, t, t_end, partial, nspan, kv_off, kv_len;
+};
+
+__device__ __forceinline__ StreamCursor stream_span(const int32_t (*items)[kItemInts], const int32_t* spans,
+                                                    int item, int sp) {
+  const int4 r = *(const int4*)(spans + (item * kMaxSpans + sp) * 4);
+  return StreamCursor{item, sp, __builtin_amdgcn_readfirstlane(r.x), __builtin_amdgcn_readfirstlane(r.y),
+                      __builtin_amdgcn_readfirstlane(r.z), __builtin_amdgcn_readfirstlane(items[item][IT_NSPAN]),
+                      __builtin_amdgcn_readfirstlane(items[item][IT_KVOFF]),
+                      __builtin_amdgcn_readfirstlane(items[item][IT_KVLEN])};
+}
+
+// First tile of the first item at or after `item` that has tiles (item == n_items: past the end).
+__device__ __forceinline__ StreamCursor stream_item_start(const int32_t (*items)[kItemInts],
+                                                          const int32_t* spans, int item, int n_items) {
+  while (item < n_items && __builtin_amdgcn_readfirstlane(items[item][IT_NSPAN]) == 0) ++item;
+  if (item >= n_items) return StreamCursor{n_items, 0, 0, 0, 0, 0, 0, 1};
+  return stream_span(items, spans, item, 0);
+}
+
+__device__ __forceinline__ StreamCursor stream_next(StreamCursor c, const int32_t (*items)[kItemInts],
+                                                    const int32_t* spans, int n_items) {
+  ++c.t;
+  if (c.t < c.t_end) return c;
+  if (c.sp + 1 < c.nspan) return stream_span(items, spans, c.item, c.sp + 1);
+  return stream_item_start(items, spans, c.item + 1, n_items);
+}
+
+template <typename E, int DQK, int DV>
+__global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
+  using TL = TileLoader<DQK, DV, kThreads / 2>;
+  constexpr int KSTEPS = DQK / 16;
+  constexpr int DB = DV / 32;
+  constexpr int NI = TL::NIDX;
+  constexpr int NS = kStages<DQK>;
+  constexpr int NIR = 2 * NS;
+  constexpr uint32_t KBUF = kBN * DQK * 2, VBUF = kBN * DV * 2;
+  __shared__ __attribute__((aligned(16))) uint16_t sK[NS][kBN * DQK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[NS][kBN * DV];
+  __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][kBN];
+  __shared__ __attribute__((aligned(16))) int32_t sItem[kStreamMaxItems][kItemInts];
+  __shared__ __attribute__((aligned(16))) int32_t sSpans[kStreamMaxItems * kMaxSpans * 4];
+  __shared__ int32_t sTotal;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2, w4 = wave & 3;
+  const int col = lane & 31, half = lane >> 5;
+  const int ltid = w4 * 64 + lane;
+
+  const int hg = blockIdx.x % P.n_head_groups;
+  const int wg = blockIdx.x / P.n_head_groups;
+  const int hpt = P.heads_per_tile;
+  const int head = hg * hpt + (w4 % hpt);
+  const int kvh = head / P.group;
+  const int rowblk = w4 / hpt + grp * (4 / hpt);
+  const int item0 = P.t.deal_start[wg];
+  const int n_items = min(P.t.deal_start[wg + 1] - item0, kStreamMaxItems);
+
+  const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
+  const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
+  const uint32_t kstride = (uint32_t)P.hkv * DQK * 2, vstride = (uint32_t)P.hkv * DV * 2;
+
+  // ---- the work-group's items into LDS ----
+  if (tid < n_items) {
+    const int ti = P.t.deal_items[item0 + tid];
+    const int32_t* tr = P.t.fwd_tiles + ti * 5;
+    const int32_t* sg = P.t.segs + tr[0] * 8;
+    int32_t* it = sItem[tid];
+    it[IT_Q0] = tr[1];
+    it[IT_ROWS] = tr[2];
+    it[IT_KVLEN] = sg[3];
+    it[IT_QROW0] = sg[4];
+    it[IT_KVOFF] = sg[5];
+    it[IT_NSPAN] = tr[4];
+    it[IT_SLOT] = P.slot != nullptr ? P.slot[ti] : -1;
+    it[9] = tr[3];  // first span in the schedule
+  }
+  __syncthreads();
+  for (int x = tid; x < n_items * kMaxSpans; x += kThreads) {
+    const int i = x / kMaxSpans, sp = x % kMaxSpans;
+    if (sp < sItem[i][IT_NSPAN])
+      *(int4*)(sSpans + x * 4) = *(const int4*)(P.t.fwd_spans + (sItem[i][9] + sp) * 4);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int first = 0;
+    for (int i = 0; i < n_items; ++i) {
+      int nt = 0;
+      for (int sp = 0; sp < sItem[i][IT_NSPAN]; ++sp)
+        nt += sSpans[(i * kMaxSpans + sp) * 4 + 1] - sSpans[(i * kMaxSpans + sp) * 4];
+      sItem[i][IT_FIRST] = first;
+      sItem[i][IT_NTILES] = nt;
+      first += nt;
+    }
+    sTotal = first;
+  }
+  __syncthreads();
+  const int n_tiles = __builtin_amdgcn_readfirstlane(sTotal);  // tiles of the whole stream
+
+  // Items without any visible key (unreachable for the supported masks): O = 0, LSE = -inf.
+  for (int i = 0; i < n_items; ++i) {
+    if (__builtin_amdgcn_readfirstlane(sItem[i][IT_NSPAN]) != 0) continue;
+    const int q0 = sItem[i][IT_Q0], a = q0 + rowblk * 32 + col, slot = sItem[i][IT_SLOT];
+    if (a < q0 + sItem[i][IT_ROWS]) {
+      const int row = sItem[i][IT_QROW0] + a;
+      if (slot >= 0) {
+        const int64_t srow = ((int64_t)(slot * P.n_head_groups + hg) * hpt + (w4 % hpt)) * P.tile_q + (a - q0);
+        for (int d = half; d < DV; d += 2) P.ws_o[srow * DV + d] = 0.f;
+        if (half == 0) P.ws_lse[srow] = -INFINITY;
+      } else {
+        uint16_t* orow = (uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV;
+        for (int d = half; d < DV; d += 2) orow[d] = 0;
+        if (half == 0) P.lse[(int64_t)head * P.t_loc + row] = -INFINITY;
+      }
+    }
+  }
+  if (n_tiles == 0) return;
+
+  // ---- tile streaming (group 0), over the whole stream ----
+  StreamCursor cI = stream_item_start(sItem, sSpans, 0, n_items);
+  int next_idx = 0;
+  int bcount[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) bcount[i] = 0;
+  auto fetch_idx = [&]() {
+    const int kb0 = cI.t * kBN;
+    dma4(P.t.kv_index + cI.kv_off + min(kb0 + lane, cI.kv_len - 1), lds_addr(sIdx[next_idx % NIR]));
+    ++next_idx;
+    cI = stream_next(cI, sItem, sSpans, n_items);
+  };
+  int idxK[NI], idxV[NI];
+  auto prepare_batch = [&](int n) {
+    const int mk = n + NS, mv = n + NS - 1;
+    if (mk >= 0 && mk < n_tiles) TL::read_index(idxK, sIdx[mk % NIR], ltid);
+    if (mv >= 0 && mv < n_tiles) TL::read_index(idxV, sIdx[mv % NIR], ltid);
+  };
+  constexpr bool kSplitIssue = NS >= 4;
+  auto issue_k_part = [&](int n) {
+    int cnt = 0;
+    const int mk = n + NS, mi = n + 2 * NS;
+    if (mk >= 0 && mk < n_tiles) {
+      TL::issue_k(sK[mk % NS], kg, idxK, kstride, ltid, w4 * 64);
+      cnt += TL::KN;
+    }
+    if (mi >= 2 * NS && mi < n_tiles) {
+      fetch_idx();
+      cnt += 1;
+    }
+    bcount[(n + NS) % NS] = cnt;
+  };
+  auto issue_v_part = [&](int n) {
+    const int mv = n + NS - 1;
+    if (mv >= 0 && mv < n_tiles) {
+      TL::issue_v(sV[mv % NS], vg, idxV, vstride, ltid, w4 * 64);
+      bcount[(n + NS) % NS] += TL::VN;
+    }
+  };
+  auto issue_batch = [&](int n) {
+    issue_k_part(n);
+    issue_v_part(n);
+  };
+  auto wait_batch = [&](int n) {
+    int allowed = 0;
+#pragma unroll
+    for (int b = 0; b < NS - 2; ++b) allowed += bcount[(n - b + NS) % NS];
+    wait_vmem_le(allowed);
+  };
+
+  // ---- per-item row state of this lane ----
+  // cur: the item whose softmax / PV is running; nxt: the next item (its Q and
+  // intervals are loaded at the end of the current item's last vector step).
+  int cur = stream_item_start(sItem, sSpans, 0, n_items).item;
+  int nxt = stream_item_start(sItem, sSpans, cur + 1, n_items).item;
+  auto item_q0 = [&](int i) { return __builtin_amdgcn_readfirstlane(sItem[i][IT_Q0]); };
+  auto lane_a = [&](int i) { return item_q0(i) + rowblk * 32 + col; };
+  auto lane_valid = [&](int i) { return lane_a(i) < item_q0(i) + sItem[i][IT_ROWS]; };
+  auto lane_row = [&](int i) { return sItem[i][IT_QROW0] + lane_a(i); };
+  const float qscale = P.scale_log2;
+  // Item i's visible intervals (into iv) and its Q row (raw, into qf; scale_q
+  // pre-scales it by scale*log2(e) in place, which is where the compiler waits
+  // for both loads: inside the vector step that issued them)
+  int lo1, hi1, lo2, hi2;
+  int4 niv;
+  typename E::vec8 qf[KSTEPS];
+  auto load_rows = [&](int i, int4& iv) {  // lanes past the item's rows load nothing
+    const bool v = lane_valid(i);
+    const int64_t row = lane_row(i);
+    u32x4_t x[KSTEPS];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) x[t] = u32x4_t{0u, 0u, 0u, 0u};
+    iv = int4{0, 0, 0, 0};
+    if (v) {
+      iv = *(const int4*)(P.t.row_iv + row * 4);
+      const uint16_t* qrow = (const uint16_t*)P.q + (row * P.hq + head) * DQK + 8 * half;
+#pragma unroll
+      for (int t = 0; t < KSTEPS; ++t) x[t] = *(const u32x4_t*)(qrow + 16 * t);
+    }
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) qf[t] = as_vec8<E>(x[t]);
+  };
+  auto scale_q = [&]() {
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+      const u32x4_t x = __builtin_bit_cast(u32x4_t, qf[t]);
+      u32x4_t y;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        y[w] = pack2<E>(E::to_float((uint16_t)(x[w] & 0xFFFFu)) * qscale,
+                        E::to_float((uint16_t)(x[w] >> 16)) * qscale);
+      qf[t] = as_vec8<E>(y);
+    }
+  };
+
+  // group 0: indices of the stream's first 2NS tiles, together with item 0's Q
+  if (grp == 0)
+    for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
+  load_rows(cur, niv);
+  wait_vmem_all();
+  scale_q();
+  lo1 = niv.x; hi1 = niv.y; lo2 = niv.z; hi2 = niv.w;
+  if (grp == 0) {
+    for (int n = -NS; n <= -2; ++n) {
+      prepare_batch(n);
+      issue_batch(n);
+    }
+    wait_batch(-2);
+    prepare_batch(-1);
+  }
+
+  uint32_t koff[kKoff<DQK>], voff[DB];
+  k_offsets<DQK>(koff, col, half);
+  v_offsets<DV>(voff, lane);
+
+  SoftmaxState<DB> st;
+  st.base = 0.f;
+  st.l = 0.f;
+#pragma unroll
+  for (int d = 0; d < DB; ++d) st.acc[d] = zero16();
+  f32x16_t s[2];
+  u32x4_t pk[2][2];
+
+  auto pv = [&](int n) {
+    const uint16_t* sv = (const uint16_t*)((const char*)sV + (n % NS) * VBUF);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const typename E::vec8 bfrag = as_vec8<E>(pk[nb][ks]);
+        const int key0 = nb * 32 + ks * 16;
+#pragma unroll
+        for (int d = 0; d < DB; ++d) {
+          const u32x2_t lo = lds_read_tr(sv + key0 * DV, voff[d]);
+          const u32x2_t hi = lds_read_tr(sv + (key0 + 8) * DV, voff[d]);
+          st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bfrag, st.acc[d]);
+        }
+      }
+  };
+  constexpr bool kFromBase = DQK <= 128;
+  f32x16_t nbase;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nbase[r] = 0.f;
+  auto scores = [&](int n) {
+    tile_scores<E, DQK, kFromBase>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, nbase);
+  };
+  auto x_step_interleaved = [&](int n) {
+    constexpr int KO = kKoff<DQK>;
+    constexpr int NP = 2 * KSTEPS;
+    constexpr int AH = kXReadAhead;
+    const uint16_t* sv = (const uint16_t*)((const char*)sV + (n % NS) * VBUF);
+    const uint16_t* skk = (const uint16_t*)((const char*)sK + ((n + 1) % NS) * KBUF);
+    auto readk = [&](int i) {
+      const int kt = i >> 1, nb = i & 1;
+      return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
+    };
+    auto readv = [&](int i, u32x2_t& lo, u32x2_t& hi) {
+      const int key0 = (i / (2 * DB)) * 32 + ((i / DB) & 1) * 16, d = i % DB;
+      lo = lds_read_tr(sv + key0 * DV, voff[d]);
+      hi = lds_read_tr(sv + (key0 + 8) * DV, voff[d]);
+    };
+    u32x4_t kr[AH];
+    u32x2_t vl[AH], vh[AH];
+#pragma unroll
+    for (int j = 0; j < AH; ++j) {
+      kr[j] = readk(j);
+      readv(j, vl[j], vh[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      const int kt = i >> 1, nb = i & 1;
+      s[nb] = E::mfma32(as_vec8<E>(kr[i % AH]), qf[kt], (kFromBase && kt == 0) ? nbase : s[nb]);
+      if (i + AH < NP) kr[i % AH] = readk(i + AH);
+      const int pnbks = i / DB, d = i % DB;
+      st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{vl[i % AH][0], vl[i % AH][1], vh[i % AH][0], vh[i % AH][1]}),
+                            as_vec8<E>(pk[pnbks >> 1][pnbks & 1]), st.acc[d]);
+      if (i + AH < NP) readv(i + AH, vl[i % AH], vh[i % AH]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto x_step_grouped = [&](int n) {
+    pv(n);
+    scores(n + 1);
+    constexpr int PVM = 4 * DB, SM = 2 * KSTEPS, AHEAD = DQK > 128 ? 3 : kReadAhead;
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+    for (int i = 0; i < PVM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      const int next = i + AHEAD;
+      if (next < PVM) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      else if (next - PVM < SM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < SM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (PVM + i + AHEAD < PVM + SM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  };
+  auto init_scores = [&]() {
+    if constexpr (!kFromBase) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
+    }
+  };
+  auto exp_pack = [&](float& lt) {
+    lt = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 8 * ks + 2 * j;
+          pk[nb][ks][j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
+          lt = dot2_acc<E>(pk[nb][ks][j], lt);
+        }
+  };
+  bool valid = lane_valid(cur);
+  auto softmax = [&](const StreamCursor& c) {
+    if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
+    float lt;
+    exp_pack(lt);
+    const bool slow = valid & ((lt > kRescaleLimit) | (st.l == 0.f));
+    if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+      const float mx = tile_max(s);
+      const bool empty = wave_half_sum(st.l) == 0.f;
+      const bool grow = (mx > 0.f) | (empty & (mx > -INFINITY));
+      const float shift = grow ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-shift);
+      st.base += shift;
+      st.l *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) nbase[r] = -st.base;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.acc[d][r] *= alpha;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][r] -= shift;
+      exp_pack(lt);
+    }
+    st.l += lt;
+  };
+  // normalise and write item i's rows (O and LSE, or its fp32 partial)
+  auto epilogue = [&](int i) {
+    const float l_tot = wave_half_sum(st.l);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (!valid) return;
+    const int q0 = item_q0(i), a = lane_a(i), slot = sItem[i][IT_SLOT];
+    const float lse2 = l_tot > 0.f ? st.base + __log2f(l_tot) : -INFINITY;
+    if (slot >= 0) {
+      const int64_t srow = ((int64_t)(slot * P.n_head_groups + hg) * hpt + (w4 % hpt)) * P.tile_q + (a - q0);
+      float* orow = P.ws_o + srow * DV;
+#pragma unroll
+      for (int d = 0; d < DB; ++d)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int dd = d * 32 + 8 * i4 + 4 * half;
+          *(f32x4_t*)(orow + dd) = f32x4_t{st.acc[d][4 * i4] * inv, st.acc[d][4 * i4 + 1] * inv,
+                                           st.acc[d][4 * i4 + 2] * inv, st.acc[d][4 * i4 + 3] * inv};
+        }
+      if (half == 0) P.ws_lse[srow] = lse2 * 0.69314718055994530942f;
+      return;
+    }
+    const int row = lane_row(i);
+    uint16_t* orow = (uint16_t*)P.o + ((int64_t)row * P.hq + head) * DV;
+#pragma unroll
+    for (int d = 0; d < DB; ++d)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int dd = d * 32 + 8 * i4 + 4 * half;
+        *(u32x2_t*)(orow + dd) = u32x2_t{pack2<E>(st.acc[d][4 * i4] * inv, st.acc[d][4 * i4 + 1] * inv),
+                                         pack2<E>(st.acc[d][4 * i4 + 2] * inv, st.acc[d][4 * i4 + 3] * inv)};
+      }
+    if (half == 0) P.lse[(int64_t)head * P.t_loc + row] = lse2 * 0.69314718055994530942f;
+  };
+
+  // The last vector step of item cur (cur's Q is done: its last scores ran in
+  // the MFMA step before): item nxt's Q and intervals are loaded and awaited
+  // at once, then Q is pre-scaled; after the softmax the next scores (item
+  // nxt's first) start from 0, as nxt has no base.  (The wait sits right after
+  // the loads so that no load is pending where the paths join: the compiler
+  // would otherwise wait for every load before each later use of Q.)
+  auto next_item_rows = [&]() {
+    load_rows(nxt, niv);
+    wait_vmem_all();
+    scale_q();
+  };
+  auto next_item_seed = [&]() {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nbase[r] = 0.f;
+    if constexpr (!kFromBase) {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) s[nb] = zero16();
+    }
+  };
+  // The first vector step of item nxt: cur's epilogue, then the switch.
+  auto start_next_item = [&]() {
+    epilogue(cur);
+    cur = nxt;
+    valid = lane_valid(cur);
+    lo1 = niv.x; hi1 = niv.y; lo2 = niv.z; hi2 = niv.w;
+    st.base = 0.f;
+    st.l = 0.f;
+#pragma unroll
+    for (int d = 0; d < DB; ++d) st.acc[d] = zero16();
+    nxt = stream_item_start(sItem, sSpans, cur + 1, n_items).item;
+  };
+
+  // stream positions of the item boundaries: the first tile of the item after cur
+  auto first_after = [&](int i) {
+    const StreamCursor c = stream_item_start(sItem, sSpans, i + 1, n_items);
+    return c.item < n_items ? __builtin_amdgcn_readfirstlane(sItem[c.item][IT_FIRST]) : n_tiles;
+  };
+  int boundary = first_after(cur);  // stream index of item nxt's first tile (n_tiles: none)
+
+  StreamCursor cY = stream_item_start(sItem, sSpans, 0, n_items);
+  __syncthreads();                // K(0) is in LDS
+  if (grp == 1) __syncthreads();  // group 1 runs one phase behind
+
+  // X(-1) = S(0); Y(0)
+  if (grp == 0) issue_batch(-1);
+  init_scores();
+  scores(0);
+  __syncthreads();
+  {
+    const bool last = boundary == 1 && nxt < n_items;  // item 0 has one tile
+    if (last) next_item_rows();
+    softmax(cY);
+    if (last) next_item_seed();
+    else init_scores();
+  }
+  cY = stream_next(cY, sItem, sSpans, n_items);
+  if (grp == 0) {
+    wait_batch(-1);
+    prepare_batch(0);
+  }
+  __syncthreads();
+  for (int n = 0; n + 1 < n_tiles; ++n) {
+    // X(n) = PV(n) + S(n+1) (S(n+1) is item nxt's first when n + 1 == boundary)
+    if (grp == 0) {
+      if constexpr (kSplitIssue) issue_k_part(n);
+      else issue_batch(n);
+    }
+    if constexpr (DQK == DV) x_step_interleaved(n);
+    else x_step_grouped(n);
+    __syncthreads();
+    // Y(n+1)
+    if (n + 1 == boundary) {
+      start_next_item();
+      boundary = first_after(cur);
+    }
+    const bool last = n + 2 == boundary && nxt < n_items;  // tile n+1 is cur's last
+    if (last) next_item_rows();
+    softmax(cY);
+    if (last) next_item_seed();
+    else init_scores();
+    cY = stream_next(cY, sItem, sSpans, n_items);
+    if (grp == 0) {
+      if constexpr (kSplitIssue) issue_v_part(n);
+      wait_batch(n);
+      prepare_batch(n + 1);
+    }
+    __syncthreads();
+  }
+  // X(N-1) = PV(N-1)
+  pv(n_tiles - 1);
+  __syncthreads();
+  if (grp == 0) __syncthreads();
+  wait_vmem_all();
+  epilogue(cur);
+}
+
 // Merge of the pieces of split K/V ranges: for every (query row, head) of a split
 // Q tile, O = sum_p w_p O_p / sum_p w_p and LSE = m + ln(sum_p w_p) with
 // w_p = exp(LSE_p - m), m = max_p LSE_p (the log-sum-exp combination of
@@ -850,7 +1383,11 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.n_head_groups;
   if (grid == 0) return hipSuccess;
   if (hook) hook->before(K_FWD, s);
-  hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (p.stream_wgs > 0)
+    hipLaunchKernelGGL((fwd_stream_kernel<E, DQK, DV>), dim3((unsigned)p.stream_wgs * (unsigned)p.n_head_groups),
+                       dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV>), dim3(grid), dim3(kThreads), 0, s, p);
   if (hook) hook->after(K_FWD, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_combine == 0) return e;

@@ -22,6 +22,8 @@ struct PlanTables {
   const int32_t* zero_rows;
   const int32_t* fwds_slot;     // split forward: partial slot per item (-1: direct)
   const int32_t* fwds_combine;  // split forward: merge records
+  const int32_t* deal_start;    // streamed forward: [wgs + 1] of the schedule launched
+  const int32_t* deal_items;    // streamed forward: items per work-group
 };
 
 struct FwdParams {
@@ -45,6 +47,10 @@ struct FwdParams {
   float* ws_lse;           // [slots * hq * tile_q] partial LSE (natural log)
   const int32_t* combine;  // [n_combine][5] merge records
   int32_t n_combine;
+  // streamed forward: work-groups per head group, each walking its items
+  // (t.deal_start / t.deal_items) as one stream of K/V tiles (0: one
+  // work-group per item)
+  int32_t stream_wgs;
 };
 
 struct BwdParams {

@@ -264,7 +264,14 @@ cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedu
  *   zero_rows     [n_zero_ranges][2] rank-major row ranges the backward zero-fills
  *   split_slot    [n_split_items] partial slot of every item of schedule 3, or -1
  *   split_combine [n_combine][5] {segment, first query, rows, first slot, pieces}
- *   n_split_slots partial slots of schedule 3 */
+ *   n_split_slots partial slots of schedule 3
+ *   fwd_deal_*    the streamed forward's deal of schedule 0's items (the
+ *                 environment variable CVA_FWD_STREAM_WGS, an integer >= 1 at
+ *                 cva_plan_create, caps wgs): wgs
+ *                 work-groups per head group (0: one work-group per item), work-group
+ *                 w takes items fwd_deal_items[fwd_deal_start[w] ..
+ *                 fwd_deal_start[w+1]) (start has wgs+1 entries)
+ *   split_deal_*  the same for schedule 3 */
 typedef struct {
   int32_t n_segs;
   const int32_t* segs;
@@ -279,6 +286,14 @@ typedef struct {
   int32_t n_combine;
   const int32_t* split_combine;
   int32_t n_split_slots;
+  int32_t fwd_deal_wgs;
+  const int32_t* fwd_deal_start;
+  const int32_t* fwd_deal_items;
+  int32_t n_fwd_deal_items;
+  int32_t split_deal_wgs;
+  const int32_t* split_deal_start;
+  const int32_t* split_deal_items;
+  int32_t n_split_deal_items;
 } cva_plan_tables;
 
 cva_status cva_plan_get_tables(const cva_plan* plan, cva_plan_tables* out);

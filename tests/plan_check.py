@@ -6,8 +6,8 @@ the zero-fill ranges, the split slots and merge records -- and asserts that
 every index a kernel dereferences through them lies inside the buffer it
 addresses (the tile records' segment ids, every row a tile covers, every
 prefix-index entry a K/V tile loads (rank-major row < T), the rows of each
-zero-fill range, every partial slot), and that the forward and dQ tiles
-partition every segment's rows.  It reads the tables through the C ABI
+zero-fill range, every partial slot, every streamed-forward item list), and
+that the forward and dQ tiles partition every segment's rows.  It reads the tables through the C ABI
 (cva_plan_get_tables / cva_plan_get_schedule) and shares no code with the
 library that builds them.
 """
@@ -16,6 +16,7 @@ import numpy as np
 # per-item span capacities of the kernels (forward, dQ, dK/dV, split forward)
 MAX_SPANS = {0: 8, 1: 8, 2: 16, 3: 8}
 ZERO_ROWS_PER_BLOCK = 8
+STREAM_MAX_ITEMS = 48
 
 
 def _req(cond, msg):
@@ -105,6 +106,18 @@ def check_plan_tables(plan, n_seqs, T, T_loc):
         covered[kvi] = True
         for a, b in zr:
             _req(not covered[a:b].any(), "zero rows: a range overlaps rows the backward writes")
+
+    # streamed forward deals: every item of the schedule dealt exactly once, at
+    # most STREAM_MAX_ITEMS per work-group (the kernel's LDS table)
+    for key, which in (("fwd_deal", 0), ("split_deal", 3)):
+        wgs, start, items = t[key]
+        n_items = len(plan.schedule(which)[2])
+        if wgs == 0:
+            continue
+        _req(len(start) == wgs + 1 and start[0] == 0 and start[-1] == len(items), f"{key}: start table")
+        sizes = np.diff(start)
+        _req(((sizes >= 1) & (sizes <= STREAM_MAX_ITEMS)).all(), f"{key}: items per work-group")
+        _req(np.array_equal(np.sort(items), np.arange(n_items)), f"{key}: every item exactly once")
 
     n_slots, comb = t["n_split_slots"], t["split_combine"]
     _req(((slots >= -1) & (slots < n_slots)).all(), "split: slot out of range")

@@ -99,6 +99,27 @@ def test_small_cases_split(ci, dtype):
     _run(w, q, k, v, split=True)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("ci", range(len(SMALL)))
+def test_small_cases_streamed(ci, dtype, monkeypatch):
+    """The streamed forward (one work-group per CU walking its items as one tile
+    stream) forced on for every head dim, plain and with split K/V ranges where
+    the case cuts: several items per work-group, item boundaries mid-stream."""
+    monkeypatch.setenv("CVA_FWD_STREAM", "1")
+    monkeypatch.setenv("CVA_FWD_STREAM_WGS", "3")  # several items per work-group
+    lens, R, r, hq, hkv, dqk, dv, mask, ex = SMALL[ci]
+    w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, dtype, mask=mask,
+                              sink=ex.get("sink", 0), window=ex.get("window", 0),
+                              branch_bounds=ex.get("bounds"), name=f"small{ci}",
+                              block=ex.get("block", 0))
+    q, k, v = synth.random_tensors(w, 100 + ci, with_dout=False)
+    plan = _run(w, q, k, v)
+    if ci in SPLIT:
+        _run(w, q, k, v, split=True)
+    wgs, start, _ = plan.tables()["fwd_deal"]
+    assert wgs > 0 and np.diff(start).max() >= 2, "no work-group walks several items"
+
+
 def test_gqa16k_split_all_rows(monkeypatch):
     """cva_fwd_split with every Q tile longer than 24 K/V tiles cut (the default
     leaves this batch whole: its longest tile walks 1.25x the per-CU average)."""

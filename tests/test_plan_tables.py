@@ -40,8 +40,11 @@ def test_every_rank_in_bounds():
         check_plan_tables(plan_for(w), len(w.lengths), w.total_tokens, w.total_tokens // w.cp_size)
 
 
+@pytest.mark.parametrize("cap", [None, "2"])
 @pytest.mark.parametrize("mask", ["causal", "lambda", "blockwise", "shared_prefix"])
-def test_random_small_batches_in_bounds(mask):
+def test_random_small_batches_in_bounds(mask, cap, monkeypatch):
+    if cap is not None:  # streamed-forward deals of several items per work-group
+        monkeypatch.setenv("CVA_FWD_STREAM_WGS", cap)
     rng = random.Random(11)
     for _ in range(12):
         R = rng.choice([1, 2, 3, 4])
