@@ -1137,9 +1137,18 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     }
     st.l += lt;
   };
+  // Boundary work runs once per item; its inputs pass through an empty asm
+  // statement so that the compiler does not hoist it (its LDS reads with their
+  // wait for every LDS operation, the division and the log) into every tile.
+  auto opaque = [](int x) {
+    asm volatile("" : "+s"(x));
+    return x;
+  };
   // normalise and write item i's rows (O and LSE, or its fp32 partial)
   auto epilogue = [&](int i) {
-    const float l_tot = wave_half_sum(st.l);
+    float l_sum = st.l;
+    asm volatile("" : "+v"(l_sum));
+    const float l_tot = wave_half_sum(l_sum);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (!valid) return;
     const int q0 = item_q0(i), a = lane_a(i), slot = sItem[i][IT_SLOT];
@@ -1178,7 +1187,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   // the loads so that no load is pending where the paths join: the compiler
   // would otherwise wait for every load before each later use of Q.)
   auto next_item_rows = [&]() {
-    load_rows(nxt, niv);
+    load_rows(opaque(nxt), niv);
     wait_vmem_all();
     scale_q();
   };
@@ -1192,8 +1201,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   };
   // The first vector step of item nxt: cur's epilogue, then the switch.
   auto start_next_item = [&]() {
-    epilogue(cur);
-    cur = nxt;
+    epilogue(opaque(cur));
+    cur = opaque(nxt);
     valid = lane_valid(cur);
     lo1 = niv.x; hi1 = niv.y; lo2 = niv.z; hi2 = niv.w;
     st.base = 0.f;
@@ -1205,7 +1214,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
 
   // stream positions of the item boundaries: the first tile of the item after cur
   auto first_after = [&](int i) {
-    const StreamCursor c = stream_item_start(sItem, sSpans, i + 1, n_items);
+    const StreamCursor c = stream_item_start(sItem, sSpans, opaque(i) + 1, n_items);
     return c.item < n_items ? __builtin_amdgcn_readfirstlane(sItem[c.item][IT_FIRST]) : n_tiles;
   };
   int boundary = first_after(cur);  // stream index of item nxt's first tile (n_tiles: none)
