@@ -335,7 +335,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU's share on a single MI355X; --gpus {args.gpus} "
-              f"(WORLD_SIZE={world}) is not supported: this build has no multi-GPU path",
+              f"(WORLD_SIZE={world}) is not supported: cva has no multi-GPU path",
               file=sys.stderr)
         return 2
 

@@ -58,7 +58,7 @@ typedef enum {
   CVA_E_HEADDIM = 6,      /* head dims not supported (Dqk < Dv, or no kernel)    */
   CVA_E_DTYPE = 7,        /* unknown dtype                                        */
   CVA_E_MASK = 8,         /* bad mask descriptor                                  */
-  CVA_E_UNSUPPORTED = 9,  /* valid request that this build does not implement     */
+  CVA_E_UNSUPPORTED = 9,  /* valid request that the library does not implement     */
   CVA_E_WORKLOAD = 10,    /* per-rank sum(q_len*kv_len) not equal (never for valid input) */
   CVA_E_HIP = 11,         /* a HIP runtime call failed                            */
   CVA_E_SCALE = 12,       /* softmax_scale not finite or not > 0                  */

@@ -8,7 +8,7 @@ accumulates in fp32 so its error is far below that).
 
 Every comparison also records its headroom, max(|err| / (atol + rtol*|ref|)),
 one JSON line per (test, output) in ``$CVA_HEADROOM_FILE`` (default
-``gpurun_out/parity_headroom.jsonl`` under the repository root): 1.0 would be
+``test_output/parity_headroom.jsonl`` under the repository root): 1.0 would be
 the tolerance itself.
 """
 import functools
@@ -25,7 +25,7 @@ import synth
 TOL = {"bf16": 2.5e-2, "fp16": 5e-3, "fp32": 1e-4}
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADROOM_FILE = os.environ.get("CVA_HEADROOM_FILE",
-                               os.path.join(ROOT, "gpurun_out", "parity_headroom.jsonl"))
+                               os.path.join(ROOT, "test_output", "parity_headroom.jsonl"))
 ORACLE_THREADS = 4  # oracle heads computed side by side (numpy releases the GIL)
 
 
