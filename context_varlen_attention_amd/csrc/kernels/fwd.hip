@@ -29,9 +29,10 @@
 //     the base moved only when some P of the tile may exceed 2^8 (the sum of a
 //     lane's P values exceeds 2^8) or the row has no base yet (lazy rescaling),
 //     so both the maximum and the O rescale are rare;
-//   * P is packed to 16 bits with v_cvt_pk and the row sum is accumulated from
-//     the packed values with v_dot2 (the sum of exactly the values the PV MFMA
-//     consumes);
+//   * P is packed to 16 bits with v_cvt_pk; the row sum is accumulated in fp32
+//     with plain adds of the values before packing (v_dot2 on the packed values
+//     would sum exactly what the PV MFMA consumes, but it issues many times
+//     slower while the other wave of the SIMD runs MFMAs);
 //   * masking is a separate code path taken only on partial tiles.
 // K/V rows are gathered through the prefix index straight into LDS with
 // global_load_lds_dwordx4 (the index_select of the RFC, never materialised),
@@ -226,23 +227,6 @@ __device__ __forceinline__ float wave_half_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
-template <typename E>
-__device__ __forceinline__ float dot2_acc(uint32_t packed, float acc);
-
-template <>
-__device__ __forceinline__ float dot2_acc<Bf16>(uint32_t packed, float acc) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed), one, acc, false);
-}
-
-template <>
-__device__ __forceinline__ float dot2_acc<Fp16>(uint32_t packed, float acc) {
-  typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-  const f16x2_t one = {(_Float16)1.0f, (_Float16)1.0f};
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed), one, acc, false);
-}
-
 // Per-lane state of the online softmax: exponent base (log2 units, shared by the
 // two half-waves holding the same query), running sum and the O^T accumulators.
 template <int DB>
@@ -300,33 +284,31 @@ __device__ __forceinline__ float tile_max(const f32x16_t (&s)[2]) {
   return wave_half_max(mx);
 }
 
-// P = exp2(S^T), packed to 16 bits, row sums from the packed values, and
-// O^T += V^T P^T over the tile's 64 keys (4 reduction steps of 16).
-template <typename E, int DV>
-__device__ __forceinline__ void tile_pv(SoftmaxState<DV / 32>& st, const f32x16_t (&s)[2],
-                                        const uint16_t* sv, const uint32_t (&voff)[DV / 32]) {
-  constexpr int DB = DV / 32;
+// P = exp2(S^T) for the 32 scores a lane holds, packed to 16 bits as the PV
+// MFMA's operand; returns the lane's share of the row sum in fp32.  Normally
+// the sum is taken from the values before packing, in four partial sums (so the
+// adds do not form one dependent chain); kFromPacked sums the packed values
+// instead, unpacked again with integer operations, which needs no register
+// beyond the packed P (for the kernel forms that are short of registers).
+template <typename E, bool kFromPacked>
+__device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16_t (&s)[2]) {
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4_t pv;
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 8 * ks + 2 * j;
-        pv[j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
-        st.l = dot2_acc<E>(pv[j], st.l);
+        const float p0 = __builtin_amdgcn_exp2f(s[nb][r]), p1 = __builtin_amdgcn_exp2f(s[nb][r + 1]);
+        const uint32_t w = pack2<E>(p0, p1);
+        pk[nb][ks][j] = w;
+        if constexpr (kFromPacked)
+          part[0] += E::to_float((uint16_t)(w & 0xFFFFu)) + E::to_float((uint16_t)(w >> 16));
+        else
+          part[j] += p0 + p1;
       }
-      const typename E::vec8 bfrag = as_vec8<E>(pv);
-      const int key0 = nb * 32 + ks * 16;
-#pragma unroll
-      for (int d = 0; d < DB; ++d) {
-        const u32x2_t lo = lds_read_tr(sv + key0 * DV, voff[d]);
-        const u32x2_t hi = lds_read_tr(sv + (key0 + 8) * DV, voff[d]);
-        st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), bfrag, st.acc[d]);
-      }
-    }
-  }
+  return kFromPacked ? part[0] : (part[0] + part[1]) + (part[2] + part[3]);
 }
 
 // Forward work-group: 8 waves in two groups of 4 (group g = wave / 4; waves w and
@@ -355,6 +337,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   constexpr int NS = kStages<DQK>;
   constexpr int NIR = 2 * NS;       // index ring slots
   constexpr uint32_t KBUF = kBN * DQK * 2, VBUF = kBN * DV * 2;  // bytes per tile buffer
+  // Dqk == Dv: each group streams one operand, its loads spread over its own
+  // MFMA steps (group 0 K and the index ring, group 1 V); otherwise group 0
+  // streams both in bursts
+  constexpr bool kSpread = DQK == DV;
   __shared__ __attribute__((aligned(16))) uint16_t sK[NS][kBN * DQK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NS][kBN * DV];
   __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][kBN];
@@ -461,6 +447,37 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     wait_vmem_le(allowed);
   };
 
+  // ---- tile streaming by operand (kSpread) ----
+  // Step n's own batch of a wave: group 0 K(n+NS), group 1 V(n+NS-1).  Batches
+  // past the last tile are still issued (same rows as the wave's last real
+  // batch, into a ring slot nobody reads any more), so that every step issues
+  // the same number of loads and every wait count is a constant.
+  int own_idx[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) own_idx[i] = 0;  // a valid row until the first batch's rows are read
+  const char* own_g = grp == 0 ? kg : vg;
+  const uint32_t own_stride = grp == 0 ? kstride : vstride;
+  const uint32_t own_ring = grp == 0 ? lds_addr(sK) : lds_addr(sV);
+  auto own_tile = [&](int n) { return grp == 0 ? n + NS : n + NS - 1; };
+  auto read_own = [&](int n) {  // rows of step n's own batch, from the index ring
+    const int m = own_tile(n);
+    if (m >= 0 && m < n_tiles) TL::read_index(own_idx, sIdx[m % NIR], ltid);
+  };
+  auto issue_own = [&](int n, int l) {  // load l of step n's own batch
+    const int m = own_tile(n);
+    const uint32_t chunk = grp == 0 ? TL::kchunk(l, ltid) : TL::vchunk(l, ltid);
+    dma16(own_g + ((uint64_t)(uint32_t)own_idx[l] * own_stride + chunk),
+          own_ring + (uint32_t)(m % NS) * KBUF + (uint32_t)(w4 * 64 + l * TL::kThreads) * 16);
+  };
+  static_assert(!kSpread || (TL::kShared && KBUF == VBUF), "operand streams need equal K and V tiles");
+  static_assert(!kSpread || NS == 4, "the operand streams' wait counts assume a 4-deep ring");
+  // group 0, after the own batch of step n >= 0: the indices of tile n + 2NS
+  // (a harmless re-fetch of the last prefix entry past the last tile)
+  auto fetch_idx_step = [&]() {
+    if (next_idx < n_tiles) fetch_idx();
+    else dma4(kvi + (kv_len - 1), lds_addr(sIdx[next_idx++ % NIR]));
+  };
+
   // group 0: indices of tiles 0 .. 2NS-1 first, so that they load together with Q
   if (grp == 0)
     for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
@@ -486,7 +503,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
   }
   wait_vmem_all();  // indices, Q and row intervals, before any tile load is in flight
-  if (grp == 0) {
+  if constexpr (kSpread) {
+    __syncthreads();  // the first tiles' indices are in LDS for both groups
+    // own batches of steps -NS .. -2: K(0 .. NS-2), V(0 .. NS-3)
+    for (int n = grp == 0 ? -NS : -NS + 1; n <= -2; ++n) {
+      read_own(n);
+#pragma unroll
+      for (int l = 0; l < NI; ++l) issue_own(n, l);
+    }
+    if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(0)
+    read_own(-1);
+  } else if (grp == 0) {
     // batches -NS .. -2
     for (int n = -NS; n <= -2; ++n) {
       prepare_batch(n);
@@ -569,6 +596,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{vl[i % AH][0], vl[i % AH][1], vh[i % AH][0], vh[i % AH][1]}),
                             as_vec8<E>(pk[pnbks >> 1][pnbks & 1]), st.acc[d]);
       if (i + AH < NP) readv(i + AH, vl[i % AH], vh[i % AH]);
+      if constexpr (kSpread) {  // own load l after pair 2 + l * NP / NI
+        if (i >= 2 && (i - 2) % (NP / NI) == 0) issue_own(n, (i - 2) / (NP / NI));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -582,19 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   };
   // P = exp2(S - base) straight away; the row maximum is only computed (and the
   // base moved) when some P exceeds 2^threshold, or on a valid row's first tile.
-  auto exp_pack = [&](float& lt) {
-    lt = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 8 * ks + 2 * j;
-          pk[nb][ks][j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
-          lt = dot2_acc<E>(pk[nb][ks][j], lt);
-        }
-  };
+  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128)>(pk, s); };
   auto softmax = [&](const TileCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
     float lt;
@@ -634,26 +652,42 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   if (grp == 1) __syncthreads();         // group 1 runs one phase behind
 
   // X(-1) = S(0); Y(0)
-  if (grp == 0) issue_batch(-1);
+  if constexpr (kSpread) {
+#pragma unroll
+    for (int l = 0; l < NI; ++l) issue_own(-1, l);
+  } else if (grp == 0) {
+    issue_batch(-1);
+  }
   init_scores();
   scores(0);
+  if (kSpread && grp == 1) wait_vmem_le((NS - 2) * NI);  // V(0)
   __syncthreads();
   softmax(cY);
   cY = next_tile(cY, sSpan, nspan);
   init_scores();
-  if (grp == 0) {
+  if constexpr (kSpread) {
+    if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(1)
+    read_own(0);
+  } else if (grp == 0) {
     wait_batch(-1);
     prepare_batch(0);
   }
   __syncthreads();
   // X(n) = PV(n) + S(n+1); Y(n+1)
   for (int n = 0; n + 1 < n_tiles; ++n) {
-    if (grp == 0) {
+    if (!kSpread && grp == 0) {
       if constexpr (kSplitIssue) issue_k_part(n);
       else issue_batch(n);
     }
     if constexpr (DQK == DV) {
+      // the MFMA step goes first on its SIMD: the partner wave's vector step is
+      // shorter and fits into the MFMAs' shadow, while an MFMA issue that waits
+      // behind vector instructions stretches the whole phase
+      __builtin_amdgcn_s_setprio(1);
       x_step_interleaved(n);
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 0) fetch_idx_step();
+      else wait_vmem_le((NS - 2) * NI);  // V(n+1): V(n+2) and V(n+3) may still be in flight
     } else {
     pv(n);
     scores(n + 1);
@@ -680,7 +714,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     softmax(cY);
     cY = next_tile(cY, sSpan, nspan);
     init_scores();
-    if (grp == 0) {
+    if constexpr (kSpread) {
+      // K(n+2): the batches of steps n-1 and n may still be in flight (one
+      // fewer load in step -1's, which fetched no indices)
+      if (grp == 0) {
+        if (n == 0) wait_vmem_le(2 * NI + 1);
+        else wait_vmem_le(2 * NI + 2);
+      }
+      read_own(n + 1);
+    } else if (grp == 0) {
       if constexpr (kSplitIssue) issue_v_part(n);
       wait_batch(n);
       prepare_batch(n + 1);
@@ -1096,19 +1138,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
         for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
     }
   };
-  auto exp_pack = [&](float& lt) {
-    lt = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 8 * ks + 2 * j;
-          pk[nb][ks][j] = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
-          lt = dot2_acc<E>(pk[nb][ks][j], lt);
-        }
-  };
+  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128)>(pk, s); };
   bool valid = lane_valid(cur);
   auto softmax = [&](const StreamCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
