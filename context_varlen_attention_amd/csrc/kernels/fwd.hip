@@ -565,16 +565,27 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   // and the PV MFMAs of tile n alternate, every LDS operand read issued AH MFMA
   // pairs ahead of its use and the order pinned pair by pair, so that the reads
   // are spread over the step and none is waited for right after its issue
-  auto x_step_interleaved = [&](int n) {
+  // K operand read i of X(n) (the scores of tile n+1)
+  auto read_k_op = [&](int n, int i) {
     constexpr int KO = kKoff<DQK>;
+    const uint16_t* skk = (const uint16_t*)((const char*)sK + ((n + 1) % NS) * KBUF);
+    const int kt = i >> 1, nb = i & 1;
+    return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
+  };
+  // The first K operand reads of the next MFMA step, issued at the end of the
+  // vector step before it (the tile is in LDS by then: group 0 has just waited
+  // for its own load, group 1's copy was published a phase earlier), so that
+  // the MFMA step does not start with a full LDS latency after its barrier.
+  u32x4_t kpre[kXReadAhead];
+  auto prefetch_k = [&](int n) {
+#pragma unroll
+    for (int j = 0; j < kXReadAhead; ++j) kpre[j] = read_k_op(n, j);
+  };
+  auto x_step_interleaved = [&](int n) {
     constexpr int NP = 2 * KSTEPS;  // == 4 * DB
     constexpr int AH = kXReadAhead;
     const uint16_t* sv = (const uint16_t*)((const char*)sV + (n % NS) * VBUF);
-    const uint16_t* skk = (const uint16_t*)((const char*)sK + ((n + 1) % NS) * KBUF);
-    auto readk = [&](int i) {
-      const int kt = i >> 1, nb = i & 1;
-      return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
-    };
+    auto readk = [&](int i) { return read_k_op(n, i); };
     auto readv = [&](int i, u32x2_t& lo, u32x2_t& hi) {  // PV operand i: (nb, ks, d) = (i / 2DB, i / DB % 2, i % DB)
       const int key0 = (i / (2 * DB)) * 32 + ((i / DB) & 1) * 16, d = i % DB;
       lo = lds_read_tr(sv + key0 * DV, voff[d]);
@@ -584,7 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     u32x2_t vl[AH], vh[AH];
 #pragma unroll
     for (int j = 0; j < AH; ++j) {
-      kr[j] = readk(j);
+      kr[j] = kpre[j];
       readv(j, vl[j], vh[j]);
     }
 #pragma unroll
@@ -668,6 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   if constexpr (kSpread) {
     if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(1)
     read_own(0);
+    if (n_tiles > 1) prefetch_k(0);
   } else if (grp == 0) {
     wait_batch(-1);
     prepare_batch(0);
@@ -722,6 +734,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         else wait_vmem_le(2 * NI + 2);
       }
       read_own(n + 1);
+      if (n + 2 < n_tiles) prefetch_k(n + 1);
     } else if (grp == 0) {
       if constexpr (kSplitIssue) issue_v_part(n);
       wait_batch(n);
