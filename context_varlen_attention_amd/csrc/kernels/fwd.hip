@@ -320,11 +320,14 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 // sums).  A barrier ends every phase, so on every SIMD one wave is in an MFMA
 // step while the other is in a vector step.
 //
-// Group 0 also streams the tiles through an NS-deep LDS ring: at the start of
-// X(n) it issues K(n+NS) and V(n+NS-1) into the slots K(n) and V(n-1) used, plus
-// the prefix indices of tile n+2NS into a small index ring, and at the end of
-// Y(n+1) waits only for the batch holding K(n+2) and V(n+1): NS-2 batches stay
-// in flight across every barrier.
+// The tiles stream through an NS-deep LDS ring, K(n+NS) into the slot K(n)
+// used and V(n+NS-1) into the slot of V(n-1), with the prefix indices of tile
+// n+2NS fetched into a small index ring; NS-2 batches stay in flight across
+// every barrier.  When Dqk == Dv each group streams one operand inside its own
+// MFMA steps (group 0 K and the indices, group 1 V, one load after every
+// fourth MFMA pair of X(n)); group 0 waits for K(n+2) at the end of Y(n+1),
+// group 1 for V(n+1) at the end of X(n).  Otherwise group 0 streams both: K
+// and the indices at the start of X(n), V after Y(n+1), then its wait.
 template <int DQK>
 constexpr int kStages = DQK > 128 ? 3 : 4;
 
@@ -655,9 +658,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     st.l += lt;
   };
 
-  // Group 0 streams the tiles: it issues batch n at the start of its MFMA step
-  // X(n) (phase 2n+2), and at the end of its vector step Y(n+1) waits for batch
-  // n+2-NS and reads the indices of batch n+1.
+  // Phases: group 0 runs X(n) in phase 2n+2 and Y(n+1) in phase 2n+3, group 1
+  // one phase later.
   TileCursor cY = span_start(sSpan, 0);  // tile whose Y step comes next
   __syncthreads();                       // K(0) is in LDS
   if (grp == 1) __syncthreads();         // group 1 runs one phase behind
