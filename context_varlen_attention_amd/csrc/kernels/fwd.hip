@@ -864,6 +864,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   constexpr int NS = kStages<DQK>;
   constexpr int NIR = 2 * NS;
   constexpr uint32_t KBUF = kBN * DQK * 2, VBUF = kBN * DV * 2;
+  constexpr bool kSpread = DQK == DV;  // operand streams, as in fwd_mfma_kernel
   __shared__ __attribute__((aligned(16))) uint16_t sK[NS][kBN * DQK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[NS][kBN * DV];
   __shared__ __attribute__((aligned(16))) int32_t sIdx[NIR][kBN];
@@ -996,6 +997,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     for (int b = 0; b < NS - 2; ++b) allowed += bcount[(n - b + NS) % NS];
     wait_vmem_le(allowed);
   };
+  // Operand streams (kSpread): as in fwd_mfma_kernel, over the stream's tiles.
+  int own_idx[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) own_idx[i] = 0;
+  const char* own_g = grp == 0 ? kg : vg;
+  const uint32_t own_stride = grp == 0 ? kstride : vstride;
+  const uint32_t own_ring = grp == 0 ? lds_addr(sK) : lds_addr(sV);
+  auto own_tile = [&](int n) { return grp == 0 ? n + NS : n + NS - 1; };
+  auto read_own = [&](int n) {
+    const int m = own_tile(n);
+    if (m >= 0 && m < n_tiles) TL::read_index(own_idx, sIdx[m % NIR], ltid);
+  };
+  auto issue_own = [&](int n, int l) {
+    const int m = own_tile(n);
+    const uint32_t chunk = grp == 0 ? TL::kchunk(l, ltid) : TL::vchunk(l, ltid);
+    dma16(own_g + ((uint64_t)(uint32_t)own_idx[l] * own_stride + chunk),
+          own_ring + (uint32_t)(m % NS) * KBUF + (uint32_t)(w4 * 64 + l * TL::kThreads) * 16);
+  };
+  static_assert(!kSpread || (TL::kShared && KBUF == VBUF), "operand streams need equal K and V tiles");
+  static_assert(!kSpread || NS == 4, "the operand streams' wait counts assume a 4-deep ring");
+  auto fetch_idx_step = [&]() {  // past the stream's last tile: a harmless re-fetch of entry 0
+    if (next_idx < n_tiles) fetch_idx();
+    else dma4(P.t.kv_index, lds_addr(sIdx[next_idx++ % NIR]));
+  };
 
   // ---- per-item row state of this lane ----
   // cur: the item whose softmax / PV is running; nxt: the next item (its Q and
@@ -1049,7 +1074,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   wait_vmem_all();
   scale_q();
   lo1 = niv.x; hi1 = niv.y; lo2 = niv.z; hi2 = niv.w;
-  if (grp == 0) {
+  if constexpr (kSpread) {
+    __syncthreads();  // the first tiles' indices are in LDS for both groups
+    for (int n = grp == 0 ? -NS : -NS + 1; n <= -2; ++n) {
+      read_own(n);
+#pragma unroll
+      for (int l = 0; l < NI; ++l) issue_own(n, l);
+    }
+    if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(0)
+    read_own(-1);
+  } else if (grp == 0) {
     for (int n = -NS; n <= -2; ++n) {
       prepare_batch(n);
       issue_batch(n);
@@ -1093,16 +1127,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   auto scores = [&](int n) {
     tile_scores<E, DQK, kFromBase>(s, qf, (const uint16_t*)((const char*)sK + (n % NS) * KBUF), koff, nbase);
   };
-  auto x_step_interleaved = [&](int n) {
+  auto read_k_op = [&](int n, int i) {
     constexpr int KO = kKoff<DQK>;
+    const uint16_t* skk = (const uint16_t*)((const char*)sK + ((n + 1) % NS) * KBUF);
+    const int kt = i >> 1, nb = i & 1;
+    return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
+  };
+  u32x4_t kpre[kXReadAhead];  // (kSpread) first K operand reads, issued before the barrier
+  auto prefetch_k = [&](int n) {
+#pragma unroll
+    for (int j = 0; j < kXReadAhead; ++j) kpre[j] = read_k_op(n, j);
+  };
+  auto x_step_interleaved = [&](int n) {
     constexpr int NP = 2 * KSTEPS;
     constexpr int AH = kXReadAhead;
     const uint16_t* sv = (const uint16_t*)((const char*)sV + (n % NS) * VBUF);
-    const uint16_t* skk = (const uint16_t*)((const char*)sK + ((n + 1) % NS) * KBUF);
-    auto readk = [&](int i) {
-      const int kt = i >> 1, nb = i & 1;
-      return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
-    };
+    auto readk = [&](int i) { return read_k_op(n, i); };
     auto readv = [&](int i, u32x2_t& lo, u32x2_t& hi) {
       const int key0 = (i / (2 * DB)) * 32 + ((i / DB) & 1) * 16, d = i % DB;
       lo = lds_read_tr(sv + key0 * DV, voff[d]);
@@ -1112,7 +1152,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     u32x2_t vl[AH], vh[AH];
 #pragma unroll
     for (int j = 0; j < AH; ++j) {
-      kr[j] = readk(j);
+      kr[j] = kSpread ? kpre[j] : readk(j);
       readv(j, vl[j], vh[j]);
     }
 #pragma unroll
@@ -1124,6 +1164,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
       st.acc[d] = E::mfma32(as_vec8<E>(u32x4_t{vl[i % AH][0], vl[i % AH][1], vh[i % AH][0], vh[i % AH][1]}),
                             as_vec8<E>(pk[pnbks >> 1][pnbks & 1]), st.acc[d]);
       if (i + AH < NP) readv(i + AH, vl[i % AH], vh[i % AH]);
+      if constexpr (kSpread) {
+        if (i >= 2 && (i - 2) % (NP / NI) == 0) issue_own(n, (i - 2) / (NP / NI));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1269,9 +1312,15 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   if (grp == 1) __syncthreads();  // group 1 runs one phase behind
 
   // X(-1) = S(0); Y(0)
-  if (grp == 0) issue_batch(-1);
+  if constexpr (kSpread) {
+#pragma unroll
+    for (int l = 0; l < NI; ++l) issue_own(-1, l);
+  } else if (grp == 0) {
+    issue_batch(-1);
+  }
   init_scores();
   scores(0);
+  if (kSpread && grp == 1) wait_vmem_le((NS - 2) * NI);  // V(0)
   __syncthreads();
   {
     const bool last = boundary == 1 && nxt < n_items;  // item 0 has one tile
@@ -1281,19 +1330,30 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     else init_scores();
   }
   cY = stream_next(cY, sItem, sSpans, n_items);
-  if (grp == 0) {
+  if constexpr (kSpread) {
+    if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(1)
+    read_own(0);
+    if (n_tiles > 1) prefetch_k(0);
+  } else if (grp == 0) {
     wait_batch(-1);
     prepare_batch(0);
   }
   __syncthreads();
   for (int n = 0; n + 1 < n_tiles; ++n) {
     // X(n) = PV(n) + S(n+1) (S(n+1) is item nxt's first when n + 1 == boundary)
-    if (grp == 0) {
+    if (!kSpread && grp == 0) {
       if constexpr (kSplitIssue) issue_k_part(n);
       else issue_batch(n);
     }
-    if constexpr (DQK == DV) x_step_interleaved(n);
-    else x_step_grouped(n);
+    if constexpr (DQK == DV) {
+      __builtin_amdgcn_s_setprio(1);
+      x_step_interleaved(n);
+      __builtin_amdgcn_s_setprio(0);
+      if (grp == 0) fetch_idx_step();
+      else wait_vmem_le((NS - 2) * NI);  // V(n+1)
+    } else {
+      x_step_grouped(n);
+    }
     __syncthreads();
     // Y(n+1)
     if (n + 1 == boundary) {
@@ -1306,7 +1366,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     if (last) next_item_seed();
     else init_scores();
     cY = stream_next(cY, sItem, sSpans, n_items);
-    if (grp == 0) {
+    if constexpr (kSpread) {
+      if (grp == 0) {  // K(n+2)
+        if (n == 0) wait_vmem_le(2 * NI + 1);
+        else wait_vmem_le(2 * NI + 2);
+      }
+      read_own(n + 1);
+      if (n + 2 < n_tiles) prefetch_k(n + 1);
+    } else if (grp == 0) {
       if constexpr (kSplitIssue) issue_v_part(n);
       wait_batch(n);
       prepare_batch(n + 1);
