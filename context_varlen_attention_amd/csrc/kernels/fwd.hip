@@ -324,9 +324,9 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 // used and V(n+NS-1) into the slot of V(n-1), with the prefix indices of tile
 // n+2NS fetched into a small index ring; NS-2 batches stay in flight across
 // every barrier.  When Dqk == Dv each group streams one operand inside its own
-// MFMA steps (group 0 K and the indices, group 1 V, one load after every
-// fourth MFMA pair of X(n)); group 0 waits for K(n+2) at the end of Y(n+1),
-// group 1 for V(n+1) at the end of X(n).  Otherwise group 0 streams both: K
+// MFMA steps (group 0 K, group 1 V, one load after every fourth MFMA pair of
+// X(n)); group 0 fetches the indices and waits for K(n+2) at the end of
+// Y(n+1), group 1 waits for V(n+1) at the end of X(n).  Otherwise group 0 streams both: K
 // and the indices at the start of X(n), V after Y(n+1), then its wait.
 template <int DQK>
 constexpr int kStages = DQK > 128 ? 3 : 4;
@@ -700,8 +700,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       __builtin_amdgcn_s_setprio(1);
       x_step_interleaved(n);
       __builtin_amdgcn_s_setprio(0);
-      if (grp == 0) fetch_idx_step();
-      else wait_vmem_le((NS - 2) * NI);  // V(n+1): V(n+2) and V(n+3) may still be in flight
+      if (grp == 1) wait_vmem_le((NS - 2) * NI);  // V(n+1): V(n+2) and V(n+3) may still be in flight
     } else {
     pv(n);
     scores(n + 1);
@@ -732,6 +731,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       // K(n+2): the batches of steps n-1 and n may still be in flight (one
       // fewer load in step -1's, which fetched no indices)
       if (grp == 0) {
+        // the indices of tile n+8 (here, where the vector step has slack, not
+        // after the MFMA step, whose end sets the phase), then K(n+2)
+        fetch_idx_step();
         if (n == 0) wait_vmem_le(2 * NI + 1);
         else wait_vmem_le(2 * NI + 2);
       }
@@ -1287,9 +1289,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
       for (int nb = 0; nb < 2; ++nb) s[nb] = zero16();
     }
   };
-  // The first vector step of item nxt: cur's epilogue, then the switch.
+  // The first vector step of item nxt: cur's epilogue, then the switch.  The
+  // epilogue's global stores share the vector-memory counter with the tile
+  // loads but may retire ahead of loads issued before them, so a counted wait
+  // for a tile load is only sound with no store in flight: they are drained
+  // here (with the loads in flight, once per item).
   auto start_next_item = [&]() {
     epilogue(opaque(cur));
+    wait_vmem_all();
     cur = opaque(nxt);
     valid = lane_valid(cur);
     lo1 = niv.x; hi1 = niv.y; lo2 = niv.z; hi2 = niv.w;
@@ -1349,8 +1356,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
       __builtin_amdgcn_s_setprio(1);
       x_step_interleaved(n);
       __builtin_amdgcn_s_setprio(0);
-      if (grp == 0) fetch_idx_step();
-      else wait_vmem_le((NS - 2) * NI);  // V(n+1)
+      if (grp == 1) wait_vmem_le((NS - 2) * NI);  // V(n+1)
     } else {
       x_step_grouped(n);
     }
@@ -1367,7 +1373,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     else init_scores();
     cY = stream_next(cY, sItem, sSpans, n_items);
     if constexpr (kSpread) {
-      if (grp == 0) {  // K(n+2)
+      if (grp == 0) {  // the indices of tile n+8, then K(n+2)
+        fetch_idx_step();
         if (n == 0) wait_vmem_le(2 * NI + 1);
         else wait_vmem_le(2 * NI + 2);
       }

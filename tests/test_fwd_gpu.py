@@ -99,14 +99,17 @@ def test_small_cases_split(ci, dtype):
     _run(w, q, k, v, split=True)
 
 
+@pytest.mark.parametrize("wgs", ["3", "1"])
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("ci", range(len(SMALL)))
-def test_small_cases_streamed(ci, dtype, monkeypatch):
+def test_small_cases_streamed(ci, dtype, wgs, monkeypatch):
     """The streamed forward (one work-group per CU walking its items as one tile
     stream) forced on for every head dim, plain and with split K/V ranges where
-    the case cuts: several items per work-group, item boundaries mid-stream."""
+    the case cuts: several items per work-group, item boundaries mid-stream.
+    With one work-group per head group every item of the case is a boundary of
+    one stream (item epilogues' stores then meet the most tile loads in flight)."""
     monkeypatch.setenv("CVA_FWD_STREAM", "1")
-    monkeypatch.setenv("CVA_FWD_STREAM_WGS", "3")  # several items per work-group
+    monkeypatch.setenv("CVA_FWD_STREAM_WGS", wgs)  # several items per work-group
     lens, R, r, hq, hkv, dqk, dv, mask, ex = SMALL[ci]
     w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, dtype, mask=mask,
                               sink=ex.get("sink", 0), window=ex.get("window", 0),
