@@ -29,10 +29,11 @@
 //     the base moved only when some P of the tile may exceed 2^8 (the sum of a
 //     lane's P values exceeds 2^8) or the row has no base yet (lazy rescaling),
 //     so both the maximum and the O rescale are rare;
-//   * P is packed to 16 bits with v_cvt_pk; the row sum is accumulated in fp32
-//     with plain adds of the values before packing (v_dot2 on the packed values
-//     would sum exactly what the PV MFMA consumes, but it issues many times
-//     slower while the other wave of the SIMD runs MFMAs);
+//   * P is packed to 16 bits with v_cvt_pk and the row sum is accumulated from
+//     the packed values (the sum of exactly the values the PV MFMA consumes),
+//     unpacked with integer operations and added in fp32 (v_dot2 would do
+//     the same in one instruction, but it issues many times slower while the
+//     other wave of the SIMD runs MFMAs);
 //   * masking is a separate code path taken only on partial tiles.
 // K/V rows are gathered through the prefix index straight into LDS with
 // global_load_lds_dwordx4 (the index_select of the RFC, never materialised),
@@ -285,14 +286,15 @@ __device__ __forceinline__ float tile_max(const f32x16_t (&s)[2]) {
 }
 
 // P = exp2(S^T) for the 32 scores a lane holds, packed to 16 bits as the PV
-// MFMA's operand; returns the lane's share of the row sum in fp32.  Normally
-// the sum is taken from the values before packing, in four partial sums (so the
-// adds do not form one dependent chain); kFromPacked sums the packed values
-// instead, unpacked again with integer operations, which needs no register
-// beyond the packed P (for the kernel forms that are short of registers).
-template <typename E, bool kFromPacked>
+// MFMA's operand; returns the lane's share of the row sum, in fp32, of exactly
+// the rounded values the MFMA consumes (unpacked again with integer
+// operations), so that O's weights sum to one and LSE matches them.  NPART
+// partial sums shorten the dependent chain of adds (fewer save registers).
+template <typename E, int NPART>
 __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16_t (&s)[2]) {
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  float part[NPART];
+#pragma unroll
+  for (int i = 0; i < NPART; ++i) part[i] = 0.f;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -300,15 +302,14 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 8 * ks + 2 * j;
-        const float p0 = __builtin_amdgcn_exp2f(s[nb][r]), p1 = __builtin_amdgcn_exp2f(s[nb][r + 1]);
-        const uint32_t w = pack2<E>(p0, p1);
+        const uint32_t w = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
         pk[nb][ks][j] = w;
-        if constexpr (kFromPacked)
-          part[0] += E::to_float((uint16_t)(w & 0xFFFFu)) + E::to_float((uint16_t)(w >> 16));
-        else
-          part[j] += p0 + p1;
+        part[j % NPART] += E::to_float((uint16_t)(w & 0xFFFFu)) + E::to_float((uint16_t)(w >> 16));
       }
-  return kFromPacked ? part[0] : (part[0] + part[1]) + (part[2] + part[3]);
+  float l = part[0];
+#pragma unroll
+  for (int i = 1; i < NPART; ++i) l += part[i];
+  return l;
 }
 
 // Forward work-group: 8 waves in two groups of 4 (group g = wave / 4; waves w and
@@ -626,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   };
   // P = exp2(S - base) straight away; the row maximum is only computed (and the
   // base moved) when some P exceeds 2^threshold, or on a valid row's first tile.
-  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128)>(pk, s); };
+  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4)>(pk, s); };
   auto softmax = [&](const TileCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
     float lt;
@@ -1198,7 +1199,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
         for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
     }
   };
-  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128)>(pk, s); };
+  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4)>(pk, s); };
   bool valid = lane_valid(cur);
   auto softmax = [&](const StreamCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
