@@ -385,7 +385,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     }
     return;
   }
-  if (tid < 4 * nspan) sSpan[tid] = P.t.fwd_spans[span0 * 4 + tid];
+  // The span table, then Q and the row intervals (they need only the tile
+  // record and the segment), so that their latencies overlap: the wait before
+  // the span table's LDS store leaves the later loads in flight.
+  // (Lanes past the tile's rows load its first row, so that no load sits in a
+  // branch, and drop the values below.)
+  const int32_t span_w = P.t.fwd_spans[span0 * 4 + min(tid, 4 * nspan - 1)];
+  __builtin_amdgcn_sched_barrier(0);  // the span load goes out first
+  const int64_t lrow = valid ? (int64_t)row : (int64_t)(q_row0 + q0);
+  u32x4_t qraw[KSTEPS];
+  {
+    const uint16_t* qrow = (const uint16_t*)P.q + (lrow * P.hq + head) * DQK + 8 * half;
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) qraw[t] = *(const u32x4_t*)(qrow + 16 * t);
+  }
+  const int4 ivr = *(const int4*)(P.t.row_iv + lrow * 4);
+  if (tid < 4 * nspan) sSpan[tid] = span_w;
   __syncthreads();
   int n_tiles = 0;
   for (int sp = 0; sp < nspan; ++sp) {
@@ -488,12 +503,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   // Q fragments, pre-scaled by scale*log2(e): lane holds Q[row][16t + 8*half .. +7].
   typename E::vec8 qf[KSTEPS];
   {
-    const uint16_t* qrow = (const uint16_t*)P.q + ((int64_t)row * P.hq + head) * DQK + 8 * half;
     const float c = P.scale_log2;
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (valid) x = *(const u32x4_t*)(qrow + 16 * t);
+      u32x4_t x = qraw[t];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) x[w] = valid ? x[w] : 0u;
       u32x4_t y;
 #pragma unroll
       for (int w = 0; w < 4; ++w)
@@ -501,11 +516,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       qf[t] = as_vec8<E>(y);
     }
   }
-  int lo1 = 0, hi1 = 0, lo2 = 0, hi2 = 0;
-  if (valid) {
-    const int32_t* iv = P.t.row_iv + (int64_t)row * 4;
-    lo1 = iv[0]; hi1 = iv[1]; lo2 = iv[2]; hi2 = iv[3];
-  }
+  const int lo1 = valid ? ivr.x : 0, hi1 = valid ? ivr.y : 0, lo2 = valid ? ivr.z : 0, hi2 = valid ? ivr.w : 0;
   wait_vmem_all();  // indices, Q and row intervals, before any tile load is in flight
   if constexpr (kSpread) {
     __syncthreads();  // the first tiles' indices are in LDS for both groups
