@@ -326,8 +326,9 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 // n+2NS fetched into a small index ring; NS-2 batches stay in flight across
 // every barrier.  When Dqk == Dv each group streams one operand inside its own
 // MFMA steps (group 0 K, group 1 V, one load after every fourth MFMA pair of
-// X(n)); group 0 fetches the indices and waits for K(n+2) at the end of
-// Y(n+1), group 1 waits for V(n+1) at the end of X(n).  Otherwise group 0 streams both: K
+// X(n)); group 0's first wave fetches the indices (for all eight waves, which
+// read them after a barrier) and group 0 waits for K(n+2) at the end of
+// Y(n+1), group 1 for V(n+1) at the end of X(n).  Otherwise group 0 streams both: K
 // and the indices at the start of X(n), V after Y(n+1), then its wait.
 template <int DQK>
 constexpr int kStages = DQK > 128 ? 3 : 4;
@@ -499,7 +500,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
 
   // group 0: indices of tiles 0 .. 2NS-1 first, so that they load together with Q
   if (grp == 0)
-    for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
+    if (!kSpread || w4 == 0)
+      for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
   // Q fragments, pre-scaled by scale*log2(e): lane holds Q[row][16t + 8*half .. +7].
   typename E::vec8 qf[KSTEPS];
   {
@@ -745,9 +747,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       if (grp == 0) {
         // the indices of tile n+8 (here, where the vector step has slack, not
         // after the MFMA step, whose end sets the phase), then K(n+2)
-        fetch_idx_step();
-        if (n == 0) wait_vmem_le(2 * NI + 1);
-        else wait_vmem_le(2 * NI + 2);
+        if (w4 == 0) {  // one wave fetches the indices for all
+          fetch_idx_step();
+          if (n == 0) wait_vmem_le(2 * NI + 1);
+          else wait_vmem_le(2 * NI + 2);
+        } else {
+          wait_vmem_le(2 * NI);
+        }
       }
       read_own(n + 1);
       if (n + 2 < n_tiles) prefetch_k(n + 1);
