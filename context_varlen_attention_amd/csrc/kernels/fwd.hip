@@ -256,21 +256,31 @@ __device__ __forceinline__ void tile_scores(f32x16_t (&s)[2], const typename E::
   }
 }
 
+// Bits [a, b) of a 64-bit word (either end may lie outside [0, 64)).
+__device__ __forceinline__ uint64_t range_bits64(int a, int b) {
+  a = max(a, 0);
+  b = min(b, 64);
+  const uint64_t below_b = b >= 64 ? ~0ull : (b <= 0 ? 0ull : (1ull << b) - 1);
+  const uint64_t below_a = a >= 64 ? ~0ull : (1ull << a) - 1;
+  return below_b & ~below_a;
+}
+
 // Element-wise mask of a partial tile: lane (query column, half) holds keys
 // kb0 + 32*nb + 8*(r/4) + 4*half + r%4; visible iff inside [lo1,hi1) or [lo2,hi2).
+// The lane's visible keys of the tile become one 64-bit word; each score then
+// takes two operations: its bit, sign-extended to a full word, selects between
+// the score's bits and those of -inf.
 __device__ __forceinline__ void tile_mask(f32x16_t (&s)[2], int kb0, int half, int lo1, int hi1,
                                           int lo2, int hi2) {
-  int x = kb0 + 4 * half;
-  asm volatile("" : "+v"(x));  // keep x + constant per element (no hoisted per-element registers)
-  const uint32_t y1 = (uint32_t)(x - lo1), n1 = (uint32_t)(hi1 - lo1);
-  const uint32_t y2 = (uint32_t)(x - lo2), n2 = (uint32_t)(hi2 - lo2);
+  const uint64_t m = (range_bits64(lo1 - kb0, hi1 - kb0) | range_bits64(lo2 - kb0, hi2 - kb0)) >> (4 * half);
+  const uint32_t w[2] = {(uint32_t)m, (uint32_t)(m >> 32)};
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const uint32_t c = (uint32_t)(nb * 32 + 8 * (r >> 2) + (r & 3));
-      const bool vis = ((y1 + c) < n1) | ((y2 + c) < n2);
-      s[nb][r] = vis ? s[nb][r] : -INFINITY;
+      const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)w[nb], 8 * (r >> 2) + (r & 3), 1);
+      const uint32_t x = __float_as_uint(s[nb][r]);
+      s[nb][r] = __uint_as_float((x & keep) | (0xFF800000u & ~keep));
     }
   }
 }
