@@ -141,6 +141,13 @@ __device__ __forceinline__ uint32_t key_bits(int lo, int hi) {
   return upto & ~((1u << lo) - 1u);
 }
 
+// Score x, or -inf where bit `bit` of the lane's visibility word vw is clear
+// (a sign-extending bit extract and a bitwise select).
+__device__ __forceinline__ float mask_score(float x, uint32_t vw, int bit) {
+  const uint32_t keep = (uint32_t)__builtin_amdgcn_sbfe((int)vw, bit, 1);
+  return __uint_as_float((__float_as_uint(x) & keep) | (0xFF800000u & ~keep));
+}
+
 // ---------------------------------------------------------------------------
 // dQ with paired waves (Q/K head dimension 192, where the single-wave form needs
 // more than 256 registers and so runs one wave per SIMD).  The same work item
@@ -388,7 +395,13 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
           f32x16_t sc = zero16();
 #pragma unroll
           for (int st = 0; st < QS; ++st) sc = E::mfma32(as_vec8<E>(ko.row(k_s, nb, st)), fr[st], sc);
-          // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
+          // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query;
+          // on a partial tile bit 8i + j of vw says whether that key is visible
+          uint32_t vw = ~0u;
+          if (partial) {
+            const int kb = kb0 + nb * 32 + 4 * half;
+            vw = key_bits(lo1 - kb, hi1 - kb) | key_bits(lo2 - kb, hi2 - kb);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             f32x4_t pv;
@@ -396,11 +409,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
             for (int j = 0; j < 4; ++j) {
               const int r = 4 * i + j;
               float x = fmaf(sc[r], sl2, -lse2);
-              if (partial) {
-                const int b = kb0 + nb * 32 + 8 * i + 4 * half + j;
-                const bool vis = ((b >= lo1) & (b < hi1)) | ((b >= lo2) & (b < hi2));
-                x = vis ? x : -INFINITY;
-              }
+              if (partial) x = mask_score(x, vw, 8 * i + j);
               pv[j] = __builtin_amdgcn_exp2f(x);
             }
             if (nb == 0) sP[pw][i][lane] = pv;
