@@ -73,3 +73,17 @@ def test_placement_share_tables_in_bounds(mask):
                            branch_bounds=bb, mask_block=128)
         for d in range(R):
             check_plan_tables(pl.device_plan(d), len(lens), sum(lens), sum(lens))
+
+
+def test_random_sweep_tables_in_bounds(monkeypatch):
+    """The plans of the seeded random GPU sweep, per-item and streamed deals."""
+    from tests.random_cases import N_CASES, random_case
+    for seed in range(N_CASES):
+        w = random_case(seed)
+        for wgs in (None, "1", "3"):
+            if wgs is None:
+                monkeypatch.delenv("CVA_FWD_STREAM_WGS", raising=False)
+            else:
+                monkeypatch.setenv("CVA_FWD_STREAM_WGS", wgs)
+            check_plan_tables(plan_for(w), len(w.lengths), w.total_tokens,
+                              w.total_tokens // w.cp_size)
