@@ -27,7 +27,10 @@ materialised, softmax taken directly):
 * ``fwd_ref`` / ``bwd_ref`` -- masked softmax attention and its gradients on the
                    rank's local rows, K/V read from the unsplit tensors (DCP
                    paper, background: masked self-attention; RFC section 1.3:
-                   outputs and Q/K/V gradients equal non-CP attention).
+                   outputs and Q/K/V gradients equal non-CP attention), with
+                   optional attention dropout.
+* ``dropout``   -- the dropout keep mask of every (sequence, head, query, key)
+                   from Philox4x32-10 (RFC section 3.5.2.2: attention_dropout).
 
 Parity status of each function is stated in its docstring; every one of them
 is pinned by tests under ``tests/test_oracle_*.py``.
@@ -36,9 +39,11 @@ from .split import (rank_local_positions, rank_major_order, rank_major_row_of_po
                     metadata_ref, workload_ref)
 from .masks import mask_ref, visible_pairs_ref
 from .attention import fwd_ref, bwd_ref, fwd_full_ref, softmax_rows_ref
+from .dropout import philox4x32_10, keep_mask, keep_scale, threshold
 
 __all__ = [
     "rank_local_positions", "rank_major_order", "rank_major_row_of_position",
     "metadata_ref", "workload_ref", "mask_ref", "visible_pairs_ref",
     "fwd_ref", "bwd_ref", "fwd_full_ref", "softmax_rows_ref",
+    "philox4x32_10", "keep_mask", "keep_scale", "threshold",
 ]

@@ -33,6 +33,12 @@ positions.  Rows no local query sees stay zero.
 A query row that sees no key gets O = 0, LSE = -inf and dQ = 0 (unreachable for
 the masks here, every row sees itself).
 
+With ``dropout=(p, seed)`` both directions apply the attention dropout of
+``oracle.dropout`` (keep mask D from Philox4x32-10 at the pair's in-sequence
+positions): O = (D * P * s) V with s = 1 / (1 - realised p), the LSE of the
+undropped softmax; dV = (D * P * s)^T dO and dP = D * s * (dO V^T) in the
+Jacobian above.
+
 Parity: pinned (tests/test_oracle_attention.py -- pure-Python brute force,
 torch float64 scaled_dot_product_attention with an explicit mask, softmax rows
 summing to one, closed forms, concatenation of all ranks against unsplit
@@ -45,6 +51,7 @@ import math
 
 import numpy as np
 
+from .dropout import keep_mask, keep_scale
 from .masks import mask_rows_ref
 from .split import rank_local_positions, rank_major_row_of_position
 
@@ -90,13 +97,21 @@ def _mask_for(w, i, L, positions):
     return mask_rows_ref(w.mask, L, positions, w.sink, w.window, bounds, getattr(w, "block", 0))
 
 
-def fwd_ref(w, q, k, v, scale=None, rows=None, block=512, heads=None):
+def _dropped(P, dropout, i, h, qpos, L):
+    """D * P * s for sequence i, head h (P unchanged without dropout)."""
+    if dropout is None:
+        return P
+    p, seed = dropout
+    return np.where(keep_mask(i, h, qpos, np.arange(L), p, seed), P * keep_scale(p), 0.0)
+
+
+def fwd_ref(w, q, k, v, scale=None, rows=None, block=512, heads=None, dropout=None):
     """Forward on rank (w.cp_size, w.rank)'s local rows.
 
     q, k, v are the *full unsplit* tensors [T, H, D] (any float dtype; upcast
     to float64).  Returns o [T_loc, Hq, Dv] and lse [Hq, T_loc] as float64;
     when ``rows`` (local row ids) or ``heads`` (query heads) are given only
-    those are computed and the rest are NaN.
+    those are computed and the rest are NaN.  ``dropout`` = (p, seed) or None.
     """
     scale = default_scale(w.d_qk) if scale is None else float(scale)
     G = w.hq // w.hkv
@@ -119,12 +134,12 @@ def fwd_ref(w, q, k, v, scale=None, rows=None, block=512, heads=None):
             for h in (range(w.hq) if heads is None else heads):
                 S = scale * (Qb[:, h, :] @ Ki[:, h // G, :].T)
                 P, l = softmax_rows_ref(S, M)
-                o[lr, h, :] = P @ Vi[:, h // G, :]
+                o[lr, h, :] = _dropped(P, dropout, i, h, ps, L) @ Vi[:, h // G, :]
                 lse[h, lr] = l
     return o, lse
 
 
-def fwd_full_ref(w, q, k, v, scale=None):
+def fwd_full_ref(w, q, k, v, scale=None, dropout=None):
     """Unsplit attention over every packed token (no CP), o [T, Hq, Dv], lse [Hq, T]."""
     scale = default_scale(w.d_qk) if scale is None else float(scale)
     G = w.hq // w.hkv
@@ -140,12 +155,12 @@ def fwd_full_ref(w, q, k, v, scale=None):
         Vi = np.asarray(v[s0: s0 + L], dtype=np.float64)
         for h in range(w.hq):
             P, l = softmax_rows_ref(scale * (Qi[:, h] @ Ki[:, h // G].T), M)
-            o[s0: s0 + L, h] = P @ Vi[:, h // G]
+            o[s0: s0 + L, h] = _dropped(P, dropout, i, h, np.arange(L), L) @ Vi[:, h // G]
             lse[h, s0: s0 + L] = l
     return o, lse
 
 
-def bwd_ref(w, q, k, v, do_local, scale=None, heads=None, rows=None, block=None):
+def bwd_ref(w, q, k, v, do_local, scale=None, heads=None, rows=None, block=None, dropout=None):
     """Backward on rank (w.cp_size, w.rank)'s share.
 
     q, k, v: full unsplit tensors.  do_local: [T_loc, Hq, Dv] gradient of the
@@ -160,6 +175,7 @@ def bwd_ref(w, q, k, v, do_local, scale=None, heads=None, rows=None, block=None)
     3.1), so the shares of disjoint row sets add up to the full gradient.
     ``block`` takes the rows of a sub-sequence that many at a time and adds the
     blocks' shares (the same sum in another order; None: all rows at once).
+    ``dropout`` = (p, seed) or None, as in the forward.
     """
     scale = default_scale(w.d_qk) if scale is None else float(scale)
     G = w.hq // w.hkv
@@ -184,8 +200,11 @@ def bwd_ref(w, q, k, v, do_local, scale=None, heads=None, rows=None, block=None)
                 g = h // G
                 P, _ = softmax_rows_ref(scale * (Qi[:, h] @ Ki[:, g].T), M)
                 dOh = dO[lrows, h, :]
-                dv_seq[s0: s0 + L, g] += P.T @ dOh
+                dv_seq[s0: s0 + L, g] += _dropped(P, dropout, i, h, pos, L).T @ dOh
                 dP = dOh @ Vi[:, g].T
+                if dropout is not None:  # the dropped entries pass no gradient back
+                    dP = np.where(keep_mask(i, h, pos, np.arange(L), *dropout), dP * keep_scale(dropout[0]),
+                                  0.0)
                 dS = P * (dP - (dP * P).sum(axis=1, keepdims=True))
                 dq[lrows, h] = scale * (dS @ Ki[:, g])
                 dk_seq[s0: s0 + L, g] += scale * (dS.T @ Qi[:, h])
