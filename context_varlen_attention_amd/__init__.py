@@ -12,6 +12,7 @@ Names follow the C ABI:
                         ``cva_plan_upload`` / ``cva_plan_get_schedule``
 * :func:`fwd`        -- ``cva_fwd``
 * :func:`bwd`        -- ``cva_bwd``
+  (both with ``dropout_p=``: ``cva_fwd_dropout`` / ``cva_bwd_dropout``)
 * :func:`local_token_ids`, :func:`rank_major_token_ids` -- the symmetric split
   and the rank-major order, read from the library's metadata (what a data
   loader and the K/V all-gather would produce).
@@ -109,7 +110,7 @@ EXPORTS = ["cva_last_error", "cva_plan_create", "cva_plan_destroy", "cva_plan_ge
            "cva_bwd", "cva_plan_get_schedule", "cva_timing_enable", "cva_timing_read", "cva_timing_select",
            "cva_placement_create", "cva_placement_get", "cva_placement_destroy",
            "cva_bwd_noalloc_max_bytes", "cva_bwd_noalloc", "cva_placement_plan_create",
-           "cva_plan_get_tables"]
+           "cva_plan_get_tables", "cva_fwd_dropout", "cva_bwd_dropout"]
 
 # timing ids of cva_timing_read; ids 1 and 2 are reserved (formerly separate
 # Delta and zero-fill launches, now part of the dQ kernel)
@@ -154,6 +155,11 @@ def load_library():
     L.cva_fwd_split.restype = i32
     L.cva_fwd_split.argtypes = [vp, vp, vp, vp, vp, vp, f32, vp, sz, vp]
     L.cva_bwd_workspace_bytes.restype = sz
+    L.cva_fwd_dropout.restype = i32
+    L.cva_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, f32, f32, ctypes.c_uint64, vp, sz, vp]
+    L.cva_bwd_dropout.restype = i32
+    L.cva_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, f32, ctypes.c_uint64,
+                                  vp]
     L.cva_bwd_workspace_bytes.argtypes = [vp]
     L.cva_bwd.restype = i32
     L.cva_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, f32, vp]
@@ -493,12 +499,14 @@ def _scale(plan, softmax_scale):
 
 
 def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, stream=None,
-        workspace=None):
+        workspace=None, dropout_p=None, seed=0):
     """``cva_fwd``: returns (o [T_loc, Hq, Dv], lse [Hq, T_loc] float32).
 
     With ``workspace`` (a device uint8 tensor of at least
     ``plan.fwd_workspace_bytes()`` bytes, or ``True`` to allocate one) this calls
     ``cva_fwd_split`` instead: the long K/V ranges are split and merged.
+    With ``dropout_p`` (a probability in [0, 1)) it calls ``cva_fwd_dropout``
+    with ``seed`` (an integer below 2**64), with or without that workspace.
     """
     import torch
     if not plan.uploaded:
@@ -519,16 +527,23 @@ def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, strea
     _expect(lse, "lse", (plan.hq, Tl), "float32", dev)
     vp = ctypes.c_void_p
     L = load_library()
+    if workspace is True:
+        with torch.cuda.stream(s):
+            workspace = torch.empty(max(plan.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
+    elif workspace is not None and s != torch.cuda.current_stream(dev):
+        workspace.record_stream(s)
+    if dropout_p is not None:
+        ws, wsb = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                       workspace.numel() * workspace.element_size())
+        _check(L.cva_fwd_dropout(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
+                                 vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
+                                 float(dropout_p), int(seed), vp(ws), wsb, vp(s.cuda_stream)))
+        return out, lse
     if workspace is None:
         _check(L.cva_fwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
                          vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
                          vp(s.cuda_stream)))
         return out, lse
-    if workspace is True:
-        with torch.cuda.stream(s):
-            workspace = torch.empty(max(plan.fwd_workspace_bytes(), 256), dtype=torch.uint8, device=dev)
-    elif s != torch.cuda.current_stream(dev):
-        workspace.record_stream(s)
     _check(L.cva_fwd_split(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
                            vp(out.data_ptr()), vp(lse.data_ptr()), _scale(plan, softmax_scale),
                            vp(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
@@ -537,8 +552,11 @@ def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, strea
 
 
 def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk_rm=None,
-        dv_rm=None, workspace=None, stream=None):
-    """``cva_bwd``: returns (dq [T_loc,Hq,Dqk], dk_rm [T,Hkv,Dqk], dv_rm [T,Hkv,Dv])."""
+        dv_rm=None, workspace=None, stream=None, dropout_p=None, seed=0):
+    """``cva_bwd``: returns (dq [T_loc,Hq,Dqk], dk_rm [T,Hkv,Dqk], dv_rm [T,Hkv,Dv]).
+
+    With ``dropout_p`` it calls ``cva_bwd_dropout`` (the backward of
+    ``fwd(..., dropout_p=p, seed=seed)``; pass the same p and seed)."""
     import torch
     if not plan.uploaded:
         plan.upload(q.device)
@@ -567,6 +585,13 @@ def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk
     _expect(dk_rm, "dk_rm", (T, plan.hkv, plan.d_qk), dt, dev)
     _expect(dv_rm, "dv_rm", (T, plan.hkv, plan.d_v), dt, dev)
     vp = ctypes.c_void_p
+    if dropout_p is not None:
+        _check(L.cva_bwd_dropout(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
+                                 vp(o.data_ptr()), vp(lse.data_ptr()), vp(dout.data_ptr()), vp(dq.data_ptr()),
+                                 vp(dk_rm.data_ptr()), vp(dv_rm.data_ptr()), vp(workspace.data_ptr()),
+                                 workspace.numel() * workspace.element_size(), _scale(plan, softmax_scale),
+                                 float(dropout_p), int(seed), vp(s.cuda_stream)))
+        return dq, dk_rm, dv_rm
     _check(L.cva_bwd(plan.handle, vp(q.data_ptr()), vp(k_rm.data_ptr()), vp(v_rm.data_ptr()),
                      vp(o.data_ptr()), vp(lse.data_ptr()), vp(dout.data_ptr()), vp(dq.data_ptr()),
                      vp(dk_rm.data_ptr()), vp(dv_rm.data_ptr()), vp(workspace.data_ptr()),

@@ -63,6 +63,21 @@ cva_status check_scale(float s) {
   return CVA_OK;
 }
 
+// Attention dropout of a call: threshold t = round(256 p) clamped to 255 (the
+// random byte of a pair must be >= t to keep it) and the scale 256 / (256 - t)
+// of the kept probabilities; t = 0 (p < 1/512) drops nothing.
+cva_status make_drop(float p, uint64_t seed, cva::DropParams* d) {
+  if (!(p >= 0.f && p < 1.f)) return fail(CVA_E_ARG, "dropout probability must be in [0, 1)");
+  const int t = std::min(255, (int)std::floor(256.0 * (double)p + 0.5));
+  d->t = (uint32_t)t;
+  d->seed_lo = (uint32_t)(seed & 0xFFFFFFFFull);
+  d->seed_hi = (uint32_t)(seed >> 32);
+  d->scale = (float)(256.0 / (256.0 - t));
+  return CVA_OK;
+}
+
+constexpr cva::DropParams kNoDrop{0u, 0u, 0u, 1.f};
+
 // Event-pair timing around kernel launches (cva_timing_enable / cva_timing_read).
 // One process-wide timer; its state is guarded by a mutex so that launches from
 // several host threads record their events without corrupting it (each
@@ -272,7 +287,7 @@ int32_t stream_wgs(const Plan& p, const cva::StreamDeal& d) {
 
 cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v_rm, void* o,
                    float* lse, float softmax_scale, void* workspace, size_t ws_bytes,
-                   bool split, void* stream) {
+                   bool split, const cva::DropParams& drop, void* stream) {
   cva_status st = check_ready(p);
   if (st != CVA_OK) return st;
   if (q == nullptr || k_rm == nullptr || v_rm == nullptr || o == nullptr || lse == nullptr)
@@ -327,6 +342,8 @@ cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v
     fp.ws_lse = (float*)((char*)workspace + (rows * p->d_v * sizeof(float) + 255) / 256 * 256);
   }
   fp.stream_wgs = stream_wgs(*p, split ? p->fwds_deal : p->fwd_deal);
+  fp.drop = drop;
+  if (drop.t != 0) fp.stream_wgs = 0;  // dropout runs one work-group per item
   hipError_t e = cva::launch_fwd(p->dtype, p->d_qk, p->d_v, fp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return CVA_OK;
@@ -337,7 +354,7 @@ cva_status run_fwd(const Plan* p, const void* q, const void* k_rm, const void* v
 cva_status cva_fwd(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
                    void* o, float* lse, float softmax_scale, void* stream) {
   return run_fwd(reinterpret_cast<const Plan*>(plan), q, k_rm, v_rm, o, lse, softmax_scale,
-                 nullptr, 0, false, stream);
+                 nullptr, 0, false, kNoDrop, stream);
 }
 
 size_t cva_fwd_workspace_bytes(const cva_plan* plan) {
@@ -349,7 +366,17 @@ cva_status cva_fwd_split(const cva_plan* plan, const void* q, const void* k_rm, 
                          void* o, float* lse, float softmax_scale, void* workspace,
                          size_t ws_bytes, void* stream) {
   return run_fwd(reinterpret_cast<const Plan*>(plan), q, k_rm, v_rm, o, lse, softmax_scale,
-                 workspace, ws_bytes, true, stream);
+                 workspace, ws_bytes, true, kNoDrop, stream);
+}
+
+cva_status cva_fwd_dropout(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                           void* o, float* lse, float softmax_scale, float dropout_p, uint64_t seed,
+                           void* workspace, size_t ws_bytes, void* stream) {
+  cva::DropParams d;
+  cva_status st = make_drop(dropout_p, seed, &d);
+  if (st != CVA_OK) return st;
+  return run_fwd(reinterpret_cast<const Plan*>(plan), q, k_rm, v_rm, o, lse, softmax_scale,
+                 workspace, ws_bytes, workspace != nullptr, d, stream);
 }
 
 size_t cva_bwd_workspace_bytes(const cva_plan* plan) {
@@ -377,7 +404,8 @@ cva_status check_bwd_args(const Plan* p, const void* q, const void* k_rm, const 
 // Launches the backward with Delta / LSE*log2(e) in `stats` (2 * T_loc * Hq floats).
 cva_status run_bwd(const Plan* p, const void* q, const void* k_rm, const void* v_rm,
                    const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
-                   void* dv_rm, float* stats, float softmax_scale, void* stream) {
+                   void* dv_rm, float* stats, float softmax_scale, const cva::DropParams& drop,
+                   void* stream) {
   cva::BwdParams bp;
   bp.q = q;
   bp.k = k_rm;
@@ -403,6 +431,7 @@ cva_status run_bwd(const Plan* p, const void* q, const void* k_rm, const void* v
   bp.t_total = p->T;
   bp.scale = softmax_scale;
   bp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  bp.drop = drop;
   hipError_t e = cva::launch_bwd(p->dtype, p->d_qk, p->d_v, bp, (hipStream_t)stream, hook());
   if (e != hipSuccess) return hip_fail(e, "backward launch");
   return CVA_OK;
@@ -424,7 +453,26 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
     return fail(CVA_E_WORKSPACE, os.str());
   }
   return run_bwd(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, (float*)workspace,
-                 softmax_scale, stream);
+                 softmax_scale, kNoDrop, stream);
+}
+
+cva_status cva_bwd_dropout(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
+                           void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
+                           float dropout_p, uint64_t seed, void* stream) {
+  const Plan* p = reinterpret_cast<const Plan*>(plan);
+  cva::DropParams d;
+  cva_status st = make_drop(dropout_p, seed, &d);
+  if (st != CVA_OK) return st;
+  if ((st = check_bwd_args(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, softmax_scale)) != CVA_OK) return st;
+  const size_t need = cva_bwd_workspace_bytes(plan);
+  if (workspace == nullptr || ws_bytes < need) {
+    std::ostringstream os;
+    os << "workspace needs " << need << " bytes";
+    return fail(CVA_E_WORKSPACE, os.str());
+  }
+  return run_bwd(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, (float*)workspace,
+                 softmax_scale, d, stream);
 }
 
 size_t cva_bwd_noalloc_max_bytes(void) { return cva::kBwdNoAllocScratchBytes; }
@@ -445,7 +493,7 @@ cva_status cva_bwd_noalloc(const cva_plan* plan, const void* q, const void* k_rm
   float* stats = nullptr;
   hipError_t e = cva::bwd_noalloc_scratch((hipStream_t)stream, &stats);
   if (e != hipSuccess) return hip_fail(e, "library device array (hipGetSymbolAddress)");
-  return run_bwd(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, stats, softmax_scale, stream);
+  return run_bwd(p, q, k_rm, v_rm, o, lse, dout, dq, dk_rm, dv_rm, stats, softmax_scale, kNoDrop, stream);
 }
 
 cva_status cva_plan_get_schedule(const cva_plan* plan, int32_t which, cva_schedule* out) {

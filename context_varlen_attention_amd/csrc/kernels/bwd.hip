@@ -163,7 +163,7 @@ __device__ __forceinline__ float mask_score(float x, uint32_t vw, int bit) {
 // through a 2-deep LDS ring, issuing tile n+1 at the start of tile n.  P is
 // never rounded, so the arithmetic is that of dq_kernel.
 // ---------------------------------------------------------------------------
-template <typename E, int DQK, int DV>
+template <typename E, int DQK, int DV, bool DROP>
 __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
   constexpr int NT = 2 * kThreads;
   const int n_dq_wg = P.n_dq_tiles * P.dq_head_groups;
@@ -210,6 +210,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
   const int a = q0 + (pw / hpt) * 32 + col;
   const bool valid = a < q0 + rows;  // the tile's own rows (a tile may end inside its segment)
   const int row = q_row0 + a;
+  [[maybe_unused]] const int seq = sg[0], qpos = sg[6] + a;  // sequence, in-sequence query position (dropout)
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
   const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
@@ -390,6 +391,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
         // ---- S wave: S^T and P of both 32-key blocks (phase 1); dS and dQ^T of
         // key block 1 (phase 2) ----
         f32x4_t p1[4];  // P of key block 1, kept in registers
+        // dropout: bit 4i + j of keep1 says whether key 32 + 8i + 4*half + j is kept;
+        // block 0's dropped P goes to the dS wave with its sign bit set (P >= 0)
+        [[maybe_unused]] uint32_t keep1 = 0;
 #pragma unroll
         for (int nb = 0; nb < BN / 32; ++nb) {
           f32x16_t sc = zero16();
@@ -412,6 +416,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
               if (partial) x = mask_score(x, vw, 8 * i + j);
               pv[j] = __builtin_amdgcn_exp2f(x);
             }
+            if constexpr (DROP) {
+              const uint32_t u =
+                  drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, kb0 + nb * 32 + 8 * i + 4 * half);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const bool kept = drop_keep(u, j, P.drop.t);
+                if (nb == 0) pv[j] = __uint_as_float(__float_as_uint(pv[j]) | (kept ? 0u : 0x80000000u));
+                else keep1 |= (kept ? 1u : 0u) << (4 * i + j);
+              }
+            }
             if (nb == 0) sP[pw][i][lane] = pv;
             else p1[i] = pv;
           }
@@ -420,6 +434,12 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
         f32x4_t dv1[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) dv1[i] = sDP[pw][i][lane];
+        if constexpr (DROP) {  // a dropped pair passes no gradient, a kept one is scaled
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dv1[i][j] = ((keep1 >> (4 * i + j)) & 1u) ? dv1[i][j] * P.drop.scale : 0.f;
+        }
         ds_dq(k_s, 1, p1, dv1);
       } else {
         // ---- dS wave: the next tile's loads and dP^T of both key blocks (phase 1);
@@ -441,6 +461,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
         for (int i = 0; i < 4; ++i) {
           p0[i] = sP[pw][i][lane];
           dv0[i] = f32x4_t{dp[0][4 * i], dp[0][4 * i + 1], dp[0][4 * i + 2], dp[0][4 * i + 3]};
+        }
+        if constexpr (DROP) {  // P's sign bit marks a dropped pair
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const uint32_t b = __float_as_uint(p0[i][j]);
+              p0[i][j] = __uint_as_float(b & 0x7FFFFFFFu);
+              dv0[i][j] = (b >> 31) ? 0.f : dv0[i][j] * P.drop.scale;
+            }
         }
         ds_dq(k_s, 0, p0, dv0);
         if (n + 1 < n_tiles) wait_vmem_all();  // tile n+1 has landed
@@ -514,7 +544,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
 template <int DQK>
 constexpr int kDkvPairStages = DQK > 128 ? 2 : 4;
 
-template <typename E, int DQK, int DV>
+template <typename E, int DQK, int DV, bool DROP>
 __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P) {
   constexpr int BQ = 64;           // queries per Q tile
   constexpr int QS = DQK / 16;     // reduction steps over Dqk
@@ -672,6 +702,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
     const char* o_s = sO[slot];
     const bool isB = (cC.seg & 1) != 0;
     const int q_rem = (isB ? qlenB : qlenA) - cC.qt * BQ;  // valid rows of this tile
+    [[maybe_unused]] const int qpos_t = (isB ? segB[6] : segA[6]) + cC.qt * BQ;  // its first query (dropout)
     if constexpr (!DSW) {
       // ---- P wave: S, P (phase 1); dV (phase 2) ----
       uint32_t pk[BQ / 32][2][4];
@@ -718,9 +749,48 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
             }
             pk[qs][r >> 3][(r & 7) >> 1] = pack2<E>(pv[0], pv[1]);
           }
+          // dropout: the P handed to the dS wave carries a set sign bit on every
+          // dropped pair (P >= 0); this wave's dV takes P with the dropped pairs zeroed
+          [[maybe_unused]] uint32_t keepw[2][4];
+          if constexpr (DROP) {
+            const int kp4 = kpos & ~3, kb = kpos & 3;
+            const int head = kvh * P.group + cC.hh;
 #pragma unroll
-          for (int st = 0; st < 2; ++st)
-            sP[kgrp][qs][st][lane] = u32x4_t{pk[qs][st][0], pk[qs][st][1], pk[qs][st][2], pk[qs][st][3]};
+            for (int i0 = 0; i0 < 4; ++i0) {
+              // queries qa .. qa + 3 of this run, possibly in two 4-query blocks
+              // (the offset qa % 4 is the same in every lane)
+              const int qa = qpos_t + qs * 32 + 8 * i0 + 4 * half;
+              const int off = qa & 3;
+              const Philox4 x = drop_block(P.drop.seed_lo, P.drop.seed_hi, seq, head, qa, kp4);
+              Philox4 y = x;
+              if (off != 0) y = drop_block(P.drop.seed_lo, P.drop.seed_hi, seq, head, qa + 4, kp4);
+              uint32_t kw = 0;  // bit j: query qa + j kept
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const int e = off + j;
+                const uint32_t w = e == 0 ? x.w[0] : e == 1 ? x.w[1] : e == 2 ? x.w[2] : e == 3 ? x.w[3]
+                                 : e == 4 ? y.w[0] : e == 5 ? y.w[1] : y.w[2];
+                kw |= (drop_keep(w, kb, P.drop.t) ? 1u : 0u) << j;
+              }
+              // elements r = 4 i0 + 0..3 sit in pk[qs][i0 / 2] words 2 (i0 % 2) and 2 (i0 % 2) + 1
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                keepw[i0 >> 1][2 * (i0 & 1) + h] =
+                    (((kw >> (2 * h)) & 1u) ? 0x0000FFFFu : 0u) | (((kw >> (2 * h + 1)) & 1u) ? 0xFFFF0000u : 0u);
+            }
+          }
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            if constexpr (DROP) {
+              sP[kgrp][qs][st][lane] =
+                  u32x4_t{pk[qs][st][0] | (~keepw[st][0] & 0x80008000u), pk[qs][st][1] | (~keepw[st][1] & 0x80008000u),
+                          pk[qs][st][2] | (~keepw[st][2] & 0x80008000u), pk[qs][st][3] | (~keepw[st][3] & 0x80008000u)};
+#pragma unroll
+              for (int w = 0; w < 4; ++w) pk[qs][st][w] &= keepw[st][w];
+            } else {
+              sP[kgrp][qs][st][lane] = u32x4_t{pk[qs][st][0], pk[qs][st][1], pk[qs][st][2], pk[qs][st][3]};
+            }
+          }
         }
       };
       if (cC.partial) phase1(std::true_type{});
@@ -765,9 +835,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
           for (int w = 0; w < 4; ++w) {
             const int r = 8 * st + 2 * w;  // elements r, r+1: queries 8i + 4*half + j, r = 4i + j
             const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * (r >> 2) + 4 * half);
-            const float p0 = E::to_float((uint16_t)(pw[w] & 0xFFFFu));
-            const float p1 = E::to_float((uint16_t)(pw[w] >> 16));
-            pd[st][w] = pack2<E>(p0 * (dp[qs][r] - dv4[r & 3]), p1 * (dp[qs][r + 1] - dv4[(r + 1) & 3]));
+            if constexpr (DROP) {  // a set sign bit marks a dropped pair: no gradient through dP
+              const float p0 = E::to_float((uint16_t)(pw[w] & 0x7FFFu));
+              const float p1 = E::to_float((uint16_t)((pw[w] >> 16) & 0x7FFFu));
+              const float d0 = (pw[w] & 0x8000u) ? 0.f : dp[qs][r] * P.drop.scale;
+              const float d1 = (pw[w] & 0x80000000u) ? 0.f : dp[qs][r + 1] * P.drop.scale;
+              pd[st][w] = pack2<E>(p0 * (d0 - dv4[r & 3]), p1 * (d1 - dv4[(r + 1) & 3]));
+            } else {
+              const float p0 = E::to_float((uint16_t)(pw[w] & 0xFFFFu));
+              const float p1 = E::to_float((uint16_t)(pw[w] >> 16));
+              pd[st][w] = pack2<E>(p0 * (dp[qs][r] - dv4[r & 3]), p1 * (dp[qs][r + 1] - dv4[(r + 1) & 3]));
+            }
           }
         }
 #pragma unroll
@@ -808,13 +886,14 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
         }
     } else {
       uint16_t* dvr = (uint16_t*)P.dv + (grow * P.hkv + kvh) * DV;
+      const float sc = DROP ? P.drop.scale : 1.f;  // dropout: kept probabilities are scaled
 #pragma unroll
       for (int d = 0; d < DV / 32; ++d)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int dd = d * 32 + 8 * i + 4 * half;
-          *(u32x2_t*)(dvr + dd) = u32x2_t{pack2<E>(acc[d][4 * i], acc[d][4 * i + 1]),
-                                           pack2<E>(acc[d][4 * i + 2], acc[d][4 * i + 3])};
+          *(u32x2_t*)(dvr + dd) = u32x2_t{pack2<E>(acc[d][4 * i] * sc, acc[d][4 * i + 1] * sc),
+                                           pack2<E>(acc[d][4 * i + 2] * sc, acc[d][4 * i + 3] * sc)};
         }
     }
   }
@@ -839,7 +918,7 @@ constexpr int kDqStages = 2;
 template <int DQK>
 constexpr int kDqBlocksPerCu = 2;
 
-template <typename E, int DQK, int DV>
+template <typename E, int DQK, int DV, bool DROP>
 __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdParams P) {
   const int n_dq_wg = P.n_dq_tiles * P.dq_head_groups;
   if ((int)blockIdx.x >= n_dq_wg) {  // the grid's last work-groups do the zero fill
@@ -879,6 +958,7 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
   const int a = q0 + (wave / hpt) * 32 + col;
   const bool valid = a < q0 + rows;  // the tile's own rows (a tile may end inside its segment)
   const int row = q_row0 + a;
+  [[maybe_unused]] const int seq = sg[0], qpos = sg[6] + a;  // sequence, in-sequence query position (dropout)
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
   const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
@@ -1045,6 +1125,18 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
         if (st < VS) dp = E::mfma32(as_vec8<E>(vo.row(v_s, nb, st)), of[st], dp);
       }
       // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
+      if constexpr (DROP) {
+        // dropout: a dropped pair passes no gradient through dP, a kept one is
+        // scaled; the random word of keys nb*32 + 8i + 4*half + 0..3 covers r = 4i..4i+3
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t u =
+              drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, kb0 + nb * 32 + 8 * i + 4 * half);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            dp[4 * i + j] = drop_keep(u, j, P.drop.t) ? dp[4 * i + j] * P.drop.scale : 0.f;
+        }
+      }
       uint32_t pd[2][4];
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
@@ -1108,11 +1200,20 @@ hipError_t launch_all(const BwdParams& p, hipStream_t s, LaunchHook* hook) {
   // dQ first: it also forms Delta and LSE * log2(e), which dK/dV read, and its
   // last n_zero_ranges work-groups zero the dK/dV rows no local query sees
   const unsigned dq_grid = (unsigned)p.n_dq_tiles * (unsigned)p.dq_head_groups + (unsigned)p.n_zero_ranges;
+  const unsigned kv_grid = (unsigned)p.n_kv_tiles * (unsigned)p.hkv;
+  if (p.drop.t != 0) {  // attention dropout
+    if constexpr (DQK > 128)
+      launch(K_BWD_DQ, dq_pair_kernel<E, DQK, DV, true>, dq_grid, 2 * kThreads);
+    else
+      launch(K_BWD_DQ, dq_kernel<E, DQK, DV, true>, dq_grid);
+    launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV, true>, kv_grid, 2 * kThreads);
+    return e;
+  }
   if constexpr (DQK > 128)
-    launch(K_BWD_DQ, dq_pair_kernel<E, DQK, DV>, dq_grid, 2 * kThreads);
+    launch(K_BWD_DQ, dq_pair_kernel<E, DQK, DV, false>, dq_grid, 2 * kThreads);
   else
-    launch(K_BWD_DQ, dq_kernel<E, DQK, DV>, dq_grid);
-  launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV>, (unsigned)p.n_kv_tiles * (unsigned)p.hkv, 2 * kThreads);
+    launch(K_BWD_DQ, dq_kernel<E, DQK, DV, false>, dq_grid);
+  launch(K_BWD_DKDV, dkdv_pair_kernel<E, DQK, DV, false>, kv_grid, 2 * kThreads);
   return e;
 }
 

@@ -167,3 +167,68 @@ __device__ inline f32x16_t zero16() {
 }
 
 }  // namespace cva
+
+// ---------------------------------------------------------------------------
+// Attention dropout (MindSpeed RFC section 3.5.2.2, attention_dropout in [0, 1)).
+// The random bits come from Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel
+// random numbers: as easy as 1, 2, 3", SC 2011): per round, the 64-bit products
+// of counter words 0 and 2 with 0xD2511F53 and 0xCD9E8D57 give the new words
+// (hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0), and the key moves on by the Weyl
+// increments 0x9E3779B9 and 0xBB67AE85.  One call covers a 4 x 4 block of
+// (query, key) pairs of one sequence and head: counter (k / 4, q / 4, head,
+// sequence) at in-sequence positions, key = the 64-bit seed; the pair's random
+// byte is byte k % 4 of output word q % 4, and the pair is kept iff that byte is
+// at least the threshold t = round(256 p) (t = 0: nothing dropped).  Kept
+// probabilities are scaled by 256 / (256 - t) where the output is normalised.
+// ---------------------------------------------------------------------------
+struct Philox4 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t y0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t y2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = y0;
+    c2 = y2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return Philox4{{c0, c1, c2, c3}};
+}
+
+// The word of the 4 x 4 block holding query qpos and keys kpos4 .. kpos4 + 3
+// (kpos4 a multiple of 4): byte i is the random byte of key kpos4 + i.
+__device__ __forceinline__ uint32_t drop_word(uint32_t seed_lo, uint32_t seed_hi, int seq, int head, int qpos,
+                                              int kpos4) {
+  const Philox4 x = philox4x32_10((uint32_t)kpos4 >> 2, (uint32_t)qpos >> 2, (uint32_t)head, (uint32_t)seq,
+                                  seed_lo, seed_hi);
+  const int i = qpos & 3;
+  return i == 0 ? x.w[0] : i == 1 ? x.w[1] : i == 2 ? x.w[2] : x.w[3];
+}
+
+// The four words of the block holding queries 4*(qpos >> 2) .. + 3 and keys
+// kpos4 .. kpos4 + 3: word i belongs to query 4*(qpos >> 2) + i.
+__device__ __forceinline__ Philox4 drop_block(uint32_t seed_lo, uint32_t seed_hi, int seq, int head, int qpos,
+                                              int kpos4) {
+  return philox4x32_10((uint32_t)kpos4 >> 2, (uint32_t)qpos >> 2, (uint32_t)head, (uint32_t)seq, seed_lo,
+                       seed_hi);
+}
+
+// Keep mask of the two 16-bit halves of a packed pair whose random bytes are
+// bytes b and b + 1 of u: 0xFFFF in each kept half.
+__device__ __forceinline__ uint32_t drop_keep_pair(uint32_t u, int b, uint32_t t) {
+  const uint32_t lo = (u >> (8 * b)) & 0xFFu, hi = (u >> (8 * b + 8)) & 0xFFu;
+  return (lo >= t ? 0x0000FFFFu : 0u) | (hi >= t ? 0xFFFF0000u : 0u);
+}
+
+// Is the pair with random byte b of u kept?
+__device__ __forceinline__ bool drop_keep(uint32_t u, int b, uint32_t t) {
+  return ((u >> (8 * b)) & 0xFFu) >= t;
+}

@@ -343,7 +343,7 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 template <int DQK>
 constexpr int kStages = DQK > 128 ? 3 : 4;
 
-template <typename E, int DQK, int DV>
+template <typename E, int DQK, int DV, bool DROP>
 __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   using TL = TileLoader<DQK, DV, kThreads / 2>;
   constexpr int KSTEPS = DQK / 16;  // 16-wide reduction steps of S^T
@@ -382,6 +382,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   const int split_slot = P.slot != nullptr ? P.slot[tile] : -1;  // piece of a split K/V range
   const bool valid = a < q0 + rows;       // the tile's own rows (a tile may end inside its segment)
   const int row = q_row0 + a;             // local row
+  [[maybe_unused]] const int seq = sg[0], qpos = sg[6] + a;  // sequence, in-sequence query position (dropout)
 
   const char* kg = (const char*)P.k + (int64_t)kvh * DQK * 2;
   const char* vg = (const char*)P.v + (int64_t)kvh * DV * 2;
@@ -651,6 +652,22 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   // P = exp2(S - base) straight away; the row maximum is only computed (and the
   // base moved) when some P exceeds 2^threshold, or on a valid row's first tile.
   auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4)>(pk, s); };
+  // Attention dropout of a tile's packed P, after its row sum (the normaliser
+  // is the undropped softmax's): the lane's keys kb0 + 32 nb + 8 run + 4 half
+  // + 0..3 sit in pk[nb][run / 2] words 2 (run % 2) (keys +0, +1) and
+  // 2 (run % 2) + 1 (keys +2, +3), and take bytes 0..3 of their block's word.
+  auto drop_tile = [&](int kb0) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int run = 0; run < 4; ++run) {
+        const uint32_t u =
+            drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, kb0 + 32 * nb + 8 * run + 4 * half);
+        const int ks = run >> 1, j0 = 2 * (run & 1);
+        pk[nb][ks][j0] &= drop_keep_pair(u, 0, P.drop.t);
+        pk[nb][ks][j0 + 1] &= drop_keep_pair(u, 2, P.drop.t);
+      }
+  };
   auto softmax = [&](const TileCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
     float lt;
@@ -680,6 +697,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       exp_pack(lt);
     }
     st.l += lt;
+    if constexpr (DROP) drop_tile(c.t * kBN);
   };
 
   // Phases: group 0 runs X(n) in phase 2n+2 and Y(n+1) in phase 2n+3, group 1
@@ -780,9 +798,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   if (grp == 0) __syncthreads();  // matches group 1's extra barrier
   wait_vmem_all();                // nothing may stay in flight past the kernel's end
 
-  // ---- epilogue: normalise, write O and LSE ----
+  // ---- epilogue: normalise (and scale the kept probabilities), write O and LSE ----
   const float l_tot = wave_half_sum(st.l);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float inv = (l_tot > 0.f ? 1.f / l_tot : 0.f) * (DROP ? P.drop.scale : 1.f);
   if (P.slot != nullptr && split_slot >= 0) {  // one piece of a split K/V range: fp32 partials
     if (valid) {
       const int64_t srow =
@@ -1498,6 +1516,7 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdParams P) {
   if ((int)threadIdx.x / hpt >= rows) return;
   const int kvh = head / P.group;
   const int row = q_row0 + a;
+  const int seq = sg[0], qpos = sg[6] + a;  // for dropout
   const float* qrow = (const float*)P.q + ((int64_t)row * P.hq + head) * DQK;
   const float* kg = (const float*)P.k;
   const float* vg = (const float*)P.v;
@@ -1523,11 +1542,14 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdParams P) {
       const float alpha = exp2f(m_run - m_new);
       const float p = exp2f(x - m_new);
       l_run = l_run * alpha + p;
-      for (int d = 0; d < DV; ++d) acc[d] = acc[d] * alpha + p * vrow[d];
+      const bool kept = P.drop.t == 0 ||
+                        drop_keep(drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, b & ~3), b & 3, P.drop.t);
+      const float pk = kept ? p : 0.f;  // dropout: the row sum keeps every probability
+      for (int d = 0; d < DV; ++d) acc[d] = acc[d] * alpha + pk * vrow[d];
       m_run = m_new;
     }
   }
-  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const float inv = (l_run > 0.f ? 1.f / l_run : 0.f) * (P.drop.t != 0 ? P.drop.scale : 1.f);
   float* orow = (float*)P.o + ((int64_t)row * P.hq + head) * DV;
   for (int d = 0; d < DV; ++d) orow[d] = acc[d] * inv;
   P.lse[(int64_t)head * P.t_loc + row] =
@@ -1539,11 +1561,13 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.n_head_groups;
   if (grid == 0) return hipSuccess;
   if (hook) hook->before(K_FWD, s);
-  if (p.stream_wgs > 0)
+  if (p.stream_wgs > 0 && p.drop.t == 0)
     hipLaunchKernelGGL((fwd_stream_kernel<E, DQK, DV>), dim3((unsigned)p.stream_wgs * (unsigned)p.n_head_groups),
                        dim3(kThreads), 0, s, p);
+  else if (p.drop.t != 0)
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, true>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, false>), dim3(grid), dim3(kThreads), 0, s, p);
   if (hook) hook->after(K_FWD, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_combine == 0) return e;

@@ -26,6 +26,14 @@ struct PlanTables {
   const int32_t* deal_items;    // streamed forward: items per work-group
 };
 
+// Attention dropout of a launch (random bytes: Philox4x32-10 per 4 x 4 block
+// of (query, key) positions, see the kernels' common helpers).
+struct DropParams {
+  uint32_t t;               // byte threshold round(256 p); 0 = no dropout
+  uint32_t seed_lo, seed_hi;
+  float scale;              // 256 / (256 - t): applied to kept probabilities
+};
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -51,6 +59,7 @@ struct FwdParams {
   // (t.deal_start / t.deal_items) as one stream of K/V tiles (0: one
   // work-group per item)
   int32_t stream_wgs;
+  DropParams drop;         // drop.t == 0: no dropout (the streamed form has none)
 };
 
 struct BwdParams {
@@ -73,6 +82,7 @@ struct BwdParams {
   int64_t t_total;
   float scale;             // softmax_scale
   float scale_log2;        // softmax_scale * log2(e)
+  DropParams drop;         // drop.t == 0: no dropout
 };
 
 // Optional hook around every kernel launch (timing); ids as in cva.h.

@@ -196,6 +196,26 @@ cva_status cva_fwd_split(const cva_plan* plan, const void* q, const void* k_rm, 
                          void* o, float* lse, float softmax_scale, void* workspace,
                          size_t ws_bytes, void* stream);
 
+/* Forward with attention dropout (RFC interface section 3.5.2.2: the
+ * attention_dropout argument, a probability p in [0, 1)).  Every softmax
+ * probability P[q,k] is kept or set to zero before it multiplies V; kept ones
+ * are scaled by 256 / (256 - t); lse is that of the undropped softmax.  The
+ * keep decision of a (sequence, query head, query, key) is a pure function of
+ * the seed and the in-sequence positions, so it does not depend on the CP
+ * split or the tiling: Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC 2011) with
+ * key = seed (low word first) and counter (k / 4, q / 4, query head, sequence
+ * index) gives one 128-bit output per 4 x 4 block; the pair's byte is byte
+ * k % 4 of word q % 4, and the pair is kept iff that byte >= t, where
+ * t = round(256 p) clamped to 255 (so the realised drop probability is t/256;
+ * t = 0 drops nothing).  workspace NULL: one launch per item as cva_fwd;
+ * otherwise as cva_fwd_split with that workspace.  The backward must be called
+ * through cva_bwd_dropout with the same p and seed.  bf16, fp16 and fp32.
+ * Errors: CVA_E_ARG if p is outside [0, 1), otherwise as cva_fwd /
+ * cva_fwd_split. */
+cva_status cva_fwd_dropout(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                           void* o, float* lse, float softmax_scale, float dropout_p, uint64_t seed,
+                           void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes cva_bwd needs (fp32 row statistics: Delta and LSE*log2(e),
  * 2 * T_loc * Hq floats). */
 size_t cva_bwd_workspace_bytes(const cva_plan* plan);
@@ -210,6 +230,16 @@ cva_status cva_bwd(const cva_plan* plan, const void* q, const void* k_rm, const 
                     const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
                     void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
                     void* stream);
+
+/* Backward of cva_fwd_dropout (same p and seed; o and lse from that forward):
+ * the same keep mask zeroes the dropped pairs' share of dV and of dP, and kept
+ * pairs are scaled by 256 / (256 - t) in both; Delta = rowsum(dO * O) with the
+ * dropped forward's O.  Arguments, workspace and results otherwise as cva_bwd.
+ * Errors: CVA_E_ARG if p is outside [0, 1), otherwise as cva_bwd. */
+cva_status cva_bwd_dropout(const cva_plan* plan, const void* q, const void* k_rm, const void* v_rm,
+                           const void* o, const float* lse, const void* dout, void* dq, void* dk_rm,
+                           void* dv_rm, void* workspace, size_t ws_bytes, float softmax_scale,
+                           float dropout_p, uint64_t seed, void* stream);
 
 /* Allocation-free backward, for callers that cannot allocate device memory:
  * code under HIP graph capture, tight serving loops, harnesses that forbid

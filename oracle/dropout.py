@@ -40,9 +40,10 @@ probability is t / 256 and kept values are scaled by 256 / (256 - t) (exactly
 unbiased for the realised probability).
 
 Parity: pinned (tests/test_oracle_dropout.py -- published known-answer vectors
-of Philox4x32-10, the inverse of the round function, drop fraction and
-unbiasedness over many seeds, p = 0 reducing to plain attention, central finite
-differences of the dropped loss, and independence of the CP split).
+of Philox4x32-10; drop fraction, byte uniformity and independence across heads,
+sequences and seeds; unbiasedness over many seeds; p = 0 reducing to plain
+attention; torch float64 autograd through the defining expression; central
+finite differences of the dropped loss; independence of the CP split).
 """
 from __future__ import annotations
 
@@ -87,13 +88,16 @@ def keep_scale(p):
 
 def random_bytes(seq, head, qpos, kpos, seed):
     """The random byte of every (query position, key position) pair of one
-    sequence and head: array of shape (len(qpos), len(kpos))."""
-    qpos = np.asarray(qpos, dtype=np.int64)[:, None]
-    kpos = np.asarray(kpos, dtype=np.int64)[None, :]
+    sequence and head: array of shape (len(qpos), len(kpos)).  The generator
+    runs once per 4 x 4 block that the positions touch."""
+    qpos = np.asarray(qpos, dtype=np.int64)
+    kpos = np.asarray(kpos, dtype=np.int64)
     seed = int(seed)
-    words = philox4x32_10(kpos >> 2, qpos >> 2, head, seq, seed & MASK32, (seed >> 32) & MASK32)
-    w = np.choose(np.broadcast_to(qpos & 3, np.broadcast_shapes(qpos.shape, kpos.shape)), words)
-    return (w >> (np.uint64(8) * (kpos & 3).astype(np.uint64))) & np.uint64(0xFF)
+    qb, qi = np.unique(qpos >> 2, return_inverse=True)
+    kb, ki = np.unique(kpos >> 2, return_inverse=True)
+    words = np.stack(philox4x32_10(kb[None, :], qb[:, None], head, seq, seed & MASK32, (seed >> 32) & MASK32))
+    w = words[(qpos & 3)[:, None], qi[:, None], ki[None, :]]  # word q % 4 of the pair's block
+    return (w >> (np.uint64(8) * (kpos & 3).astype(np.uint64))[None, :]) & np.uint64(0xFF)
 
 
 def keep_mask(seq, head, qpos, kpos, p, seed):

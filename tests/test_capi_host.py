@@ -268,6 +268,24 @@ def test_errors_before_device_work():
     assert lib.cva_plan_upload(p.handle, None, 0, None) == 1
 
 
+@pytest.mark.parametrize("p", [1.0, -0.25, 1.5, float("nan")])
+def test_dropout_probability_rejected(p):
+    """Dropout entry points refuse a probability outside [0, 1) before anything
+    else (CVA_E_ARG), and a valid one reaches the usual checks."""
+    lib = cva.load_library()
+    plan = cva.Plan([0, 64], 1, 0, 2, 2, 64, 64, "bf16")
+    vp = ctypes.c_void_p
+    st = lib.cva_fwd_dropout(plan.handle, *([vp(16)] * 5), 0.125, p, 7, None, 0, None)
+    assert cva.STATUS[st] == "CVA_E_ARG"
+    assert "dropout" in lib.cva_last_error().decode()
+    st = lib.cva_bwd_dropout(plan.handle, *([vp(16)] * 9), vp(16), 1 << 20, 0.125, p, 7, None)
+    assert cva.STATUS[st] == "CVA_E_ARG"
+    st = lib.cva_fwd_dropout(plan.handle, *([vp(16)] * 5), 0.125, 0.1, 7, None, 0, None)
+    assert cva.STATUS[st] == "CVA_E_NOT_UPLOADED"
+    st = lib.cva_bwd_dropout(plan.handle, *([vp(16)] * 9), vp(16), 1 << 20, 0.125, 0.1, 7, None)
+    assert cva.STATUS[st] == "CVA_E_NOT_UPLOADED"
+
+
 def test_zero_rows_complement_prefixes():
     """Rank-major rows that dK/dV zero-fills are exactly those outside every prefix."""
     for R, r in ((2, 0), (2, 1), (4, 2), (1, 0)):
