@@ -20,7 +20,10 @@ other kernels run without instrumentation.  ``cpu_baseline`` times the fp64
 oracle on a bounded sample of the same workload on this host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long128k]
-                       [--mask M] [--dtype D] [--no-split]
+                       [--mask M] [--dtype D] [--no-split] [--dropout P]
+
+With ``--dropout P`` the step runs cva_fwd_dropout / cva_bwd_dropout (a fresh
+seed per step); ``value`` still counts the same useful MFMA flops.
 
 The forward is cva_fwd_split whenever the plan cuts a Q tile's K/V range (a
 tile walking more than 4/3 of the average work per compute unit), else
@@ -328,6 +331,9 @@ def main():
                          "plan cuts a Q tile's K/V range, i.e. needs a forward workspace)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dropout", type=float, default=None,
+                    help="attention dropout probability (cva_fwd_dropout / cva_bwd_dropout); each step "
+                         "draws its mask from seed + step index")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -373,10 +379,20 @@ def main():
     log(f"workload {w.name}: T={T} T_loc={T_loc} seqs={len(w.lengths)} pairs/head={pairs} "
         f"fwd_only={fwd_only}")
 
+    n_step = [0]
+
     def step(plan):
-        cva.fwd(plan, q, k, v, out=o, lse=lse, workspace=fwd_ws)
+        if args.dropout is None:
+            cva.fwd(plan, q, k, v, out=o, lse=lse, workspace=fwd_ws)
+            if not fwd_only:
+                cva.bwd(plan, q, k, v, o, lse, do, dq=dq, dk_rm=dk, dv_rm=dv, workspace=ws)
+            return
+        seed = args.seed + n_step[0]
+        n_step[0] += 1
+        cva.fwd(plan, q, k, v, out=o, lse=lse, workspace=fwd_ws, dropout_p=args.dropout, seed=seed)
         if not fwd_only:
-            cva.bwd(plan, q, k, v, o, lse, do, dq=dq, dk_rm=dk, dv_rm=dv, workspace=ws)
+            cva.bwd(plan, q, k, v, o, lse, do, dq=dq, dk_rm=dk, dv_rm=dv, workspace=ws,
+                    dropout_p=args.dropout, seed=seed)
 
     n_prof = max(1, min(args.steps, 10))  # profile-pass steps (see below)
     planner = LookAheadPlanner(cva, w, args.warmup + n_prof + args.steps)
@@ -451,7 +467,8 @@ def main():
     d = kernels[dom]
     roofline = {"kernel": dom, "bound": d.get("bound"), "achieved": d.get("achieved"),
                 "peak": d.get("peak"), "unit": d.get("unit"), "frac": d.get("frac"),
-                "traffic": measured_traffic(dom, traffic_key(w)),
+                # (the committed counters are of the kernels without dropout)
+                "traffic": None if args.dropout is not None else measured_traffic(dom, traffic_key(w)),
                 "per_launch": (f"{kfl[dom]:.4e} flop" if dom in kfl else f"{kby.get(dom, 0)} B")}
     fwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("fwd")) or None
     bwd_ms = sum(kernels[n]["ms_per_step"] for n in kernels if n.startswith("bwd"))
@@ -472,7 +489,7 @@ def main():
                    "sub_sequences": int(len(w.lengths)), "cp_size": w.cp_size, "rank": w.rank,
                    "hq": w.hq, "hkv": w.hkv, "d_qk": w.d_qk, "d_v": w.d_v, "mask": w.mask,
                    "step": "plan (look-ahead) + upload + fwd" + ("" if fwd_only else " + bwd"),
-                   "fwd_split": fwd_ws is not None},
+                   "fwd_split": fwd_ws is not None, "dropout": args.dropout},
         "pct_of_peak": 100.0 * value / peak,
         "useful_tflop_per_step": (fl_fwd + fl_bwd) / 1e12,
         "fwd_tflops": fl_fwd / (fwd_ms * 1e-3) / 1e12 if fwd_ms else None,

@@ -406,6 +406,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
             const int kb = kb0 + nb * 32 + 4 * half;
             vw = key_bits(lo1 - kb, hi1 - kb) | key_bits(lo2 - kb, hi2 - kb);
           }
+          [[maybe_unused]] uint32_t du[4];  // dropout: random words of keys nb*32 + 8i + 4*half + 0..3
+          if constexpr (DROP)
+            drop_words_st(du, P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos - col, kb0 + nb * 32, lane);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             f32x4_t pv;
@@ -417,11 +420,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
               pv[j] = __builtin_amdgcn_exp2f(x);
             }
             if constexpr (DROP) {
-              const uint32_t u =
-                  drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, kb0 + nb * 32 + 8 * i + 4 * half);
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const bool kept = drop_keep(u, j, P.drop.t);
+                const bool kept = drop_keep(du[i], j, P.drop.t);
                 if (nb == 0) pv[j] = __uint_as_float(__float_as_uint(pv[j]) | (kept ? 0u : 0x80000000u));
                 else keep1 |= (kept ? 1u : 0u) << (4 * i + j);
               }
@@ -753,25 +754,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
           // dropped pair (P >= 0); this wave's dV takes P with the dropped pairs zeroed
           [[maybe_unused]] uint32_t keepw[2][4];
           if constexpr (DROP) {
-            const int kp4 = kpos & ~3, kb = kpos & 3;
-            const int head = kvh * P.group + cC.hh;
+            // byte j of qb[i0]: the random byte of this lane's key and query
+            // qs*32 + 8 i0 + 4 half + j of the tile
+            uint32_t qb[4];
+            drop_bytes_s(qb, P.drop.seed_lo, P.drop.seed_hi, seq, kvh * P.group + cC.hh, k0 + kgrp * 32,
+                         qpos_t + qs * 32, lane);
 #pragma unroll
             for (int i0 = 0; i0 < 4; ++i0) {
-              // queries qa .. qa + 3 of this run, possibly in two 4-query blocks
-              // (the offset qa % 4 is the same in every lane)
-              const int qa = qpos_t + qs * 32 + 8 * i0 + 4 * half;
-              const int off = qa & 3;
-              const Philox4 x = drop_block(P.drop.seed_lo, P.drop.seed_hi, seq, head, qa, kp4);
-              Philox4 y = x;
-              if (off != 0) y = drop_block(P.drop.seed_lo, P.drop.seed_hi, seq, head, qa + 4, kp4);
-              uint32_t kw = 0;  // bit j: query qa + j kept
+              uint32_t kw = 0;  // bit j: query 8 i0 + 4 half + j kept
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int e = off + j;
-                const uint32_t w = e == 0 ? x.w[0] : e == 1 ? x.w[1] : e == 2 ? x.w[2] : e == 3 ? x.w[3]
-                                 : e == 4 ? y.w[0] : e == 5 ? y.w[1] : y.w[2];
-                kw |= (drop_keep(w, kb, P.drop.t) ? 1u : 0u) << j;
-              }
+              for (int j = 0; j < 4; ++j) kw |= (drop_keep(qb[i0], j, P.drop.t) ? 1u : 0u) << j;
               // elements r = 4 i0 + 0..3 sit in pk[qs][i0 / 2] words 2 (i0 % 2) and 2 (i0 % 2) + 1
 #pragma unroll
               for (int h = 0; h < 2; ++h)
@@ -1127,15 +1119,14 @@ __global__ __launch_bounds__(kThreads, kDqBlocksPerCu<DQK>) void dq_kernel(BwdPa
       // lane holds keys nb*32 + 8i + 4*half + j (r = 4i + j) for its query
       if constexpr (DROP) {
         // dropout: a dropped pair passes no gradient through dP, a kept one is
-        // scaled; the random word of keys nb*32 + 8i + 4*half + 0..3 covers r = 4i..4i+3
+        // scaled; the random word u[i] of keys nb*32 + 8i + 4*half + 0..3 covers r = 4i..4i+3
+        uint32_t u[4];
+        drop_words_st(u, P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos - col, kb0 + nb * 32, lane);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t u =
-              drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, kb0 + nb * 32 + 8 * i + 4 * half);
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            dp[4 * i + j] = drop_keep(u, j, P.drop.t) ? dp[4 * i + j] * P.drop.scale : 0.f;
-        }
+            dp[4 * i + j] = drop_keep(u[i], j, P.drop.t) ? dp[4 * i + j] * P.drop.scale : 0.f;
       }
       uint32_t pd[2][4];
 #pragma unroll

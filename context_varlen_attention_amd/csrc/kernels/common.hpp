@@ -232,3 +232,74 @@ __device__ __forceinline__ uint32_t drop_keep_pair(uint32_t u, int b, uint32_t t
 __device__ __forceinline__ bool drop_keep(uint32_t u, int b, uint32_t t) {
   return ((u >> (8 * b)) & 0xFFu) >= t;
 }
+
+// 4 x 4 transpose of 32-bit values over the four lanes of each quad (lanes
+// 4m .. 4m+3): lane d holds x[0..3]; afterwards x[i] of lane d is what x[d]
+// was in lane i.  Two butterfly stages (partners lane ^ 2, then lane ^ 1, by
+// DPP quad permutes); every lane of the wave must be active.
+__device__ __forceinline__ void quad_transpose(uint32_t (&x)[4], int lane) {
+  const bool b1 = (lane & 2) != 0, b0 = (lane & 1) != 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {  // pairs (0, 2), (1, 3): swap the half whose index bit 1 differs
+    const uint32_t send = b1 ? x[p] : x[p + 2];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0x4E, 0xF, 0xF, false);
+    x[p] = b1 ? recv : x[p];
+    x[p + 2] = b1 ? x[p + 2] : recv;
+  }
+#pragma unroll
+  for (int p = 0; p < 4; p += 2) {  // pairs (0, 1), (2, 3): swap the element whose index bit 0 differs
+    const uint32_t send = b0 ? x[p] : x[p + 1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)send, 0xB1, 0xF, 0xF, false);
+    x[p] = b0 ? recv : x[p];
+    x[p + 1] = b0 ? x[p + 1] : recv;
+  }
+}
+
+// The word of the 4 x 4 generator blocks that belongs to queries q0 + j
+// (j = 0..3, q0 % 4 == off for every lane) and keys kp4 .. kp4 + 3: the blocks
+// of q0 and q0 + 4 cover them.
+__device__ __forceinline__ void drop_query_words(uint32_t (&w)[4], uint32_t s0, uint32_t s1, int seq, int head,
+                                                 int q0, int off, int kp4) {
+  const Philox4 a = drop_block(s0, s1, seq, head, q0, kp4);
+  if (off == 0) {  // (wave-uniform)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = a.w[j];
+    return;
+  }
+  const Philox4 b = drop_block(s0, s1, seq, head, q0 + 4, kp4);
+  // query q0 + j is word off + j of the first block, or of the second past 3
+  const uint32_t c[7] = {a.w[0], a.w[1], a.w[2], a.w[3], b.w[0], b.w[1], b.w[2]};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = off == 1 ? c[j + 1] : off == 2 ? c[j + 2] : c[j + 3];
+}
+
+// Random words of a 32-key block in the S^T layout (lane = query qw + (lane &
+// 31), keys kb + 8 r + 4 (lane >> 5) + 0..3 for r = 0..3, kb % 32 == 0): u[r] is
+// the word whose bytes 0..3 belong to those four keys.  The four lanes of a quad
+// (four consecutive queries) need the same blocks: lane d runs the generator
+// for run r = d and the quad exchanges the words.  qw: the wave's first query
+// (the same in every lane).
+__device__ __forceinline__ void drop_words_st(uint32_t (&u)[4], uint32_t s0, uint32_t s1, int seq, int head,
+                                              int qw, int kb, int lane) {
+  const int d = lane & 3, half = lane >> 5;
+  const int q0 = qw + (lane & 28);  // the quad's first query
+  drop_query_words(u, s0, s1, seq, head, q0, qw & 3, kb + 8 * d + 4 * half);
+  quad_transpose(u, lane);
+}
+
+// Random bytes of a 32-query block in the S layout (lane = key kw + (lane & 31)
+// with kw % 4 == 0; queries qb + 8 r + 4 (lane >> 5) + j for r, j = 0..3): byte j
+// of b[r] belongs to query qb + 8 r + 4 (lane >> 5) + j.  The four lanes of a
+// quad (four consecutive keys) need the same blocks: lane d runs the generator
+// for run r = d, regroups the bytes by key and the quad exchanges them.
+__device__ __forceinline__ void drop_bytes_s(uint32_t (&b)[4], uint32_t s0, uint32_t s1, int seq, int head,
+                                             int kw, int qb, int lane) {
+  const int d = lane & 3, half = lane >> 5;
+  uint32_t w[4];  // w[j]: the word of query qb + 8 d + 4 half + j (its byte e: key + e of the quad)
+  drop_query_words(w, s0, s1, seq, head, qb + 8 * d + 4 * half, qb & 3, kw + (lane & 28));
+#pragma unroll
+  for (int e = 0; e < 4; ++e)  // b[e]: byte e of w[0..3], i.e. the quad's key e for the run's four queries
+    b[e] = ((w[0] >> (8 * e)) & 0xFFu) | (((w[1] >> (8 * e)) & 0xFFu) << 8) | (((w[2] >> (8 * e)) & 0xFFu) << 16) |
+           (((w[3] >> (8 * e)) & 0xFFu) << 24);
+  quad_transpose(b, lane);
+}

@@ -658,15 +658,16 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   // 2 (run % 2) + 1 (keys +2, +3), and take bytes 0..3 of their block's word.
   auto drop_tile = [&](int kb0) {
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb) {
+      uint32_t u[4];
+      drop_words_st(u, P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos - col, kb0 + 32 * nb, lane);
 #pragma unroll
       for (int run = 0; run < 4; ++run) {
-        const uint32_t u =
-            drop_word(P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos, kb0 + 32 * nb + 8 * run + 4 * half);
         const int ks = run >> 1, j0 = 2 * (run & 1);
-        pk[nb][ks][j0] &= drop_keep_pair(u, 0, P.drop.t);
-        pk[nb][ks][j0 + 1] &= drop_keep_pair(u, 2, P.drop.t);
+        pk[nb][ks][j0] &= drop_keep_pair(u[run], 0, P.drop.t);
+        pk[nb][ks][j0 + 1] &= drop_keep_pair(u[run], 2, P.drop.t);
       }
+    }
   };
   auto softmax = [&](const TileCursor& c) {
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
