@@ -298,9 +298,10 @@ __device__ __forceinline__ float tile_max(const f32x16_t (&s)[2]) {
 // P = exp2(S^T) for the 32 scores a lane holds, packed to 16 bits as the PV
 // MFMA's operand; returns the lane's share of the row sum, in fp32, of exactly
 // the rounded values the MFMA consumes (unpacked again with integer
-// operations), so that O's weights sum to one and LSE matches them.  NPART
+// operations), so that O's weights sum to one and LSE matches them (EXACT:
+// of the unrounded values instead, the softmax's own normaliser).  NPART
 // partial sums shorten the dependent chain of adds (fewer save registers).
-template <typename E, int NPART>
+template <typename E, int NPART, bool EXACT = false>
 __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16_t (&s)[2]) {
   float part[NPART];
 #pragma unroll
@@ -312,9 +313,11 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 8 * ks + 2 * j;
-        const uint32_t w = pack2<E>(__builtin_amdgcn_exp2f(s[nb][r]), __builtin_amdgcn_exp2f(s[nb][r + 1]));
+        const float e0 = __builtin_amdgcn_exp2f(s[nb][r]), e1 = __builtin_amdgcn_exp2f(s[nb][r + 1]);
+        const uint32_t w = pack2<E>(e0, e1);
         pk[nb][ks][j] = w;
-        part[j % NPART] += E::to_float((uint16_t)(w & 0xFFFFu)) + E::to_float((uint16_t)(w >> 16));
+        if constexpr (EXACT) part[j % NPART] += e0 + e1;
+        else part[j % NPART] += E::to_float((uint16_t)(w & 0xFFFFu)) + E::to_float((uint16_t)(w >> 16));
       }
   float l = part[0];
 #pragma unroll
@@ -514,6 +517,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     if (!kSpread || w4 == 0)
       for (int m = 0; m < 2 * NS && m < n_tiles; ++m) fetch_idx();
   // Q fragments, pre-scaled by scale*log2(e): lane holds Q[row][16t + 8*half .. +7].
+  // Q pre-scaled by scale * log2(e) and rounded back to 16 bits; with dropout
+  // Q stays as given and the vector step scales the fp32 scores instead (the
+  // dropout path keeps the softmax closer to its definition: with sharply
+  // peaked rows the roundings of P's exponent and normaliser, amplified by the
+  // dropped entries, would reach the 16-bit tolerance of the gradients)
   typename E::vec8 qf[KSTEPS];
   {
     const float c = P.scale_log2;
@@ -522,10 +530,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       u32x4_t x = qraw[t];
 #pragma unroll
       for (int w = 0; w < 4; ++w) x[w] = valid ? x[w] : 0u;
-      u32x4_t y;
+      u32x4_t y = x;
+      if constexpr (!DROP) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        y[w] = pack2<E>(E::to_float((uint16_t)(x[w] & 0xFFFFu)) * c, E::to_float((uint16_t)(x[w] >> 16)) * c);
+        for (int w = 0; w < 4; ++w)
+          y[w] = pack2<E>(E::to_float((uint16_t)(x[w] & 0xFFFFu)) * c, E::to_float((uint16_t)(x[w] >> 16)) * c);
+      }
       qf[t] = as_vec8<E>(y);
     }
   }
@@ -646,12 +656,14 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[nb][r] = -st.base;
+        for (int r = 0; r < 16; ++r) s[nb][r] = DROP ? 0.f : -st.base;
     }
   };
   // P = exp2(S - base) straight away; the row maximum is only computed (and the
   // base moved) when some P exceeds 2^threshold, or on a valid row's first tile.
-  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4)>(pk, s); };
+  // (with dropout the row sum is of the unrounded P where registers allow: at
+  // Q/K head dim 192 the fp32 values kept for it would spill)
+  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4), DROP && DQK <= 128>(pk, s); };
   // Attention dropout of a tile's packed P, after its row sum (the normaliser
   // is the undropped softmax's): the lane's keys kb0 + 32 nb + 8 run + 4 half
   // + 0..3 sit in pk[nb][run / 2] words 2 (run % 2) (keys +0, +1) and
@@ -670,6 +682,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     }
   };
   auto softmax = [&](const TileCursor& c) {
+    if constexpr (DROP) {  // unscaled scores (chains from zero): S * scale * log2(e) - base
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[nb][r] = fmaf(s[nb][r], P.scale_log2, -st.base);
+    }
     if (c.partial) tile_mask(s, c.t * kBN, half, lo1, hi1, lo2, hi2);
     float lt;
     exp_pack(lt);
@@ -685,8 +703,10 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
       const float alpha = __builtin_amdgcn_exp2f(-shift);
       st.base += shift;
       st.l *= alpha;
+      if constexpr (!DROP) {  // (unused when !kFromBase; with dropout the chains start from zero)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) nbase[r] = -st.base;  // (unused when !kFromBase)
+        for (int r = 0; r < 16; ++r) nbase[r] = -st.base;
+      }
 #pragma unroll
       for (int d = 0; d < DB; ++d)
 #pragma unroll
