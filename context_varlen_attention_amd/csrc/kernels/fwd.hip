@@ -610,10 +610,13 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     const int kt = i >> 1, nb = i & 1;
     return lds_read128(skk + nb * 32 * DQK + (kt / KO) * 16 * KO, koff[kt % KO]);
   };
-  // The first K operand reads of the next MFMA step, issued at the end of the
-  // vector step before it (the tile is in LDS by then: group 0 has just waited
-  // for its own load, group 1's copy was published a phase earlier), so that
-  // the MFMA step does not start with a full LDS latency after its barrier.
+  // The first K operand reads of the next MFMA step, issued by group 1 at the
+  // end of the vector step before it (its copy of the tile was published by
+  // group 0's waits and a barrier a phase earlier), so that the MFMA step does
+  // not start with a full LDS latency after its barrier.  Group 0 reads them
+  // at the start of its MFMA step: at the end of its vector step each of its
+  // waves has waited only for its own share of the tile's loads, and the rows
+  // of the other waves' shares are safe to read only after the barrier.
   u32x4_t kpre[kXReadAhead];
   auto prefetch_k = [&](int n) {
 #pragma unroll
@@ -631,6 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
     };
     u32x4_t kr[AH];
     u32x2_t vl[AH], vh[AH];
+    if (grp == 0) prefetch_k(n);  // (group 1 read them before the barrier)
 #pragma unroll
     for (int j = 0; j < AH; ++j) {
       kr[j] = kpre[j];
@@ -744,7 +748,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   if constexpr (kSpread) {
     if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(1)
     read_own(0);
-    if (n_tiles > 1) prefetch_k(0);
+    if (grp == 1 && n_tiles > 1) prefetch_k(0);
   } else if (grp == 0) {
     wait_batch(-1);
     prepare_batch(0);
@@ -805,7 +809,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
         }
       }
       read_own(n + 1);
-      if (n + 2 < n_tiles) prefetch_k(n + 1);
+      if (grp == 1 && n + 2 < n_tiles) prefetch_k(n + 1);
     } else if (grp == 0) {
       if constexpr (kSplitIssue) issue_v_part(n);
       wait_batch(n);
@@ -1219,6 +1223,9 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
     };
     u32x4_t kr[AH];
     u32x2_t vl[AH], vh[AH];
+    if constexpr (kSpread) {
+      if (grp == 0) prefetch_k(n);  // (group 1 read them before the barrier)
+    }
 #pragma unroll
     for (int j = 0; j < AH; ++j) {
       kr[j] = kSpread ? kpre[j] : readk(j);
@@ -1407,7 +1414,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
   if constexpr (kSpread) {
     if (grp == 0) wait_vmem_le((NS - 2) * NI);  // K(1)
     read_own(0);
-    if (n_tiles > 1) prefetch_k(0);
+    if (grp == 1 && n_tiles > 1) prefetch_k(0);
   } else if (grp == 0) {
     wait_batch(-1);
     prepare_batch(0);
@@ -1446,7 +1453,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_stream_kernel(FwdParams P) {
         else wait_vmem_le(2 * NI + 2);
       }
       read_own(n + 1);
-      if (n + 2 < n_tiles) prefetch_k(n + 1);
+      if (grp == 1 && n + 2 < n_tiles) prefetch_k(n + 1);
     } else if (grp == 0) {
       if constexpr (kSplitIssue) issue_v_part(n);
       wait_batch(n);

@@ -87,3 +87,42 @@ def test_placement_shares_match_oracle_and_reduce_to_full_attention(ci, dtype):
     fo, fl = oracle.fwd_full_ref(w, q, k, v)
     assert_close(mo, fo, dtype, "O reduced over devices")
     assert_close(ml, fl, dtype, "LSE reduced over devices")
+
+
+@pytest.mark.parametrize("ci", [0, 1, 4])
+def test_placement_dropout_reduces_to_full_dropout_attention(ci):
+    """Attention dropout on placement shares: the keep mask follows in-sequence
+    positions, so the devices' partial outputs, reduced by their LSE, equal
+    unsplit attention with the same dropout."""
+    import torch
+    import context_varlen_attention_amd as cva
+    R, B, hq, hkv, dqk, dv, mask, mp = CASES[ci]
+    dtype = "bf16"
+    bb = None
+    if mask == "shared_prefix":
+        bb = np.array([synth.shared_prefix_bounds(L, prefix=256) for L in LENS])
+    w = synth.custom_workload(LENS, 1, 0, hq, hkv, dqk, dv, dtype, mask=mask, sink=mp.get("sink", 0),
+                              window=mp.get("window", 0), branch_bounds=bb, block=mp.get("block", 0),
+                              name=f"placed_drop{ci}")
+    print(f"[placement dropout] case {ci}: devices={R} block={B} mask={mask}", flush=True)
+    q, k, v = synth.random_tensors(w, 950 + ci, with_dout=False)
+    pl = cva.Placement(w.cu_seqlens, R, B, hq=hq, hkv=hkv, d_qk=dqk, d_v=dv, dtype=dtype, mask=mask,
+                       sink=w.sink, window=w.window, branch_bounds=bb, mask_block=w.block)
+    dt = torch_dtype(dtype)
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)).to("cuda", dt) for x in (q, k, v))
+    T = w.total_tokens
+    p, seed = 0.2, 4242 + ci
+    parts = []
+    for d in range(R):
+        pp = pl.device_plan(d)
+        o = torch.full((T, hq, dv), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((hq, T), float("nan"), dtype=torch.float32, device="cuda")
+        cva.fwd(pp, tq, tk, tv, out=o, lse=lse, workspace=True, dropout_p=p, seed=seed)
+        torch.cuda.synchronize()
+        o, lse = o.double().cpu().numpy(), lse.double().cpu().numpy()
+        mine = ~np.isnan(lse[0])
+        parts.append((np.where(mine[:, None, None], o, np.nan), np.where(mine[None, :], lse, np.nan)))
+    mo, ml = _merge(parts)
+    fo, fl = oracle.fwd_full_ref(w, q, k, v, dropout=(p, seed))
+    assert_close(mo, fo, dtype, "O reduced over devices (dropout)")
+    assert_close(ml, fl, dtype, "LSE reduced over devices (dropout)")
