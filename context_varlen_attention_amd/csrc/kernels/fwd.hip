@@ -38,6 +38,7 @@
 // K/V rows are gathered through the prefix index straight into LDS with
 // global_load_lds_dwordx4 (the index_select of the RFC, never materialised),
 // one tile ahead, with the tile's indices fetched two tiles ahead.
+#include <cmath>
 #include <type_traits>
 
 #include "../host/plan.hpp"
@@ -346,7 +347,7 @@ __device__ __forceinline__ float exp_pack_tile(u32x4_t (&pk)[2][2], const f32x16
 template <int DQK>
 constexpr int kStages = DQK > 128 ? 3 : 4;
 
-template <typename E, int DQK, int DV, bool DROP>
+template <typename E, int DQK, int DV, bool DROP, bool EXACT_SUM>
 __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   using TL = TileLoader<DQK, DV, kThreads / 2>;
   constexpr int KSTEPS = DQK / 16;  // 16-wide reduction steps of S^T
@@ -665,9 +666,11 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_mfma_kernel(FwdParams P) {
   };
   // P = exp2(S - base) straight away; the row maximum is only computed (and the
   // base moved) when some P exceeds 2^threshold, or on a valid row's first tile.
-  // (with dropout the row sum is of the unrounded P where registers allow: at
-  // Q/K head dim 192 the fp32 values kept for it would spill)
-  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4), DROP && DQK <= 128>(pk, s); };
+  // (EXACT_SUM: the row sum is of the unrounded P, the softmax's own normaliser;
+  // the launch takes it with dropout and at softmax scales up to 1.5x the
+  // default, for Q/K head dims up to 128 -- at 192 the fp32 values kept for it
+  // would spill)
+  auto exp_pack = [&](float& lt) { lt = exp_pack_tile<E, (DQK > 128 ? 1 : 4), EXACT_SUM>(pk, s); };
   // Attention dropout of a tile's packed P, after its row sum (the normaliser
   // is the undropped softmax's): the lane's keys kb0 + 32 nb + 8 run + 4 half
   // + 0..3 sit in pk[nb][run / 2] words 2 (run % 2) (keys +0, +1) and
@@ -1584,6 +1587,16 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdParams P) {
       l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994530942f : -INFINITY;
 }
 
+// Row normaliser of the forward without dropout: the sum of the unrounded P
+// (the softmax's own, and the faster form) at softmax scales up to 1.5x the
+// default 1/sqrt(Dqk); for sharper scales the sum of the P values as rounded
+// for the PV MFMA, so that O's weights sum to one exactly: with the pre-scaled
+// 16-bit Q and a dominant weight the backward's rowsum(dO * O) needs that.
+template <int DQK>
+bool exact_row_sum(const FwdParams& p) {
+  return DQK <= 128 && p.scale_log2 <= 1.5f * 1.4426950408889634f / std::sqrt((float)DQK);
+}
+
 template <typename E, int DQK, int DV>
 hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
   const unsigned grid = (unsigned)p.n_tiles * (unsigned)p.n_head_groups;
@@ -1593,9 +1606,11 @@ hipError_t launch_mfma(const FwdParams& p, hipStream_t s, LaunchHook* hook) {
     hipLaunchKernelGGL((fwd_stream_kernel<E, DQK, DV>), dim3((unsigned)p.stream_wgs * (unsigned)p.n_head_groups),
                        dim3(kThreads), 0, s, p);
   else if (p.drop.t != 0)
-    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, true, DQK <= 128>), dim3(grid), dim3(kThreads), 0, s, p);
+  else if (exact_row_sum<DQK>(p))
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, false, DQK <= 128>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((fwd_mfma_kernel<E, DQK, DV, false, false>), dim3(grid), dim3(kThreads), 0, s, p);
   if (hook) hook->after(K_FWD, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.n_combine == 0) return e;

@@ -77,6 +77,16 @@ def test_small_cases(ci, dtype):
     _run(w, q, k, v, do)
 
 
+def test_sharp_scale_d128():
+    """Softmax scale 0.2 at Q/K head dim 128 (2.3x the default): past 1.5x the
+    default the forward normalises by the sum of the rounded P (the other
+    tests, at the default scale, take the unrounded sum)."""
+    lens, R, r, hq, hkv, dqk, dv, mask, ex = CASES[1]
+    w = synth.custom_workload(lens, R, r, hq, hkv, dqk, dv, "bf16", mask=mask, name="bsharp")
+    q, k, v, do = synth.random_tensors(w, 602)
+    _run(w, q, k, v, do, scale=0.2)
+
+
 def test_tiny_bf16_custom_scale():
     w = synth.make_workload("tiny", dtype="bf16")
     q, k, v, do = synth.make_tensors(w)
