@@ -195,14 +195,24 @@ KERNEL_SOURCES = {
 COMMON_SOURCES = ["kernels/common.hpp", "kernels/launch.hpp", "host/plan.hpp", "host/schedule.cpp"]
 
 
+def code_text(src):
+    """C++/HIP source with comments removed and runs of white space collapsed
+    (string literals are kept as written)."""
+    import re
+    token = re.compile(r'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'', re.S)
+    src = token.sub(lambda m: " " if m.group(0)[0] == "/" else m.group(0), src)
+    return " ".join(src.split())
+
+
 def kernel_source_hash(kernel):
-    """sha256 over the sources a kernel's memory traffic depends on."""
+    """sha256 over the code (comments and white space left out) of the sources
+    a kernel's memory traffic depends on."""
     import hashlib
     h = hashlib.sha256()
     base = os.path.join(ROOT, "context_varlen_attention_amd", "csrc")
     for rel in KERNEL_SOURCES.get(kernel, []) + COMMON_SOURCES:
-        with open(os.path.join(base, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(base, rel), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

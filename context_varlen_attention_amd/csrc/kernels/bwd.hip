@@ -26,6 +26,13 @@
 //   dkdv_pair_kernel  K/V-stationary: a work-group owns 128 keys of one K/V
 //                     head and walks the 64-row Q tiles that see them; paired
 //                     waves per 32 keys, see below.
+//
+// Attention dropout (MindSpeed RFC section 3.5.2.2) is a second instantiation
+// of each kernel (DROP): dV takes P with the dropped pairs zeroed and the kept
+// ones scaled by 256 / (256 - t), and dS = P (dP' - Delta) with dP' the same
+// mask and scale applied to dP; the keep bytes come from Philox4x32-10, one
+// call per 4 x 4 block of (query, key) positions shared by a quad of lanes,
+// and where P crosses to the partner wave its sign bit carries the mask.
 #include <mutex>
 #include <type_traits>
 

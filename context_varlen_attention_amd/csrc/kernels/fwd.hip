@@ -10,8 +10,9 @@
 //   m' = max(m, rowmax S), P = exp(S - m'), l = l e^(m-m') + rowsum P,
 //   O = O e^(m-m') + P V;  finally O /= l, LSE = m + ln l.
 //
-// MFMA formulation.  A work-group is 4 waves; each wave owns 32 query rows of
-// one head.  The kernel computes the transposed scores S^T = K Q^T with
+// MFMA formulation.  A work-group is 8 waves in two groups of four that run the
+// same steps one phase apart (below); each wave owns 32 query rows of one
+// head.  The kernel computes the transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16 (A = K rows from LDS, B = Q from registers), so every lane
 // ends up holding 16 keys of ONE query column: the softmax statistics are
 // lane-local, plus one v_permlane32_swap with the other half-wave.  The output
@@ -29,15 +30,24 @@
 //     the base moved only when some P of the tile may exceed 2^8 (the sum of a
 //     lane's P values exceeds 2^8) or the row has no base yet (lazy rescaling),
 //     so both the maximum and the O rescale are rare;
-//   * P is packed to 16 bits with v_cvt_pk and the row sum is accumulated from
-//     the packed values (the sum of exactly the values the PV MFMA consumes),
-//     unpacked with integer operations and added in fp32 (v_dot2 would do
-//     the same in one instruction, but it issues many times slower while the
-//     other wave of the SIMD runs MFMAs);
+//   * P is packed to 16 bits with v_cvt_pk; the row sum adds the fp32 P values
+//     (at softmax scales beyond 1.5x the default, and at Q/K head dim 192, it
+//     adds the packed values the PV MFMA consumes instead, unpacked with
+//     integer operations -- v_dot2 would do that in one instruction, but it
+//     issues many times slower while the other wave of the SIMD runs MFMAs);
 //   * masking is a separate code path taken only on partial tiles.
 // K/V rows are gathered through the prefix index straight into LDS with
-// global_load_lds_dwordx4 (the index_select of the RFC, never materialised),
-// one tile ahead, with the tile's indices fetched two tiles ahead.
+// global_load_lds_dwordx4 (the index_select of the RFC, never materialised)
+// through a 4-stage ring (3 at Q/K head dim 192), the tiles' indices fetched
+// 2 x 4 tiles ahead.
+//
+// Attention dropout (MindSpeed RFC section 3.5.2.2) is a second instantiation
+// of the per-item kernel: Q stays unscaled (the vector step forms
+// S * scale * log2(e) - base with one fma per score), the row sum is that of the
+// undropped P, the packed P is ANDed with the keep mask of the tile (bytes of
+// Philox4x32-10 outputs, one generator call per 4 x 4 block of (query, key)
+// positions, shared by the four lanes of a quad) and 1/l carries the
+// 256 / (256 - t) scale of the kept values.
 #include <cmath>
 #include <type_traits>
 
