@@ -498,6 +498,12 @@ def _scale(plan, softmax_scale):
     return float(softmax_scale)
 
 
+def _check_seed(dropout_p, seed):
+    """The dropout seed is the generator's 64-bit key: an integer in [0, 2**64)."""
+    if dropout_p is not None and not (isinstance(seed, (int, np.integer)) and 0 <= int(seed) < (1 << 64)):
+        raise ValueError(f"dropout seed must be an integer in [0, 2**64), got {seed!r}")
+
+
 def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, stream=None,
         workspace=None, dropout_p=None, seed=0):
     """``cva_fwd``: returns (o [T_loc, Hq, Dv], lse [Hq, T_loc] float32).
@@ -508,6 +514,7 @@ def fwd(plan: Plan, q, k_rm, v_rm, softmax_scale=None, out=None, lse=None, strea
     With ``dropout_p`` (a probability in [0, 1)) it calls ``cva_fwd_dropout``
     with ``seed`` (an integer below 2**64), with or without that workspace.
     """
+    _check_seed(dropout_p, seed)
     import torch
     if not plan.uploaded:
         plan.upload(q.device)
@@ -557,6 +564,7 @@ def bwd(plan: Plan, q, k_rm, v_rm, o, lse, dout, softmax_scale=None, dq=None, dk
 
     With ``dropout_p`` it calls ``cva_bwd_dropout`` (the backward of
     ``fwd(..., dropout_p=p, seed=seed)``; pass the same p and seed)."""
+    _check_seed(dropout_p, seed)
     import torch
     if not plan.uploaded:
         plan.upload(q.device)

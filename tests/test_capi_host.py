@@ -286,6 +286,16 @@ def test_dropout_probability_rejected(p):
     assert cva.STATUS[st] == "CVA_E_NOT_UPLOADED"
 
 
+@pytest.mark.parametrize("seed", [-1, 1 << 64, 0.5, "7"])
+def test_dropout_seed_rejected(seed):
+    """The binding refuses a dropout seed outside [0, 2**64) before any device work."""
+    plan = cva.Plan([0, 64], 1, 0, 2, 2, 64, 64, "bf16")
+    with pytest.raises(ValueError):
+        cva.fwd(plan, None, None, None, dropout_p=0.1, seed=seed)
+    with pytest.raises(ValueError):
+        cva.bwd(plan, None, None, None, None, None, None, dropout_p=0.1, seed=seed)
+
+
 def test_zero_rows_complement_prefixes():
     """Rank-major rows that dK/dV zero-fills are exactly those outside every prefix."""
     for R, r in ((2, 0), (2, 1), (4, 2), (1, 0)):
