@@ -40,10 +40,11 @@ def plan_for(w):
                     mask=w.mask, sink=w.sink, window=w.window, branch_bounds=bb, block=w.block)
 
 
-@functools.lru_cache(maxsize=1)
+@functools.lru_cache(maxsize=8)
 def workload_tensors(name, mask=None, dtype=None, with_dout=True):
-    """(workload, [q, k, v(, do)]) of a named workload, kept for the next test
-    that asks for the same one (the full-size tensors take seconds to draw)."""
+    """(workload, [q, k, v(, do)]) of a named workload, kept for every later test
+    that asks for the same one (the full-size tensors take up to a minute or two
+    to draw; the suite's eight variants hold about 20 GB of host memory)."""
     w = synth.make_workload(name, mask=mask, dtype=dtype)
     return w, synth.make_tensors(w, with_dout=with_dout)
 

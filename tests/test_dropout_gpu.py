@@ -6,15 +6,17 @@ published definition -- so the kernels' O, LSE, dQ and rank-major dK/dV must
 match ``oracle.fwd_ref`` / ``oracle.bwd_ref`` with ``dropout=(p, seed)`` to the
 same tolerances as without dropout.  Covered: every mask, GQA and MHA, Q/K head
 dims 64, 128 and 192 (the per-item forward, which dropout always uses), split
-K/V ranges, several CP ranks, fp32 forward, p = 0 against the plain path, and a
-seeded random sweep.
+K/V ranges, several CP ranks, fp32 forward, p = 0 against the plain path, a
+seeded random sweep, and sampled rows of the full-size workloads (positions up
+to 131072, the generator's counters far from zero) in the benchmark's launch
+configuration.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from tests.gpu_helpers import assert_close, device_inputs, plan_for
+from tests.gpu_helpers import assert_close, device_inputs, plan_for, workload_tensors
 from tests.random_cases import random_case
 from tests.test_bwd_gpu import CASES
 
@@ -125,3 +127,37 @@ def test_random_sweep(seed):
     q, k, v, do = synth.random_tensors(w, 700 + seed)
     rng = np.random.default_rng([13, seed])
     _run(w, q, k, v, do, p=float(rng.choice([0.05, 0.2, 0.5, 0.75])), seed=int(rng.integers(0, 1 << 63)))
+
+
+def _sample_rows(w, n, seed):
+    T_loc = w.total_tokens // w.cp_size
+    rng = np.random.default_rng(seed)
+    rows = set(rng.integers(0, T_loc, size=n).tolist()) | {0, T_loc - 1, T_loc // 2, T_loc // 2 - 1}
+    return sorted(rows)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,mask,dtype,heads", [("long128k", None, None, [0, 31]), ("mla32k", None, "bf16", [0, 15]),
+                                                   ("sparse8", "blockwise", None, [15])])
+def test_full_size_sampled_rows(name, mask, dtype, heads):
+    """O, LSE and dQ of sampled local rows (a row's dQ depends on that row only)
+    with dropout, forward as the benchmark runs it (split where the plan cuts)."""
+    import torch
+    import context_varlen_attention_amd as cva
+    w, (q, k, v, do) = workload_tensors(name, mask=mask, dtype=dtype)
+    rows = _sample_rows(w, 24, 5)
+    p, seed = 0.1, (7 << 40) + 11
+    print(f"[drop] {w.name} {w.dtype} mask={w.mask} rows={len(rows)} heads={heads} p={p}", flush=True)
+    plan = plan_for(w)
+    tq, tk, tv, tdo = device_inputs(w, q, k, v, do)
+    ws = True if plan.fwd_workspace_bytes() > 0 else None
+    o, lse = cva.fwd(plan, tq, tk, tv, workspace=ws, dropout_p=p, seed=seed)
+    dq, _, _ = cva.bwd(plan, tq, tk, tv, o, lse, tdo, dropout_p=p, seed=seed)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.fwd_ref(w, q, k, v, rows=rows, heads=heads, dropout=(p, seed))
+    loc = cva.local_token_ids(w.cu_seqlens, w.cp_size, w.rank)
+    rdq, _, _ = oracle.bwd_ref(w, q, k, v, do[loc], heads=heads, rows=rows, dropout=(p, seed))
+    o, lse, dq = o.float().cpu().numpy(), lse.cpu().numpy(), dq.float().cpu().numpy()
+    assert_close(o[rows][:, heads], o_ref[rows][:, heads], w.dtype, "O")
+    assert_close(lse[heads][:, rows], lse_ref[heads][:, rows], w.dtype, "LSE")
+    assert_close(dq[rows][:, heads], rdq[rows][:, heads], w.dtype, "dQ")
