@@ -138,7 +138,7 @@ def _sample_rows(w, n, seed):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,mask,dtype,heads", [("long128k", None, None, [0, 31]), ("mla32k", None, "bf16", [0, 15]),
-                                                   ("sparse8", "blockwise", None, [15])])
+                                                   ("mla32k", None, "fp16", [3]), ("sparse8", "blockwise", None, [15])])
 def test_full_size_sampled_rows(name, mask, dtype, heads):
     """O, LSE and dQ of sampled local rows (a row's dQ depends on that row only)
     with dropout, forward as the benchmark runs it (split where the plan cuts)."""

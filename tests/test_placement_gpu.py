@@ -89,7 +89,7 @@ def test_placement_shares_match_oracle_and_reduce_to_full_attention(ci, dtype):
     assert_close(ml, fl, dtype, "LSE reduced over devices")
 
 
-@pytest.mark.parametrize("ci", [0, 1, 4])
+@pytest.mark.parametrize("ci", [0, 1, 3, 4])
 def test_placement_dropout_reduces_to_full_dropout_attention(ci):
     """Attention dropout on placement shares: the keep mask follows in-sequence
     positions, so the devices' partial outputs, reduced by their LSE, equal
