@@ -570,6 +570,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
   __shared__ __attribute__((aligned(16))) int32_t sIv[NS][BQ * 4];
   __shared__ __attribute__((aligned(16))) uint32_t sMask[4][BQ];          // per P wave: visible keys of each query
   __shared__ __attribute__((aligned(16))) u32x4_t sP[4][BQ / 32][2][64];  // packed P, in the MFMA operand layout
+  __shared__ __attribute__((aligned(16))) uint32_t sKeep[4][64];  // dropout: second query half's keep bits, per dS wave
   __shared__ __attribute__((aligned(16))) int32_t sSpan[kDkvMaxSpans * 4];
 
   const int tid = threadIdx.x;
@@ -759,8 +760,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
           }
           // dropout: the P handed to the dS wave carries a set sign bit on every
           // dropped pair (P >= 0); this wave's dV takes P with the dropped pairs zeroed
+          // (dropout: the first query half's mask is formed here; the second
+          // half's by the dS wave, which has slack in this phase, see below)
           [[maybe_unused]] uint32_t keepw[2][4];
-          if constexpr (DROP) {
+          if (DROP && qs == 0) {
             // byte j of qb[i0]: the random byte of this lane's key and query
             // qs*32 + 8 i0 + 4 half + j of the tile
             uint32_t qb[4];
@@ -780,7 +783,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
           }
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
-            if constexpr (DROP) {
+            if (DROP && qs == 0) {
               sP[kgrp][qs][st][lane] =
                   u32x4_t{pk[qs][st][0] | (~keepw[st][0] & 0x80008000u), pk[qs][st][1] | (~keepw[st][1] & 0x80008000u),
                           pk[qs][st][2] | (~keepw[st][2] & 0x80008000u), pk[qs][st][3] | (~keepw[st][3] & 0x80008000u)};
@@ -795,6 +798,16 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
       if (cC.partial) phase1(std::true_type{});
       else phase1(std::false_type{});
       __syncthreads();  // P is in LDS
+      if constexpr (DROP) {  // the second query half's keep bits from the dS wave
+        const uint32_t kb = sKeep[kgrp][lane];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const int r = 8 * st + 2 * w;  // elements r, r + 1 of the half
+            pk[1][st][w] &= (((kb >> r) & 1u) ? 0x0000FFFFu : 0u) | (((kb >> (r + 1)) & 1u) ? 0xFFFF0000u : 0u);
+          }
+      }
 #pragma unroll
       for (int qs = 0; qs < BQ / 32; ++qs)
 #pragma unroll
@@ -823,6 +836,20 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
 #pragma unroll
         for (int qs = 0; qs < BQ / 32; ++qs) dp[qs] = E::mfma32(as_vec8<E>(oo.row(o_s, qs, st)), frag[st], dp[qs]);
       if (n + NS - 1 < n_tiles) issue(cI, n + NS - 1);  // into the slot tile n-1 used
+      // dropout: the keep bits of the second query half (bit 4 i0 + j: query
+      // 32 + 8 i0 + 4 half + j of the tile), for this wave's dS and, through
+      // LDS, its partner's dV
+      [[maybe_unused]] uint32_t kbits1 = 0;
+      if constexpr (DROP) {
+        uint32_t qb[4];
+        drop_bytes_s(qb, P.drop.seed_lo, P.drop.seed_hi, seq, kvh * P.group + cC.hh, k0 + kgrp * 32,
+                     qpos_t + 32, lane);
+#pragma unroll
+        for (int i0 = 0; i0 < 4; ++i0)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kbits1 |= (drop_keep(qb[i0], j, P.drop.t) ? 1u : 0u) << (4 * i0 + j);
+        sKeep[kgrp][lane] = kbits1;
+      }
       __syncthreads();  // P is in LDS
 #pragma unroll
       for (int qs = 0; qs < BQ / 32; ++qs) {
@@ -834,11 +861,17 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dkdv_pair_kernel(BwdParams P)
           for (int w = 0; w < 4; ++w) {
             const int r = 8 * st + 2 * w;  // elements r, r+1: queries 8i + 4*half + j, r = 4i + j
             const f32x4_t dv4 = *(const f32x4_t*)(sD[slot] + qs * 32 + 8 * (r >> 2) + 4 * half);
-            if constexpr (DROP) {  // a set sign bit marks a dropped pair: no gradient through dP
+            if (DROP && qs == 0) {  // a set sign bit marks a dropped pair: no gradient through dP
               const float p0 = E::to_float((uint16_t)(pw[w] & 0x7FFFu));
               const float p1 = E::to_float((uint16_t)((pw[w] >> 16) & 0x7FFFu));
               const float d0 = (pw[w] & 0x8000u) ? 0.f : dp[qs][r] * P.drop.scale;
               const float d1 = (pw[w] & 0x80000000u) ? 0.f : dp[qs][r + 1] * P.drop.scale;
+              pd[st][w] = pack2<E>(p0 * (d0 - dv4[r & 3]), p1 * (d1 - dv4[(r + 1) & 3]));
+            } else if (DROP) {  // second half: this wave's own keep bits
+              const float p0 = E::to_float((uint16_t)(pw[w] & 0xFFFFu));
+              const float p1 = E::to_float((uint16_t)(pw[w] >> 16));
+              const float d0 = ((kbits1 >> r) & 1u) ? dp[qs][r] * P.drop.scale : 0.f;
+              const float d1 = ((kbits1 >> (r + 1)) & 1u) ? dp[qs][r + 1] * P.drop.scale : 0.f;
               pd[st][w] = pack2<E>(p0 * (d0 - dv4[r & 3]), p1 * (d1 - dv4[(r + 1) & 3]));
             } else {
               const float p0 = E::to_float((uint16_t)(pw[w] & 0xFFFFu));
