@@ -31,8 +31,8 @@
 // of each kernel (DROP): dV takes P with the dropped pairs zeroed and the kept
 // ones scaled by 256 / (256 - t), and dS = P (dP' - Delta) with dP' the same
 // mask and scale applied to dP; the keep bytes come from Philox4x32-10, one
-// call per 4 x 4 block of (query, key) positions shared by a quad of lanes,
-// and where P crosses to the partner wave its sign bit carries the mask.
+// call per 4 x 4 block of (query, key) positions shared by a quad of lanes.
+// The paired kernels split the mask work between their two waves.
 #include <mutex>
 #include <type_traits>
 
@@ -398,8 +398,8 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
         // ---- S wave: S^T and P of both 32-key blocks (phase 1); dS and dQ^T of
         // key block 1 (phase 2) ----
         f32x4_t p1[4];  // P of key block 1, kept in registers
-        // dropout: bit 4i + j of keep1 says whether key 32 + 8i + 4*half + j is kept;
-        // block 0's dropped P goes to the dS wave with its sign bit set (P >= 0)
+        // dropout: bit 4i + j of keep1 says whether key 32 + 8i + 4*half + j is kept
+        // (block 0's mask is formed by the dS wave, which applies it)
         [[maybe_unused]] uint32_t keep1 = 0;
 #pragma unroll
         for (int nb = 0; nb < BN / 32; ++nb) {
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
             vw = key_bits(lo1 - kb, hi1 - kb) | key_bits(lo2 - kb, hi2 - kb);
           }
           [[maybe_unused]] uint32_t du[4];  // dropout: random words of keys nb*32 + 8i + 4*half + 0..3
-          if constexpr (DROP)
+          if (DROP && nb == 1)
             drop_words_st(du, P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos - col, kb0 + nb * 32, lane);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -426,13 +426,9 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
               if (partial) x = mask_score(x, vw, 8 * i + j);
               pv[j] = __builtin_amdgcn_exp2f(x);
             }
-            if constexpr (DROP) {
+            if (DROP && nb == 1) {
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const bool kept = drop_keep(du[i], j, P.drop.t);
-                if (nb == 0) pv[j] = __uint_as_float(__float_as_uint(pv[j]) | (kept ? 0u : 0x80000000u));
-                else keep1 |= (kept ? 1u : 0u) << (4 * i + j);
-              }
+              for (int j = 0; j < 4; ++j) keep1 |= (drop_keep(du[i], j, P.drop.t) ? 1u : 0u) << (4 * i + j);
             }
             if (nb == 0) sP[pw][i][lane] = pv;
             else p1[i] = pv;
@@ -463,6 +459,10 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sDP[pw][i][lane] = f32x4_t{dp[1][4 * i], dp[1][4 * i + 1], dp[1][4 * i + 2], dp[1][4 * i + 3]};
+        // dropout: block 0's random words (this wave's rows are its partner's),
+        // formed while the S wave still exponentiates
+        [[maybe_unused]] uint32_t du0[4];
+        if constexpr (DROP) drop_words_st(du0, P.drop.seed_lo, P.drop.seed_hi, seq, head, qpos - col, kb0, lane);
         __syncthreads();  // P of block 0 and dP of block 1 are in LDS
         f32x4_t p0[4], dv0[4];
 #pragma unroll
@@ -470,15 +470,11 @@ __global__ __launch_bounds__(2 * kThreads, 1) void dq_pair_kernel(BwdParams P) {
           p0[i] = sP[pw][i][lane];
           dv0[i] = f32x4_t{dp[0][4 * i], dp[0][4 * i + 1], dp[0][4 * i + 2], dp[0][4 * i + 3]};
         }
-        if constexpr (DROP) {  // P's sign bit marks a dropped pair
+        if constexpr (DROP) {  // a dropped pair passes no gradient, a kept one is scaled
 #pragma unroll
           for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t b = __float_as_uint(p0[i][j]);
-              p0[i][j] = __uint_as_float(b & 0x7FFFFFFFu);
-              dv0[i][j] = (b >> 31) ? 0.f : dv0[i][j] * P.drop.scale;
-            }
+            for (int j = 0; j < 4; ++j) dv0[i][j] = drop_keep(du0[i], j, P.drop.t) ? dv0[i][j] * P.drop.scale : 0.f;
         }
         ds_dq(k_s, 0, p0, dv0);
         if (n + 1 < n_tiles) wait_vmem_all();  // tile n+1 has landed
