@@ -107,7 +107,7 @@ def test_p0_equals_plain_path():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp16"])
-@pytest.mark.parametrize("ci", [0, 2, 7, 10])
+@pytest.mark.parametrize("ci", [0, 2, 5, 7, 10, 11])
 def test_extreme_rates(ci, dtype):
     """The ends of the probability range.
 
