@@ -163,6 +163,9 @@ def device_info(torch, dev):
                     info["max_clock_mhz"] = int(m.group(1))
                 if c:
                     info["compute_units"] = int(c.group(1))
+                n = re.search(r"Marketing Name:[ \t]+(\S[^\n]*)", agent)
+                if n and not info["name"]:  # torch may report an empty name
+                    info["name"] = n.group(1).strip()
                 break
     except (OSError, subprocess.SubprocessError):
         pass
