@@ -170,10 +170,12 @@ def _sample_rows(w, n, seed):
 
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,mask,dtype,heads", [("long128k", None, None, [0, 31]), ("mla32k", None, "bf16", [0, 15]),
-                                                   ("mla32k", None, "fp16", [3]), ("sparse8", "blockwise", None, [15])])
+                                                   ("mla32k", None, "fp16", [3]), ("sparse8", "blockwise", None, [15]),
+                                                   ("sparse8", "lambda", None, [7]), ("sparse8", "shared_prefix", None, [0])])
 def test_full_size_sampled_rows(name, mask, dtype, heads):
     """O, LSE and dQ of sampled local rows (a row's dQ depends on that row only)
-    with dropout, forward as the benchmark runs it (split where the plan cuts)."""
+    with dropout, forward as the benchmark runs it (split where the plan cuts); sparse8
+    under the lambda, shared-prefix and blockwise masks."""
     import torch
     import context_varlen_attention_amd as cva
     w, (q, k, v, do) = workload_tensors(name, mask=mask, dtype=dtype)
